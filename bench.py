@@ -1,0 +1,265 @@
+"""Benchmark of Taylor-state attention on one MI355X.
+
+One timed "step" is one chunked prefill (every prefill stage of the path) of
+the prefill workload: B=4, H=8, N=8192, d=16, d_v=64, n=3, a=1, chunk=64,
+bfloat16 q/k/v, float32 accumulation, state and output.  The inputs are
+seeded synthetic Gaussians (q, k normalised per token) resident in HBM before
+timing starts; successive steps keep folding tokens into the same state, which
+does not change the cost of a step.
+
+Alongside, the decode workload (B=64 streams, H=8, n=3, float32 state built by
+prefill of a seeded N=65536 context, then 256 single-token steps) is timed and
+reported as microseconds per token (= per step), and the float64 oracle is
+timed on the host cores on a bounded sample of the prefill workload.
+
+Prints one JSON line.  `--gpus N` with N > 1 is refused: the path runs on one
+GPU (heads shard across GPUs with no communication).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+PREFILL = dict(B=4, H=8, N=8192, d=16, d_v=64, n=3, a=1.0, chunk=64)
+DECODE = dict(B=64, H=8, N0=65536, steps=256, d=16, d_v=64, n=3, a=1.0)
+
+
+def state_width(d, n):
+    from math import comb
+    return sum(comb(d + m - 1, m) for m in range(n))
+
+
+def prefill_algorithmic(cfg, in_bytes=2, out_bytes=4):
+    """Bytes and flops per launch of the chunk kernel (all B*H*N head-tokens)."""
+    D = state_width(cfg["d"], cfg["n"])
+    ht = cfg["B"] * cfg["H"] * cfg["N"]
+    dv, d, c = cfg["d_v"], cfg["d"], cfg["chunk"]
+    bytes_per_ht = in_bytes * (2 * d + dv) + out_bytes * dv + 4.0 * D * (dv + 1) / cfg["N"]
+    flops_per_ht = 4.0 * D * (dv + 1) + (c + 1) * (d + dv + 1) + 2.0 * D
+    return bytes_per_ht * ht, flops_per_ht * ht, bytes_per_ht, ht
+
+
+def decode_algorithmic(cfg):
+    D = state_width(cfg["d"], cfg["n"])
+    heads = cfg["B"] * cfg["H"]
+    state_bytes = 4.0 * D * (cfg["d_v"] + 1)
+    io = 4.0 * (2 * cfg["d"] + 2 * cfg["d_v"])
+    return heads * (2 * state_bytes + io), heads
+
+
+def make_prefill_inputs(torch, dev):
+    import taylor_inputs as TI
+    c = PREFILL
+    q, k, v = TI.make_qkv(TI.SEEDS["prefill"], c["B"], c["H"], c["N"], c["d"], c["d_v"], dtype="bf16")
+    to = lambda x: torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    return (q, k, v), (to(q), to(k), to(v))
+
+
+def time_prefill(torch, rsp, qkv, steps, warmup):
+    c = PREFILL
+    q, k, v = qkv
+    st = rsp.new_state(c["B"], c["H"], c["n"], device=q.device)
+    out = torch.empty(c["B"], c["H"], c["N"], c["d_v"], device=q.device, dtype=torch.float32)
+    ws_bytes = rsp.prefill_workspace_bytes(c["B"], c["H"], c["N"], c["n"], c["chunk"])
+    ws = torch.empty(max(ws_bytes // 4, 1), device=q.device, dtype=torch.float32)
+
+    def step():
+        rsp.prefill(q, k, v, st, c["n"], c["a"], chunk=c["chunk"], out=out, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step timing
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / steps
+    # per-phase timing (events recorded by the library between its launches,
+    # on the same stream the kernels run on)
+    evs = []
+    for _ in range(steps):
+        quad = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for e in quad:
+            e.record()  # materialise the HIP event handle
+        evs.append(quad)
+    torch.cuda.synchronize()
+    for quad in evs:
+        rsp.set_phase_events(quad)
+        step()
+    rsp.set_phase_events(None)
+    torch.cuda.synchronize()
+    phases = [[quad[i].elapsed_time(quad[i + 1]) for quad in evs] for i in range(3)]
+    avg = [sum(p) / len(p) for p in phases]
+    return ms_per_step, {"segment_sums_ms": avg[0], "scan_ms": avg[1], "chunk_kernel_ms": avg[2]}, out
+
+
+def time_decode(torch, rsp, dev, use_graph=True):
+    c = DECODE
+    B, H, N0, S = c["B"], c["H"], c["N0"], c["steps"]
+    g = torch.Generator(device=dev).manual_seed(1003)
+    st = rsp.new_state(B, H, c["n"], device=dev)
+    # context prefill in slices of 8192 tokens (the state is additive)
+    for t0 in range(0, N0, 8192):
+        q = torch.randn(B, H, 8192, c["d"], device=dev, generator=g)
+        k = torch.randn(B, H, 8192, c["d"], device=dev, generator=g)
+        v = torch.randn(B, H, 8192, c["d_v"], device=dev, generator=g)
+        q = q / q.norm(dim=-1, keepdim=True)
+        k = k / k.norm(dim=-1, keepdim=True)
+        rsp.prefill(q, k, v, st, c["n"], c["a"], chunk=64)
+        del q, k, v
+    qs = torch.randn(S, B, H, c["d"], device=dev, generator=g)
+    ks = torch.randn(S, B, H, c["d"], device=dev, generator=g)
+    vs = torch.randn(S, B, H, c["d_v"], device=dev, generator=g)
+    qs = qs / qs.norm(dim=-1, keepdim=True)
+    ks = ks / ks.norm(dim=-1, keepdim=True)
+    outs = torch.empty(S, B, H, c["d_v"], device=dev)
+    torch.cuda.synchronize()
+
+    def run():
+        for s in range(S):
+            rsp.decode(qs[s], ks[s], vs[s], st, c["n"], c["a"], out=outs[s])
+
+    run()  # warm-up pass (also advances the state by 256 tokens)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    run()
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1000.0 / S
+    graph_us = None
+    if use_graph:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=s):
+            run()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = 3
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph_us = e0.elapsed_time(e1) * 1000.0 / (S * reps)
+    return eager_us, graph_us
+
+
+def cpu_baseline(qkv_host, sample_every=4):
+    """The float64 oracle on every `sample_every`-th query row of the prefill
+    workload, all heads; time extrapolated to the whole job by the number of
+    (query, key) pairs."""
+    import numpy as np
+
+    import oracle
+    c = PREFILL
+    q, k, v = qkv_host
+    BH, N = c["B"] * c["H"], c["N"]
+    pos = np.arange(sample_every - 1, N, sample_every)
+    rows = (np.arange(BH)[:, None] * N + pos[None, :]).ravel()
+    sample_pairs = float(BH * (pos + 1).sum())
+    full_pairs = float(BH) * N * (N + 1) / 2
+    t0 = time.perf_counter()
+    oracle.taylor_direct(q, k, v, c["n"], c["a"], rows=rows)
+    dt = time.perf_counter() - t0
+    full_s = dt * full_pairs / sample_pairs
+    return {
+        "value": c["B"] * N / full_s,
+        "unit": "tokens/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"float64 direct O(N^2) sum on every {sample_every}th query row of all {BH} heads "
+                  f"({rows.size} rows, {sample_pairs:.3g} of {full_pairs:.3g} query-key pairs, {dt:.1f} s); "
+                  f"time extrapolated by pair count to the full job ({full_s:.1f} s)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: every (b, h) head is independent, so the path shards "
+              "across GPUs by heads with no communication; multi-GPU runs are not part of this build.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import recurrent_state_phi_amd as rsp
+    dev = "cuda:0"
+    host, qkv = make_prefill_inputs(torch, dev)
+    print(f"[bench] prefill inputs resident; timing {args.steps} steps", file=sys.stderr, flush=True)
+    ms, phases, _ = time_prefill(torch, rsp, qkv, args.steps, args.warmup)
+    c = PREFILL
+    tokens = c["B"] * c["N"]
+    alg_bytes, alg_flops, bytes_per_ht, ht = prefill_algorithmic(c)
+    t_k = phases["chunk_kernel_ms"] * 1e-3
+    achieved = alg_bytes / t_k / 1e9
+    result = {
+        "metric": "prefill tokens/s + decode us/token, n=3 Taylor states, d=16 d_v=64, 1 GPU",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian q, k normalised per token; Gaussian v)",
+        "config": {"workload": "prefill B=4 H=8 N=8192 d=16 d_v=64 n=3 a=1 chunk=64, bf16 q/k/v, fp32 accumulate/state/out",
+                   "global_batch": c["B"], "seq_len": c["N"], "heads": c["H"], "parallelism": "none (1 GPU)"},
+        "phases_ms": phases,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "prefill_chunk_kernel<3, bf16, 64, full, float>",
+            "algorithmic_bytes_per_launch": alg_bytes, "bytes_per_head_token": bytes_per_ht,
+            "mfma_tflops_algorithmic": alg_flops / t_k / 1e12,
+            "mfma_frac_algorithmic": alg_flops / t_k / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "whole_step_hbm_frac": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        },
+    }
+    if not args.no_decode:
+        print("[bench] decode: prefill 65536-token context for 512 heads, then 256 steps", file=sys.stderr, flush=True)
+        eager_us, graph_us = time_decode(torch, rsp, dev, use_graph=not args.no_graph)
+        best = min(x for x in (eager_us, graph_us) if x is not None)
+        dbytes, heads = decode_algorithmic(DECODE)
+        result["decode"] = {
+            "us_per_token": best, "us_per_token_eager": eager_us, "us_per_token_graph": graph_us,
+            "tokens_per_s": DECODE["B"] / (best * 1e-6),
+            "workload": "decode B=64 H=8 n=3 fp32 state after a 65536-token context, 256 steps",
+            "roofline": {"bound": "hbm", "achieved": dbytes / (best * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": dbytes / (best * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                         "algorithmic_bytes_per_step": dbytes},
+        }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (float64 oracle, sampled rows)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(host)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,128 @@
+/*
+ * taylor_attn.h -- C ABI of the MI355X (gfx950) Taylor-state attention library.
+ *
+ * Method: "A Taylor-Series Route to Linear-Time Transformers with a Fixed Number
+ * of Recurrent States" (arXiv 2610.20637).
+ *   section 3.1, Eq. (1)-(2): causal attention with exp(q.k/a) replaced by the
+ *       n-term polynomial sum_{m<n} (q.k)^m / (m! a^m);
+ *   section 3.2-3.3, Eq. (3)-(7): the history collapses into n states
+ *       A_m = sum_i k_i^{(x)m} (x) [v_i; 1], one rank-one update per token;
+ *   section 3.4: each state stored in the symmetric basis of C(d+m-1, m)
+ *       monomials with weights sqrt(m! / prod_i c_i!);
+ *   section 3.5: prefill in chunks -- a causally masked c x c block on the
+ *       diagonal plus the states for everything earlier; states are additive.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Supported shapes: d = 16, d_v = 64, n in {1, 2, 3, 4}.  Anything else
+ *   returns TAYLOR_EUNSUPPORTED without launching.
+ * - Tensors are dense, row-major, on the current HIP device:
+ *     q, k : [B, H, N, d]       v, o : [B, H, N, d_v]      (decode: N = 1)
+ *   element type given by `in_dtype` (q, k, v) and `out_dtype` (o).
+ * - State (float32, B*H*taylor_state_numel(d, d_v, n) floats, one buffer):
+ *     first  B*H*D*d_v floats: S[b][h][D][d_v]   (value index fastest)
+ *     then   B*H*D     floats: T[b][h][D]        (the ones-column, Eq. (6))
+ *   with D = taylor_state_width(d, n).  Row r enumerates the features of all
+ *   orders m = 0..n-1 in ascending m; inside one order the multi-indices
+ *   i_1 <= ... <= i_m appear in lexicographic order; every row carries the
+ *   sqrt-multinomial weight of section 3.4.  The temperature a and the factors
+ *   1/(m! a^m) are applied when the state is read, so the state does not
+ *   depend on a.
+ * - Prefill and decode ADD to the state they are given (Eq. (7)): output o_t
+ *   sees the tokens already folded into `state` plus this call's tokens i <= t.
+ *   Prefill of [0, N) equals prefill of [0, t1) followed by prefill of [t1, N),
+ *   and equals N single-token decode calls (up to rounding).
+ * - No normalisation of q or k happens inside; the division by the normaliser
+ *   has no epsilon and no clamp.
+ * - Ownership: the caller owns every buffer.  The library never allocates
+ *   device memory and never synchronises; all work is enqueued on `stream`
+ *   (0 = the null stream).  Calls are thread-safe; the error string is
+ *   thread-local.
+ * - Errors: TAYLOR_EINVAL (bad pointer or size, nothing launched),
+ *   TAYLOR_EUNSUPPORTED (shape or option not built, nothing launched),
+ *   TAYLOR_EHIP (a HIP call failed; the message names it).
+ *   taylor_last_error() describes the last failure on the calling thread.
+ */
+#ifndef TAYLOR_ATTN_H
+#define TAYLOR_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
+
+typedef enum { TAYLOR_F32 = 0, TAYLOR_BF16 = 1 } taylor_dtype;
+
+enum {
+    TAYLOR_OK = 0,
+    TAYLOR_EINVAL = -1,
+    TAYLOR_EUNSUPPORTED = -2,
+    TAYLOR_EHIP = -3
+};
+
+/* D = sum_{m<n} C(d+m-1, m): rows of the stacked state (section 3.4; Eq. (6)
+ * stacked over m).  Host only.  Returns -1 for d < 1 or n < 1. */
+int64_t taylor_state_width(int d, int n);
+
+/* Floats per (b, h) head: D * (d_v + 1) (section 4, "Memory").  Host only.
+ * Returns -1 for invalid arguments. */
+int64_t taylor_state_numel(int d, int d_v, int n);
+
+/* Zero B*H heads of state (the empty history, Eq. (4) at t < 0).
+ * state: device, B*H*taylor_state_numel(d, d_v, n) floats. */
+int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStream_t stream);
+
+/* Bytes of device workspace taylor_attn_prefill needs for these sizes (0 when
+ * the sequence fits one segment).  Host only; -1 cast to size_t on error. */
+size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n, int chunk);
+
+/* Chunked prefill (section 3.5): for every head and every t in [0, N)
+ *   o_t = sum_m alpha_m <phi_m(q_t), A_m(t)>[:d_v] / (same)[d_v],
+ *   A_m(t) = state_m + sum_{i<=t} phi_m(k_i) [v_i; 1]^T          (Eq. (5)-(7))
+ * evaluated in chunks of `chunk` tokens: the masked chunk x chunk polynomial
+ * block on the diagonal, the states for all earlier tokens.  On return (in
+ * stream order) `state` holds A_m(N-1).
+ *   q, k, v : device, in_dtype (TAYLOR_F32 or TAYLOR_BF16); o : device, out_dtype.
+ *   N >= 0 (N = 0 is a no-op), any N (the last chunk may be partial).
+ *   a > 0 : temperature.
+ *   chunk : 32 or 64 for TAYLOR_F32 inputs; 32, 64 or 128 for TAYLOR_BF16.
+ *   in_dtype selects the matrix-core arithmetic: float32 inputs use float32
+ *   MFMA throughout; bfloat16 inputs use bfloat16 MFMA with float32
+ *   accumulation and a float32 state.
+ *   workspace : device, at least taylor_prefill_workspace_bytes(...) bytes
+ *   (may be NULL when that is 0); it is scratch, its contents are undefined
+ *   afterwards.  o must not alias q, k, v or state. */
+int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, float* state,
+                        int B, int H, int N, int d, int d_v, int n, float a, int chunk,
+                        taylor_dtype in_dtype, taylor_dtype out_dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One decode step per head (section 3.3, Eq. (7), then Eq. (5)): update the
+ * state with the new token first, then read it (the token attends to itself).
+ *   q, k : device [B, H, d]; v, o : device [B, H, d_v]; dtypes as above.
+ *   state: device, read and written in place. */
+int taylor_attn_decode(const void* q, const void* k, const void* v, void* o, float* state,
+                       int B, int H, int d, int d_v, int n, float a,
+                       taylor_dtype in_dtype, taylor_dtype out_dtype, hipStream_t stream);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* taylor_last_error(void);
+
+/* Profiling hook.  With count == 4 and non-NULL events, every following
+ * taylor_attn_prefill on this thread records events[0] before its first
+ * launch, events[1] after the segment-sum kernel, events[2] after the scan
+ * kernel and events[3] after the chunk kernel, all on its stream (events of
+ * phases that do not run are recorded back to back).  count == 0 turns it
+ * off.  The events stay owned by the caller. */
+int taylor_set_phase_events(hipEvent_t* events, int count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TAYLOR_ATTN_H */

@@ -1,0 +1,147 @@
+// C ABI of the Taylor-state attention library: argument checks, workspace
+// sizing and dispatch to the gfx950 kernels.  Declarations and the contract
+// of every entry point are in include/taylor_attn.h.
+#include "../../include/taylor_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <string>
+
+#include "taylor_device.h"
+#include "taylor_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local hipEvent_t g_phase_events[4] = {nullptr, nullptr, nullptr, nullptr};
+thread_local bool g_phase_events_on = false;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int64_t binom(int64_t n, int64_t k) {
+  int64_t r = 1;
+  for (int64_t i = 1; i <= k; ++i) r = r * (n - k + i) / i;
+  return r;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shapes compiled into this build.
+bool shape_supported(int d, int d_v, int n) { return d == taylor::kD && d_v == taylor::kDV && n >= 1 && n <= 4; }
+
+int check_dtypes(taylor_dtype in, taylor_dtype out) {
+  if ((in != TAYLOR_F32 && in != TAYLOR_BF16) || (out != TAYLOR_F32 && out != TAYLOR_BF16))
+    return fail(TAYLOR_EINVAL, "dtype must be TAYLOR_F32 or TAYLOR_BF16");
+  return TAYLOR_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(TAYLOR_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t taylor_state_width(int d, int n) {
+  if (d < 1 || n < 1) return -1;
+  int64_t s = 0;
+  for (int m = 0; m < n; ++m) s += binom(d + m - 1, m);
+  return s;
+}
+
+int64_t taylor_state_numel(int d, int d_v, int n) {
+  if (d_v < 1) return -1;
+  const int64_t D = taylor_state_width(d, n);
+  return D < 0 ? -1 : D * (int64_t)(d_v + 1);
+}
+
+const char* taylor_last_error(void) { return g_last_error.c_str(); }
+
+int taylor_set_phase_events(hipEvent_t* events, int count) {
+  if (count == 0) {
+    g_phase_events_on = false;
+    return TAYLOR_OK;
+  }
+  if (count != 4 || events == nullptr) return fail(TAYLOR_EINVAL, "taylor_set_phase_events: need 4 events or count 0");
+  for (int i = 0; i < 4; ++i) {
+    if (events[i] == nullptr) return fail(TAYLOR_EINVAL, "taylor_set_phase_events: null event");
+    g_phase_events[i] = events[i];
+  }
+  g_phase_events_on = true;
+  return TAYLOR_OK;
+}
+
+int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStream_t stream) {
+  if (B < 0 || H < 0) return fail(TAYLOR_EINVAL, "taylor_state_init: B and H must be >= 0");
+  if (!shape_supported(d, d_v, n)) return fail(TAYLOR_EUNSUPPORTED, "taylor_state_init: only d=16, d_v=64, n in 1..4");
+  const size_t bytes = (size_t)B * H * taylor_state_numel(d, d_v, n) * sizeof(float);
+  if (bytes == 0) return TAYLOR_OK;
+  if (state == nullptr) return fail(TAYLOR_EINVAL, "taylor_state_init: state is NULL");
+  const hipError_t e = hipMemsetAsync(state, 0, bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "taylor_state_init: hipMemsetAsync");
+  return TAYLOR_OK;
+}
+
+size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n, int chunk) {
+  if (B < 0 || H < 0 || N < 0 || !shape_supported(d, d_v, n) || chunk <= 0) return (size_t)-1;
+  const taylor::PrefillPlan p = taylor::plan_prefill(B * H, N, n, chunk);
+  return p.workspace_floats * sizeof(float);
+}
+
+int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, float* state, int B, int H, int N,
+                        int d, int d_v, int n, float a, int chunk, taylor_dtype in_dtype, taylor_dtype out_dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (int e = check_dtypes(in_dtype, out_dtype)) return e;
+  if (B < 0 || H < 0 || N < 0) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: B, H, N must be >= 0");
+  if (!(a > 0.0f) || a == __builtin_inff()) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: a must be finite and > 0");
+  if (!shape_supported(d, d_v, n))
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: only d=16, d_v=64, n in 1..4 are built");
+  const bool in_bf16 = in_dtype == TAYLOR_BF16, out_bf16 = out_dtype == TAYLOR_BF16;
+  if (!taylor::prefill_supported(n, chunk, in_bf16))
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: unsupported (n, chunk, in_dtype): chunk must be 32/64 "
+                                     "(float32) or 32/64/128 (bfloat16), n in 1..3");
+  if ((int64_t)B * H == 0 || N == 0) return TAYLOR_OK;
+  if (!q || !k || !v || !o || !state) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state))
+    return fail(TAYLOR_EINVAL, "taylor_attn_prefill: q, k, v, o and state must be 16-byte aligned");
+  if ((int64_t)B * H > (1 << 24) || (int64_t)N * chunk > ((int64_t)1 << 40))
+    return fail(TAYLOR_EINVAL, "taylor_attn_prefill: sizes out of range");
+  const taylor::PrefillPlan plan = taylor::plan_prefill(B * H, N, n, chunk);
+  const size_t need = plan.workspace_floats * sizeof(float);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need)
+      return fail(TAYLOR_EINVAL, "taylor_attn_prefill: workspace too small (need " + std::to_string(need) +
+                                     " bytes, see taylor_prefill_workspace_bytes)");
+    if (!aligned16(workspace)) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: workspace must be 16-byte aligned");
+  }
+  taylor::PrefillArgs args{q, k, v, o, state, static_cast<float*>(workspace), B * H, N, n, chunk, a,
+                           in_bf16, out_bf16, plan, stream, g_phase_events_on ? g_phase_events : nullptr};
+  const hipError_t e = taylor::launch_prefill(args);
+  if (e != hipSuccess) return hip_fail(e, "taylor_attn_prefill: kernel launch");
+  return TAYLOR_OK;
+}
+
+int taylor_attn_decode(const void* q, const void* k, const void* v, void* o, float* state, int B, int H, int d,
+                       int d_v, int n, float a, taylor_dtype in_dtype, taylor_dtype out_dtype, hipStream_t stream) {
+  if (int e = check_dtypes(in_dtype, out_dtype)) return e;
+  if (B < 0 || H < 0) return fail(TAYLOR_EINVAL, "taylor_attn_decode: B and H must be >= 0");
+  if (!(a > 0.0f) || a == __builtin_inff()) return fail(TAYLOR_EINVAL, "taylor_attn_decode: a must be finite and > 0");
+  if (!shape_supported(d, d_v, n))
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_decode: only d=16, d_v=64, n in 1..4 are built");
+  if ((int64_t)B * H == 0) return TAYLOR_OK;
+  if ((int64_t)B * H > (1 << 30)) return fail(TAYLOR_EINVAL, "taylor_attn_decode: B*H out of range");
+  if (!q || !k || !v || !o || !state) return fail(TAYLOR_EINVAL, "taylor_attn_decode: NULL tensor pointer");
+  if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(TAYLOR_EINVAL, "taylor_attn_decode: q, k, v, o and state must be 16-byte aligned");
+  taylor::DecodeArgs args{q, k, v, o, state, B * H, n, a, in_dtype == TAYLOR_BF16, out_dtype == TAYLOR_BF16, stream};
+  const hipError_t e = taylor::launch_decode(args);
+  if (e != hipSuccess) return hip_fail(e, "taylor_attn_decode: kernel launch");
+  return TAYLOR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,124 @@
+// Single-token decode step (section 3.3, Eq. (7), then the readout of Eq. (5), of
+// "A Taylor-Series Route to Linear-Time Transformers with a Fixed Number of
+// Recurrent States", arXiv 2610.20637).
+//
+// Per head: A <- A + phi(k) [v; 1]^T, then y = phi_hat(q)^T A and o = y[:dv] / y[dv],
+// with phi_hat(q) = alpha_m phi_m(q), alpha_m = 1 / (m! a^m).  The state is
+// streamed from HBM exactly once (read, add the rank-one term, write back,
+// accumulate the read), so the kernel is bound by HBM bandwidth: 2 * 4 * D * 65
+// bytes per head per step against about 4 * D * 65 flops.
+//
+// One 256-thread workgroup per (b, h).  Thread layout for the S block
+// [D][64]: 16 threads cover one 256-byte row with float4 accesses, 16 rows are
+// in flight per pass, so every wave reads four full rows per instruction.
+#include "taylor_device.h"
+#include "taylor_launch.h"
+
+namespace taylor {
+
+__constant__ FeatureTable kFeatTab = make_feature_table();
+
+template <int NT, typename TIN, typename TOUT>
+__global__ __launch_bounds__(256) void decode_step_kernel(const TIN* __restrict__ q, const TIN* __restrict__ k,
+                                                          const TIN* __restrict__ v, TOUT* __restrict__ o,
+                                                          float* __restrict__ S, float* __restrict__ T,
+                                                          float inv_a) {
+  constexpr int D = state_width(NT);
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+
+  __shared__ float xq[kD], xk[kD];
+  __shared__ __align__(16) float vs[kDV];
+  __shared__ float phq[D], phk[D];
+  __shared__ __align__(16) float red[4][kDV];
+  __shared__ float red_den[4];
+
+  if (tid < kD) xq[tid] = Elem<TIN>::load(q, (size_t)bh * kD + tid);
+  else if (tid < 2 * kD) xk[tid - kD] = Elem<TIN>::load(k, (size_t)bh * kD + tid - kD);
+  else if (tid < 2 * kD + kDV) vs[tid - 2 * kD] = Elem<TIN>::load(v, (size_t)bh * kDV + tid - 2 * kD);
+  __syncthreads();
+
+  const float a2 = inv_a * inv_a;
+  const float4 alpha_q = make_float4(1.0f, inv_a, 0.5f * a2, a2 * inv_a * (1.0f / 6.0f));
+  const float4 alpha_k = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+  for (int f = tid; f < D; f += 256) {
+    phq[f] = feature_value(kFeatTab, f, xq, alpha_q);
+    phk[f] = feature_value(kFeatTab, f, xk, alpha_k);
+  }
+  __syncthreads();
+
+  // S block: rank-one update then read, one pass over [D][64].
+  float* __restrict__ Sh = S + (size_t)bh * D * kDV;
+  const int c4 = tid & 15, rg = tid >> 4;
+  const float4 vv = *reinterpret_cast<const float4*>(&vs[4 * c4]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int r = rg; r < D; r += 16) {
+    float4* p = reinterpret_cast<float4*>(Sh + (size_t)r * kDV + 4 * c4);
+    float4 s = *p;
+    const float pk = phk[r];
+    s.x += pk * vv.x; s.y += pk * vv.y; s.z += pk * vv.z; s.w += pk * vv.w;
+    *p = s;
+    const float pq = phq[r];
+    acc.x += pq * s.x; acc.y += pq * s.y; acc.z += pq * s.z; acc.w += pq * s.w;
+  }
+  // T block (the ones-column): same update and read.
+  float* __restrict__ Th = T + (size_t)bh * D;
+  float dacc = 0.f;
+  for (int r = tid; r < D; r += 256) {
+    const float t = Th[r] + phk[r];
+    Th[r] = t;
+    dacc += phq[r] * t;
+  }
+
+  // Reduce the 16 row groups: 4 inside a wave (lanes 16 apart), then 4 waves.
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+#pragma unroll
+  for (int off = 1; off <= 32; off <<= 1) dacc += __shfl_xor(dacc, off);
+  if (lane < 16) *reinterpret_cast<float4*>(&red[wave][4 * lane]) = acc;
+  if (lane == 0) red_den[wave] = dacc;
+  __syncthreads();
+  if (tid < kDV) {
+    const float y = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    const float den = red_den[0] + red_den[1] + red_den[2] + red_den[3];
+    Elem<TOUT>::store(o, (size_t)bh * kDV + tid, y / den);
+  }
+}
+
+template <int NT, typename TIN, typename TOUT>
+static hipError_t launch_decode_t(const DecodeArgs& a) {
+  const int D = state_width(NT);
+  float* S = a.state;
+  float* T = a.state + (size_t)a.BH * D * kDV;
+  hipLaunchKernelGGL((decode_step_kernel<NT, TIN, TOUT>), dim3(a.BH), dim3(256), 0, a.stream,
+                     static_cast<const TIN*>(a.q), static_cast<const TIN*>(a.k), static_cast<const TIN*>(a.v),
+                     static_cast<TOUT*>(a.o), S, T, 1.0f / a.a);
+  return hipGetLastError();
+}
+
+template <int NT>
+static hipError_t launch_decode_n(const DecodeArgs& a) {
+  if (!a.in_bf16 && !a.out_bf16) return launch_decode_t<NT, float, float>(a);
+  if (!a.in_bf16 && a.out_bf16) return launch_decode_t<NT, float, uint16_t>(a);
+  if (a.in_bf16 && !a.out_bf16) return launch_decode_t<NT, uint16_t, float>(a);
+  return launch_decode_t<NT, uint16_t, uint16_t>(a);
+}
+
+hipError_t launch_decode(const DecodeArgs& a) {
+  switch (a.n) {
+    case 1: return launch_decode_n<1>(a);
+    case 2: return launch_decode_n<2>(a);
+    case 3: return launch_decode_n<3>(a);
+    case 4: return launch_decode_n<4>(a);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace taylor

@@ -1,0 +1,48 @@
+// Host-side launch interface between the C ABI (taylor_abi.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace taylor {
+
+struct DecodeArgs {
+  const void* q; const void* k; const void* v; void* o;
+  float* state;
+  int BH, n;
+  float a;
+  bool in_bf16, out_bf16;
+  hipStream_t stream;
+};
+
+// How a prefill call is split: every (b, h) sequence is cut into `nseg`
+// segments of `chunks_per_seg` chunks of `chunk` tokens.
+struct PrefillPlan {
+  int nchunks = 0;
+  int nseg = 1;
+  int chunks_per_seg = 0;
+  size_t workspace_floats = 0;  // BH * nseg * D * 65 when nseg > 1, else 0
+};
+
+PrefillPlan plan_prefill(int BH, int N, int n, int chunk);
+
+struct PrefillArgs {
+  const void* q; const void* k; const void* v; void* o;
+  float* state;
+  float* workspace;
+  int BH, N, n, chunk;
+  float a;
+  bool in_bf16, out_bf16;
+  PrefillPlan plan;
+  hipStream_t stream;
+  hipEvent_t* events;  // 4 phase events or nullptr
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a);
+
+// Whether a (n, chunk, input dtype) combination is compiled.
+bool prefill_supported(int n, int chunk, bool in_bf16);
+
+}  // namespace taylor

@@ -1,0 +1,109 @@
+"""Host-side checks of the C ABI (no GPU needed: nothing here launches a kernel).
+
+The library must load, export every function include/taylor_attn.h declares,
+size states and workspaces by the closed forms of the paper ("A Taylor-Series
+Route to Linear-Time Transformers with a Fixed Number of Recurrent States",
+sections 3.4, 4 and 5.8), and reject bad arguments before any HIP call.
+"""
+import ctypes
+import json
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "taylor_attn.h")
+GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_figures.json")))
+
+
+@pytest.fixture(scope="module")
+def rsp():
+    from recurrent_state_phi_amd import build as B
+    if not os.path.exists(B.LIB):
+        B.build()
+    import recurrent_state_phi_amd as rsp
+    return rsp
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(taylor_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for want in ("taylor_state_init", "taylor_attn_prefill", "taylor_attn_decode"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(rsp):
+    lib = ctypes.CDLL(rsp.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(rsp.EXPORTED_SYMBOLS)
+
+
+def test_state_width_closed_form(rsp):
+    printed = GOLDEN["symmetric_widths_d16"]["value"]
+    for n in range(1, 7):
+        assert rsp.state_width(16, n) == sum(printed[:n])
+    for d in (1, 2, 6, 64):
+        for n in range(1, 6):
+            assert rsp.state_width(d, n) == sum(math.comb(d + m - 1, m) for m in range(n))
+    assert rsp.state_numel(16, 64, 3) == GOLDEN["state_elements_per_head_n3"]["value"]
+    # section 5.8: six terms at d = 16 / d = 64 with bfloat16 elements
+    g = GOLDEN["state_size_bf16_MB"]
+    assert round(rsp.state_numel(16, 64, 6) * 2 / 2 ** 20, 1) == g["d16_n6"]
+    assert round(rsp.state_numel(64, 64, 6) * 2 / 2 ** 30, 1) == g["d64_n6_per_head"]
+    assert rsp.state_width(0, 3) == -1 and rsp.state_width(16, 0) == -1
+
+
+def test_workspace_sizing(rsp):
+    # one segment per head when the heads alone fill the GPU: no workspace
+    assert rsp.prefill_workspace_bytes(64, 8, 4096, 3, 64) == 0
+    assert rsp.prefill_workspace_bytes(1, 1, 0, 3, 64) == 0
+    ws = rsp.prefill_workspace_bytes(4, 8, 8192, 3, 64)
+    nseg = ws // (4 * 8 * 9945 * 4)
+    assert ws == 4 * 8 * nseg * 9945 * 4 and nseg > 1
+    assert 4 * 8 * nseg >= 256
+
+
+def _prefill_rc(lib, **kw):
+    args = dict(q=None, k=None, v=None, o=None, state=None, B=1, H=1, N=64, d=16, d_v=64, n=3, a=1.0,
+                chunk=64, ind=0, outd=0, ws=None, wsb=0, stream=None)
+    args.update(kw)
+    return lib.taylor_attn_prefill(*args.values())
+
+
+def test_invalid_arguments_are_rejected_before_launch(rsp):
+    lib = rsp.raw_library()
+    assert _prefill_rc(lib) == -1                       # NULL pointers
+    assert b"NULL" in lib.taylor_last_error()
+    assert _prefill_rc(lib, d=32) == -2                 # shape not built
+    assert _prefill_rc(lib, d_v=128) == -2
+    assert _prefill_rc(lib, n=5) == -2
+    assert _prefill_rc(lib, chunk=48) == -2
+    assert _prefill_rc(lib, chunk=128, ind=0) == -2     # float32 path stops at chunk 64
+    assert _prefill_rc(lib, a=0.0) == -1
+    assert _prefill_rc(lib, a=float("nan")) == -1
+    assert _prefill_rc(lib, N=-1) == -1
+    assert _prefill_rc(lib, ind=7) == -1
+    assert _prefill_rc(lib, N=0) == 0                   # empty sequence: nothing to do
+    assert _prefill_rc(lib, B=0) == 0
+    # misaligned pointer (never dereferenced: rejected first)
+    assert _prefill_rc(lib, q=16, k=16, v=16, o=16, state=8) == -1
+    assert b"aligned" in lib.taylor_last_error()
+    # workspace too small for a multi-segment plan
+    assert _prefill_rc(lib, B=1, H=1, N=4096, q=16, k=16, v=16, o=16, state=16) == -1
+    assert b"workspace" in lib.taylor_last_error()
+    dec = lib.taylor_attn_decode
+    assert dec(None, None, None, None, None, 1, 1, 16, 64, 3, 1.0, 0, 0, None) == -1
+    assert dec(None, None, None, None, None, 1, 1, 16, 64, 9, 1.0, 0, 0, None) == -2
+    assert dec(None, None, None, None, None, 0, 4, 16, 64, 3, 1.0, 0, 0, None) == 0
+    assert lib.taylor_state_init(None, 1, 1, 16, 64, 3, None) == -1
+    assert lib.taylor_state_init(None, 0, 1, 16, 64, 3, None) == 0
+    assert lib.taylor_set_phase_events(None, 4) == -1
+    assert lib.taylor_set_phase_events(None, 0) == 0

@@ -1,0 +1,274 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (max over rows of ||o_t - o_t^oracle||_inf / ||o_t^oracle||_inf):
+1e-4 for float32 inputs, 2e-2 for bfloat16 inputs with float32 accumulation.
+Inputs come from taylor_inputs (seeded, identical on both sides).  Method:
+"A Taylor-Series Route to Linear-Time Transformers with a Fixed Number of
+Recurrent States" (arXiv 2610.20637), sections 3.1-3.5.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import taylor_inputs as TI
+from oracle import recurrent as R
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def rsp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import recurrent_state_phi_amd as rsp
+    return rsp
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def to_dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+def run_prefill(rsp, q, k, v, n, a, chunk, dtype, out_dtype=torch.float32, state=None):
+    B, H = q.shape[:2]
+    if state is None:
+        state = rsp.new_state(B, H, n, device=DEV)
+    o = rsp.prefill(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), state, n, a, chunk=chunk,
+                    out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), state
+
+
+def oracle_state(k, v, n):
+    """A_m = sum_i phi_m(k_i) [v_i; 1]^T stacked over m (Eq. (6)), float64, per head."""
+    k = k.astype(np.float64)
+    v1 = np.concatenate([v.astype(np.float64), np.ones(v.shape[:-1] + (1,))], axis=-1)
+    feats = np.concatenate([R.phi(k, m) for m in range(n)], axis=-1)      # [..., N, D]
+    return np.einsum("...nd,...nc->...dc", feats, v1)
+
+
+# ---------------------------------------------------------------------------
+# tiny config: B=1, H=1, N=256, d=16, d_v=64, n=3, a=1, float32
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_tiny_prefill_all_outputs(rsp, chunk):
+    say("tiny prefill f32 chunk", chunk)
+    q, k, v = TI.make_qkv(TI.SEEDS["tiny"], 1, 1, 256, 16, 64)
+    ref = oracle.taylor_direct(q, k, v, 3, 1.0)
+    got, _ = run_prefill(rsp, q, k, v, 3, 1.0, chunk, "f32")
+    assert oracle.rel_err_rowwise(got, ref) <= TOL["f32"]
+
+
+def test_tiny_decode_all_outputs(rsp):
+    say("tiny decode f32, 256 steps")
+    q, k, v = TI.make_qkv(TI.SEEDS["tiny"], 1, 1, 256, 16, 64)
+    ref = oracle.taylor_direct(q, k, v, 3, 1.0)
+    st = rsp.new_state(1, 1, 3, device=DEV)
+    qd, kd, vd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
+    outs = []
+    for t in range(256):
+        outs.append(rsp.decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), st, 3, 1.0))
+    got = torch.stack(outs, dim=2).cpu().numpy().astype(np.float64)
+    assert oracle.rel_err_rowwise(got, ref) <= TOL["f32"]
+
+
+# ---------------------------------------------------------------------------
+# orders, chunks, dtypes, ragged lengths
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 2, 3])
+@pytest.mark.parametrize("dtype,chunk", [("f32", 32), ("f32", 64), ("bf16", 32), ("bf16", 64), ("bf16", 128)])
+def test_prefill_ragged_vs_oracle(rsp, n, dtype, chunk):
+    say("prefill ragged", n, dtype, chunk)
+    q, k, v = TI.make_qkv(77, 2, 3, 1000, 16, 64, dtype=dtype)
+    ref = oracle.taylor_direct(q, k, v, n, 1.0)
+    got, st = run_prefill(rsp, q, k, v, n, 1.0, chunk, dtype)
+    assert oracle.rel_err_rowwise(got, ref) <= TOL[dtype]
+    S, T = (x.cpu().numpy().astype(np.float64) for x in rsp.state_views(st, 2, 3, n))
+    A = oracle_state(k, v, n)
+    scale = np.abs(A).max(axis=(-1, -2), keepdims=True)
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    assert np.abs(S - A[..., :64]).max() <= tol * scale.max()
+    assert np.abs(T - A[..., 64]).max() <= tol * scale.max()
+
+
+@pytest.mark.parametrize("N", [1, 2, 15, 17, 33, 64, 65, 129])
+def test_prefill_short_lengths(rsp, N):
+    say("prefill short", N)
+    q, k, v = TI.make_qkv(5, 1, 2, N, 16, 64)
+    ref = oracle.taylor_direct(q, k, v, 3, 0.8)
+    got, _ = run_prefill(rsp, q, k, v, 3, 0.8, 32, "f32")
+    assert oracle.rel_err_rowwise(got, ref) <= TOL["f32"]
+
+
+def test_bf16_output(rsp):
+    say("prefill bf16 out")
+    q, k, v = TI.make_qkv(6, 1, 4, 700, 16, 64, dtype="bf16")
+    ref = oracle.taylor_direct(q, k, v, 3, 1.0)
+    got, _ = run_prefill(rsp, q, k, v, 3, 1.0, 64, "bf16", out_dtype=torch.bfloat16)
+    assert oracle.rel_err_rowwise(got, ref) <= TOL["bf16"]
+
+
+def test_many_heads_single_segment(rsp):
+    """600 heads: the plan uses one segment per head (no workspace)."""
+    say("prefill 600 heads")
+    assert rsp.prefill_workspace_bytes(20, 30, 300, 3, 64) == 0
+    q, k, v = TI.make_qkv(8, 20, 30, 300, 16, 64, dtype="bf16")
+    rows = np.arange(0, 20 * 30 * 300, 37)
+    ref = oracle.taylor_direct(q, k, v, 3, 1.0, rows=rows)
+    got, _ = run_prefill(rsp, q, k, v, 3, 1.0, 64, "bf16")
+    assert oracle.rel_err_rowwise(got.reshape(-1, 64)[rows], ref) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# additivity, resume and prefill == decode loop (section 5.2, Eq. (7))
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_split_prefill_equals_whole(rsp, dtype):
+    say("split prefill", dtype)
+    q, k, v = TI.make_qkv(9, 2, 2, 900, 16, 64, dtype=dtype)
+    ref = oracle.taylor_direct(q, k, v, 3, 1.0)
+    whole, st_whole = run_prefill(rsp, q, k, v, 3, 1.0, 64, dtype)
+    t1 = 333
+    a_out, st = run_prefill(rsp, q[:, :, :t1], k[:, :, :t1], v[:, :, :t1], 3, 1.0, 64, dtype)
+    # checkpoint/resume: the state goes through host memory and back
+    st = st.cpu().to(DEV)
+    b_out, st = run_prefill(rsp, q[:, :, t1:], k[:, :, t1:], v[:, :, t1:], 3, 1.0, 64, dtype, state=st)
+    split = np.concatenate([a_out, b_out], axis=2)
+    assert oracle.rel_err_rowwise(split, ref) <= TOL[dtype]
+    assert oracle.rel_err_rowwise(split, whole) <= TOL[dtype]
+    sw, ss = st_whole.cpu().numpy(), st.cpu().numpy()
+    assert np.abs(sw - ss).max() <= (1e-5 if dtype == "f32" else 1e-2) * np.abs(sw).max()
+
+
+def test_prefill_equals_decode_loop(rsp):
+    say("prefill vs decode loop")
+    q, k, v = TI.make_qkv(10, 1, 3, 300, 16, 64)
+    pre, st_p = run_prefill(rsp, q, k, v, 3, 1.3, 64, "f32")
+    st = rsp.new_state(1, 3, 3, device=DEV)
+    qd, kd, vd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
+    outs = [rsp.decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), st, 3, 1.3)
+            for t in range(300)]
+    dec = torch.stack(outs, dim=2).cpu().numpy().astype(np.float64)
+    assert oracle.rel_err_rowwise(dec, pre) <= 2 * TOL["f32"]
+    assert np.abs(st.cpu().numpy() - st_p.cpu().numpy()).max() <= 1e-5 * np.abs(st_p.cpu().numpy()).max()
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_after_prefix(rsp, n, dtype):
+    say("decode after prefix", n, dtype)
+    B, H, N0, steps = 2, 3, 200, 24
+    q, k, v = TI.make_qkv(11, B, H, N0 + steps, 16, 64, dtype=dtype)
+    ref = oracle.taylor_direct(q, k, v, n, 1.0)
+    st = rsp.new_state(B, H, n, device=DEV)
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    for t in range(N0):  # build the prefix by decode (also covers n = 4)
+        rsp.decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), st, n, 1.0)
+    outs = [rsp.decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), st, n, 1.0)
+            for t in range(N0, N0 + steps)]
+    got = torch.stack(outs, dim=2).cpu().numpy().astype(np.float64)
+    assert oracle.rel_err_rowwise(got, ref[:, :, N0:]) <= TOL[dtype]
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size, on sampled rows
+# ---------------------------------------------------------------------------
+def sample_rows(B, H, N, per_head, chunk, seed=0):
+    rng = np.random.default_rng(seed)
+    rows = []
+    for bh in range(B * H):
+        pos = {0, N - 1, chunk - 1, chunk, min(N - 1, 2 * chunk + 1)}
+        pos.update(rng.integers(0, N, per_head).tolist())
+        rows.extend(bh * N + p for p in sorted(pos))
+    return np.asarray(rows, np.int64)
+
+
+def test_prefill_workload_sampled(rsp):
+    """B=4, H=8, N=8192, n=3, a=1, chunk=64, bfloat16 inputs, float32 out."""
+    say("prefill workload 4x8x8192 bf16")
+    B, H, N = 4, 8, 8192
+    q, k, v = TI.make_qkv(TI.SEEDS["prefill"], B, H, N, 16, 64, dtype="bf16")
+    got, st = run_prefill(rsp, q, k, v, 3, 1.0, 64, "bf16")
+    rows = sample_rows(B, H, N, 48, 64)
+    ref = oracle.taylor_direct(q, k, v, 3, 1.0, rows=rows)
+    assert oracle.rel_err_rowwise(got.reshape(-1, 64)[rows], ref) <= TOL["bf16"]
+    S, T = (x.cpu().numpy().astype(np.float64) for x in rsp.state_views(st, B, H, 3))
+    A = oracle_state(k[:1, :2], v[:1, :2], 3)
+    assert np.abs(T[:1, :2] - A[..., 64]).max() <= 2e-2 * np.abs(A[..., 64]).max()
+    assert np.abs(S[:1, :2] - A[..., :64]).max() <= 2e-2 * np.abs(A[..., :64]).max()
+
+
+@pytest.mark.parametrize("n", [1, 2, 3])
+def test_order_sweep_workload(rsp, n):
+    """B=2, H=8, N=4096, float32, a=1: all rows against the oracle."""
+    say("order sweep", n)
+    B, H, N = 2, 8, 4096
+    q, k, v = TI.make_qkv(TI.SEEDS["order_sweep"], B, H, N, 16, 64)
+    got, _ = run_prefill(rsp, q, k, v, n, 1.0, 64, "f32")
+    rows = sample_rows(B, H, N, 256, 64)
+    ref = oracle.taylor_direct(q, k, v, n, 1.0, rows=rows)
+    assert oracle.rel_err_rowwise(got.reshape(-1, 64)[rows], ref) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("variant", ["normalised", "unnormalised"])
+def test_long_prefill_workload(rsp, variant):
+    """B=1, H=16, N=65536, chunk=128, bfloat16 inputs; the unnormalised q,k ~ N(0, 4^2)
+    variant must be reported non-converged by the oracle while the GPU still matches it."""
+    say("long prefill", variant)
+    B, H, N = 1, 16, 65536
+    norm = variant == "normalised"
+    seed = TI.SEEDS["long" if norm else "long_unnormalised"]
+    q, k, v = TI.make_qkv(seed, B, H, N, 16, 64, normalize=norm, scale=4.0, dtype="bf16")
+    got, _ = run_prefill(rsp, q, k, v, 3, 1.0, 128, "bf16")
+    rows = sample_rows(B, H, N, 8, 128)
+    ref = oracle.taylor_direct(q, k, v, 3, 1.0, rows=rows)
+    assert oracle.rel_err_rowwise(got.reshape(-1, 64)[rows], ref) <= TOL["bf16"]
+    rep = oracle.convergence_report(q[:, :1, :256], k[:, :1, :256], v[:, :1, :256], 1.0, 6)
+    assert rep["non_converged"] == (not norm)
+
+
+def test_decode_workload_sampled(rsp):
+    """B=64 streams, H=8, n=3: states prefilled from an N=65536 context, then 256 steps (float32)."""
+    say("decode workload 64x8, ctx 65536, 256 steps")
+    B, H, N0, steps, n = 64, 8, 65536, 256, 3
+    heads = [(0, 0), (7, 3), (21, 5), (33, 1), (42, 7), (50, 2), (63, 6), (63, 0)]
+    # inputs of the sampled heads from the seeded generator; the other heads get
+    # seeded torch noise of the same distribution (they are computed but not compared)
+    g = torch.Generator(device=DEV).manual_seed(1234)
+    qd = torch.randn(B, H, N0 + steps, 16, device=DEV, generator=g)
+    kd = torch.randn(B, H, N0 + steps, 16, device=DEV, generator=g)
+    vd = torch.randn(B, H, N0 + steps, 64, device=DEV, generator=g)
+    qd = qd / qd.norm(dim=-1, keepdim=True)
+    kd = kd / kd.norm(dim=-1, keepdim=True)
+    host = {}
+    for b, h in heads:
+        q1, k1, v1 = TI.head_qkv(TI.SEEDS["decode"], b, h, N0 + steps, 16, 64)
+        host[(b, h)] = (q1, k1, v1)
+        qd[b, h] = torch.from_numpy(q1).to(DEV)
+        kd[b, h] = torch.from_numpy(k1).to(DEV)
+        vd[b, h] = torch.from_numpy(v1).to(DEV)
+    st = rsp.new_state(B, H, n, device=DEV)
+    rsp.prefill(qd[:, :, :N0].contiguous(), kd[:, :, :N0].contiguous(), vd[:, :, :N0].contiguous(), st, n, 1.0,
+                chunk=64)
+    qs = qd[:, :, N0:].permute(2, 0, 1, 3).contiguous()
+    ks = kd[:, :, N0:].permute(2, 0, 1, 3).contiguous()
+    vs = vd[:, :, N0:].permute(2, 0, 1, 3).contiguous()
+    del qd, kd, vd
+    outs = torch.empty(steps, B, H, 64, device=DEV)
+    for s in range(steps):
+        rsp.decode(qs[s], ks[s], vs[s], st, n, 1.0, out=outs[s])
+    got = outs.cpu().numpy().astype(np.float64)
+    for b, h in heads:
+        q1, k1, v1 = host[(b, h)]
+        rows = np.arange(N0, N0 + steps)
+        ref = oracle.taylor_direct(q1, k1, v1, n, 1.0, rows=rows)
+        assert oracle.rel_err_rowwise(got[:, b, h], ref) <= TOL["f32"], (b, h)
