@@ -197,6 +197,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: every (b, h) head is independent, so the path shards "
@@ -206,8 +209,22 @@ def main():
 
     import torch
 
-    import recurrent_state_phi_amd as rsp
     dev = "cuda:0"
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": src.numel() * 4, "calibrate_copy_bytes_written": dst.numel() * 4,
+                          "launches": 3}), flush=True)
+        return
+
+    import recurrent_state_phi_amd as rsp
+    if args.only == "decode":
+        eager_us, graph_us = time_decode(torch, rsp, dev, use_graph=not args.no_graph)
+        print(json.dumps({"decode_us_per_token_eager": eager_us, "decode_us_per_token_graph": graph_us}), flush=True)
+        return
     host, qkv = make_prefill_inputs(torch, dev)
     print(f"[bench] prefill inputs resident; timing {args.steps} steps", file=sys.stderr, flush=True)
     ms, phases, _ = time_prefill(torch, rsp, qkv, args.steps, args.warmup)
@@ -242,7 +259,7 @@ def main():
             "whole_step_hbm_frac": alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
         },
     }
-    if not args.no_decode:
+    if not args.no_decode and args.only == "all":
         print("[bench] decode: prefill 65536-token context for 512 heads, then 256 steps", file=sys.stderr, flush=True)
         eager_us, graph_us = time_decode(torch, rsp, dev, use_graph=not args.no_graph)
         best = min(x for x in (eager_us, graph_us) if x is not None)
