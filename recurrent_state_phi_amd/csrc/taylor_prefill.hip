@@ -15,19 +15,26 @@
 //                      caller's state
 //   3. chunk kernel  : each segment replays its chunks from its prefix.
 //
-// Layout of the work inside one 256-thread workgroup (4 waves):
-//   - the S part of the state (D x 64, float32) lives in MFMA accumulator
-//     registers for the whole segment: wave w owns value columns 16w..16w+15,
-//     a 16-row tile of S is one f32x4 per lane (rows 4*(lane/16)+r, column
-//     lane%16);
-//   - the ones-column T (D floats) lives in LDS;
-//   - per chunk, q/k (as float), v, phi_hat(Q), phi(K) and the masked
-//     polynomial block P are staged in LDS; every contraction is an MFMA
-//     (bfloat16 16x16x32 with float32 accumulation for bfloat16 inputs,
-//     float32 16x16x4 for float32 inputs).
+// Work inside one 256-thread workgroup (4 waves of 64):
+//   - the S part of the state (D x 64, float32) stays in MFMA accumulator
+//     registers for the whole segment; wave w owns value columns 16w..16w+15
+//     and a 16-row tile of S is one f32x4 per lane (rows 4*(lane/16)+r, column
+//     lane%16).  The ones-column T is column 0 of extra accumulator tiles.
+//   - global loads of chunk j+1 are issued into registers while chunk j is
+//     computed (software pipelining), so HBM latency overlaps the math; the
+//     outputs of chunk j are divided and stored while chunk j+1 is staged.
+//   - per chunk: q, k (as float), V^T, phi_hat(Q), phi(K) and the masked
+//     polynomial block P are staged in LDS and shared by the 4 waves; every
+//     contraction is an MFMA (bfloat16 16x16x32 with float32 accumulation for
+//     bfloat16 inputs, float32 16x16x4 for float32 inputs).
 //   - the state is read straight from the accumulators: for a bfloat16 read the
 //     two 16-row tiles of one 32-feature block are packed into one B operand,
-//     and the query features are fetched in the matching k-slot order.
+//     and the query features are fetched in the matching k-slot order.  The
+//     normaliser uses the same MFMAs: T (the ones-column of the state) is a
+//     B column for the read (split into bfloat16 high and low parts, so it
+//     keeps float32 accuracy), a ones column turns P into its row sums, and
+//     the T update is phi(K)^T times a ones column, accumulated in registers.
+//   - three barriers per chunk: inputs staged | features and P ready | chunk done.
 #include <type_traits>
 
 #include "taylor_device.h"
@@ -47,6 +54,14 @@ struct PrefillShape {
   static constexpr int KS = BF ? C + 8 : DP + 16;     // BF: PhK^T [DP][KS]; F32: PhK [C][KS]
   static constexpr int VS = BF ? C + 8 : kDV + 16;    // BF: V^T [64][VS];   F32: V [C][VS]
   static constexpr int PS = BF ? C + 8 : C + 1;       // P [C][PS]
+  // 16-byte global loads per chunk and per thread
+  static constexpr int QK_UNITS = BF ? 2 * C : 4 * C;     // units of q (and as many of k)
+  static constexpr int V_UNITS = BF ? 8 * C : 16 * C;     // units of v
+  static constexpr int NQK = (2 * QK_UNITS + 255) / 256;
+  static constexpr int NV = (V_UNITS + 255) / 256;
+  static constexpr int NTW = (NFT + 3) / 4;  // T tiles per wave (tile ft belongs to wave ft % 4)
+  // two workgroups per CU when registers and LDS allow it
+  static constexpr int MIN_WAVES = (BF && C <= 64) ? 2 : 1;
 };
 
 // p_n(y) = sum_{m<n} y^m / m!  (Horner), y = q.k / a.
@@ -66,7 +81,7 @@ __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
 template <int NT, bool BF, int C, bool FULL, typename TOUT>
-__global__ __launch_bounds__(256) void prefill_chunk_kernel(
+__global__ __launch_bounds__(256, (PrefillShape<NT, BF, C>::MIN_WAVES)) void prefill_chunk_kernel(
     const void* __restrict__ q_, const void* __restrict__ k_, const void* __restrict__ v_,
     TOUT* __restrict__ o,
     const float* __restrict__ pre_S, const float* __restrict__ pre_T, int pre_slots,
@@ -81,7 +96,11 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
   const IT* __restrict__ k = static_cast<const IT*>(k_);
   const IT* __restrict__ v = static_cast<const IT*>(v_);
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, li = lane & 15, g = lane >> 4;
+  // The wave index is made explicitly uniform (a scalar register): MFMA
+  // instructions ignore the EXEC mask, so every condition guarding one must be
+  // a scalar branch, never a per-lane predicate.
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int gseg = FULL ? nseg : nseg - 1;
   const int bh = blockIdx.x / gseg, seg = blockIdx.x % gseg;
   const int t_begin = seg * cps * C;
@@ -90,12 +109,16 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
 
   __shared__ __align__(16) float Xq[FULL ? C : 1][kD];
   __shared__ __align__(16) float Xk[C][kD];
+  __shared__ __align__(16) uint16_t Xqb[(FULL && BF) ? C : 1][kD];  // raw bfloat16 q, k for Q K^T
+  __shared__ __align__(16) uint16_t Xkb[BF ? C : 1][kD];
   __shared__ __align__(16) LT PhQ[FULL ? C : 1][Sh::QS];
   __shared__ __align__(16) LT PhK[BF ? DP : C][Sh::KS];
   __shared__ __align__(16) LT Vl[BF ? kDV : C][Sh::VS];
   __shared__ __align__(16) LT P[FULL ? C : 1][Sh::PS];
-  __shared__ float Ts[DP];
-  __shared__ float den[FULL ? C : 1];
+  // T published for the normaliser read: bfloat16 high/low parts, or float32
+  __shared__ __align__(16) uint16_t Thb[(FULL && BF) ? DP : 1], Tlb[(FULL && BF) ? DP : 1];
+  __shared__ __align__(16) float Ts[(FULL && !BF) ? DP : 1];
+  __shared__ __align__(16) float invden[FULL ? C : 1];  // 1 / normaliser of the chunk being finished
 
   // ---- the segment's starting state -------------------------------------
   f32x4 Sacc[NFT];
@@ -108,62 +131,162 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
         const int row = 16 * ft + 4 * g + r;
         Sacc[ft][r] = (ps && row < D) ? ps[(size_t)row * kDV + col] : 0.0f;
       }
-    if (tid < DP) {
-      const float* pt = pre_T ? pre_T + ((size_t)bh * pre_slots + (pre_slots == 1 ? 0 : seg)) * D : nullptr;
-      Ts[tid] = (pt && tid < D) ? pt[tid] : 0.0f;
-    }
+  }
+  // T lives in MFMA accumulators too: column 0 of tile ft (owned by wave ft % 4)
+  f32x4 Tacc[Sh::NTW];
+  {
+    const float* pt = pre_T ? pre_T + ((size_t)bh * pre_slots + (pre_slots == 1 ? 0 : seg)) * D : nullptr;
+#pragma unroll
+    for (int j = 0; j < Sh::NTW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (w + 4 * j) + 4 * g + r;
+        Tacc[j][r] = (pt && li == 0 && w + 4 * j < NFT && row < D) ? pt[row] : 0.0f;
+      }
   }
 
   const float a2 = inv_a * inv_a;
   const float am_q[3] = {1.0f, inv_a, 0.5f * a2};
-  const float am_k[3] = {1.0f, 1.0f, 1.0f};
 
-  for (int t0 = t_begin; t0 < t_end; t0 += C) {
-    const int nv = min(C, t_end - t0);
-    const size_t tok0 = (size_t)bh * N + t0;
-
-    // ---- phase 1: stage q, k (as float) and v ----------------------------
-    if constexpr (BF) {
-      constexpr int NQK = FULL ? 4 * C : 2 * C;  // 16-byte loads of q and k
-      for (int i = tid; i < NQK; i += 256) {
-        const bool isk = FULL ? (i >= 2 * C) : true;
-        const int rem = (FULL && isk) ? i - 2 * C : i;
-        const int tok = rem >> 1, half = rem & 1;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (tok < nv) raw = *reinterpret_cast<const uint4*>((isk ? k : q) + (tok0 + tok) * kD + 8 * half);
-        float* dst = isk ? &Xk[tok][8 * half] : &Xq[FULL ? tok : 0][8 * half];
-        *reinterpret_cast<float4*>(dst) = make_float4(bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y));
-        *reinterpret_cast<float4*>(dst + 4) = make_float4(bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w));
-      }
-      for (int i = tid; i < 8 * C; i += 256) {  // v -> V^T
-        const int tok = i >> 3, c8 = i & 7;
-        uint4 raw = make_uint4(0, 0, 0, 0);
-        if (tok < nv) raw = *reinterpret_cast<const uint4*>(v + (tok0 + tok) * kDV + 8 * c8);
-        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+  // ---- software-pipelined global loads -------------------------------------
+  // Unit i < QK_UNITS is a 16-byte piece of q, the next QK_UNITS are pieces of
+  // k; v units are one token's 8 (bfloat16) or 4 (float32) consecutive columns.
+  uint4 rqk[Sh::NQK], rv[Sh::NV];
+  auto issue_loads = [&](int c0) {
+    const int nvc = min(C, t_end - c0);
+    const size_t base = (size_t)bh * N + c0;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          Vl[8 * c8 + 2 * j][tok] = (uint16_t)(wd[j] & 0xFFFFu);
-          Vl[8 * c8 + 2 * j + 1][tok] = (uint16_t)(wd[j] >> 16);
+    for (int u = 0; u < Sh::NQK; ++u) {
+      const int i = tid + 256 * u;
+      rqk[u] = make_uint4(0, 0, 0, 0);
+      if (i < 2 * Sh::QK_UNITS) {
+        const bool isk = i >= Sh::QK_UNITS;
+        if (FULL || isk) {
+          const int rem = isk ? i - Sh::QK_UNITS : i;
+          const int tok = BF ? rem >> 1 : rem >> 2;
+          const int part = BF ? rem & 1 : rem & 3;
+          if (tok < nvc)
+            rqk[u] = *reinterpret_cast<const uint4*>((isk ? k : q) + (base + tok) * kD + (BF ? 8 : 4) * part);
         }
       }
-    } else {
-      constexpr int NQK = FULL ? 8 * C : 4 * C;  // float4 loads of q and k
-      for (int i = tid; i < NQK; i += 256) {
-        const bool isk = FULL ? (i >= 4 * C) : true;
-        const int rem = (FULL && isk) ? i - 4 * C : i;
-        const int tok = rem >> 2, qu = rem & 3;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tok < nv) x = *reinterpret_cast<const float4*>((isk ? k : q) + (tok0 + tok) * kD + 4 * qu);
-        float* dst = isk ? &Xk[tok][4 * qu] : &Xq[FULL ? tok : 0][4 * qu];
-        *reinterpret_cast<float4*>(dst) = x;
-      }
-      for (int i = tid; i < 16 * C; i += 256) {
-        const int tok = i >> 4, c4 = i & 15;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (tok < nv) x = *reinterpret_cast<const float4*>(v + (tok0 + tok) * kDV + 4 * c4);
-        *reinterpret_cast<float4*>(&Vl[tok][4 * c4]) = x;
+    }
+#pragma unroll
+    for (int u = 0; u < Sh::NV; ++u) {
+      const int i = tid + 256 * u;
+      rv[u] = make_uint4(0, 0, 0, 0);
+      if (i < Sh::V_UNITS) {
+        const int tok = BF ? i >> 3 : i >> 4;
+        const int part = BF ? i & 7 : i & 15;
+        if (tok < nvc) rv[u] = *reinterpret_cast<const uint4*>(v + (base + tok) * kDV + (BF ? 8 : 4) * part);
       }
     }
+  };
+  auto stage_loads = [&]() {
+#pragma unroll
+    for (int u = 0; u < Sh::NQK; ++u) {
+      const int i = tid + 256 * u;
+      if (i < 2 * Sh::QK_UNITS) {
+        const bool isk = i >= Sh::QK_UNITS;
+        if (FULL || isk) {
+          const int rem = isk ? i - Sh::QK_UNITS : i;
+          if constexpr (BF) {
+            const int tok = rem >> 1, half = rem & 1;
+            float* dst = isk ? &Xk[tok][8 * half] : &Xq[FULL ? tok : 0][8 * half];
+            const uint4 raw = rqk[u];
+            *reinterpret_cast<uint4*>(isk ? &Xkb[tok][8 * half] : &Xqb[(FULL && BF) ? tok : 0][8 * half]) = raw;
+            *reinterpret_cast<float4*>(dst) =
+                make_float4(bf16_lo(raw.x), bf16_hi(raw.x), bf16_lo(raw.y), bf16_hi(raw.y));
+            *reinterpret_cast<float4*>(dst + 4) =
+                make_float4(bf16_lo(raw.z), bf16_hi(raw.z), bf16_lo(raw.w), bf16_hi(raw.w));
+          } else {
+            const int tok = rem >> 2, qu = rem & 3;
+            float* dst = isk ? &Xk[tok][4 * qu] : &Xq[FULL ? tok : 0][4 * qu];
+            *reinterpret_cast<uint4*>(dst) = rqk[u];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < Sh::NV; ++u) {
+      const int i = tid + 256 * u;
+      if (i < Sh::V_UNITS) {
+        if constexpr (BF) {  // transpose into V^T [column][token]
+          const int tok = i >> 3, c8 = i & 7;
+          const uint32_t wd[4] = {rv[u].x, rv[u].y, rv[u].z, rv[u].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            Vl[8 * c8 + 2 * j][tok] = (uint16_t)(wd[j] & 0xFFFFu);
+            Vl[8 * c8 + 2 * j + 1][tok] = (uint16_t)(wd[j] >> 16);
+          }
+        } else {
+          const int tok = i >> 4, c4 = i & 15;
+          *reinterpret_cast<uint4*>(&Vl[tok][4 * c4]) = rv[u];
+        }
+      }
+    }
+  };
+  // Publish T (held by lanes li == 0) in LDS for the normaliser read.
+  auto publish_T = [&]() {
+    if constexpr (FULL) {
+      if (li == 0) {
+#pragma unroll
+        for (int j = 0; j < Sh::NTW; ++j) {
+          const int ft = w + 4 * j;
+          if (ft < NFT) {
+            const int row = 16 * ft + 4 * g;
+            if constexpr (BF) {
+              float lo[4];
+              uint16_t hb[4], lb[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const __bf16 h = f32_to_bf16(Tacc[j][r]);
+                lo[r] = Tacc[j][r] - (float)h;
+                hb[r] = __builtin_bit_cast(uint16_t, h);
+                lb[r] = __builtin_bit_cast(uint16_t, f32_to_bf16(lo[r]));
+              }
+              *reinterpret_cast<uint2*>(&Thb[row]) =
+                  make_uint2(hb[0] | (uint32_t)hb[1] << 16, hb[2] | (uint32_t)hb[3] << 16);
+              *reinterpret_cast<uint2*>(&Tlb[row]) =
+                  make_uint2(lb[0] | (uint32_t)lb[1] << 16, lb[2] | (uint32_t)lb[3] << 16);
+            } else {
+              *reinterpret_cast<float4*>(&Ts[row]) = make_float4(Tacc[j][0], Tacc[j][1], Tacc[j][2], Tacc[j][3]);
+            }
+          }
+        }
+      }
+    }
+  };
+
+  f32x4 Y[NTT];  // this wave's outputs of the chunk being finished
+  int prev_t0 = -1, prev_nv = 0;
+  // o = Y / den for the previous chunk (den in LDS, Y in registers).
+  auto epilogue = [&]() {
+    if constexpr (FULL) {
+      if (prev_t0 >= 0) {
+        const size_t tok0 = (size_t)bh * N + prev_t0;
+#pragma unroll
+        for (int mt = 0; mt < NTT; ++mt) {
+          const float4 inv = *reinterpret_cast<const float4*>(&invden[16 * mt + 4 * g]);
+          const float iv[4] = {inv.x, inv.y, inv.z, inv.w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int row = 16 * mt + 4 * g + r;
+            if (row < prev_nv) Elem<TOUT>::store(o, (tok0 + row) * kDV + col, Y[mt][r] * iv[r]);
+          }
+        }
+      }
+    }
+  };
+
+  issue_loads(t_begin);
+  for (int t0 = t_begin; t0 < t_end; t0 += C) {
+    const int nv = min(C, t_end - t0);
+
+    // ---- phase 1: stage chunk j, prefetch chunk j+1, finish chunk j-1 ----
+    publish_T();
+    stage_loads();
+    if (t0 + C < t_end) issue_loads(t0 + C);
+    epilogue();
     __syncthreads();
 
     // ---- phase 2: feature maps phi_hat(Q) and phi(K) ---------------------
@@ -179,31 +302,29 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             const float4 t = *reinterpret_cast<const float4*>(src + j);
             x[j] = t.x; x[j + 1] = t.y; x[j + 2] = t.z; x[j + 3] = t.w;
           }
-          float vals[F1 - F0];
-          for_features<NT, F0, F1>(x, ISQ ? am_q : am_k, [&](int f, float val) { vals[f] = val; });
-          if constexpr (ISQ) {
-            if constexpr (BF) {
+          // padding tokens have x = 0, so only their constant feature needs masking
+          const float am_k[3] = {tok < nv ? 1.0f : 0.0f, 1.0f, 1.0f};
+          float grp[4];
+          for_features<NT, F0, F1>(x, ISQ ? am_q : am_k, [&](int f, float val) {
+            if constexpr (ISQ) {
+              grp[f & 3] = val;
+              if ((f & 3) == 3) {
+                if constexpr (BF) {
+                  *reinterpret_cast<uint2*>(&PhQ[FULL ? tok : 0][F0 + f - 3]) =
+                      make_uint2(pack_bf16x2(grp[0], grp[1]), pack_bf16x2(grp[2], grp[3]));
+                } else {
 #pragma unroll
-              for (int f = 0; f < F1 - F0; f += 4) {
-                const uint2 pk = make_uint2(pack_bf16x2(vals[f], vals[f + 1]), pack_bf16x2(vals[f + 2], vals[f + 3]));
-                *reinterpret_cast<uint2*>(&PhQ[FULL ? tok : 0][F0 + f]) = pk;
+                  for (int j = 0; j < 4; ++j) PhQ[FULL ? tok : 0][F0 + f - 3 + j] = grp[j];
+                }
               }
             } else {
-#pragma unroll
-              for (int f = 0; f < F1 - F0; ++f) PhQ[FULL ? tok : 0][F0 + f] = vals[f];
-            }
-          } else {
-            const bool valid = tok < nv;  // padding tokens must not reach the state
-#pragma unroll
-            for (int f = 0; f < F1 - F0; ++f) {
-              const float val = valid ? vals[f] : 0.0f;
               if constexpr (BF) {
                 PhK[F0 + f][tok] = __builtin_bit_cast(uint16_t, f32_to_bf16(val));
               } else {
                 PhK[tok][F0 + f] = val;
               }
             }
-          }
+          });
         }
       };
       using T_ = std::true_type;
@@ -222,23 +343,20 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
         else phi_rows(F_{}, std::integral_constant<int, 3 * Q4>{}, std::integral_constant<int, DP>{});
       }
     }
-    __syncthreads();
 
     if constexpr (FULL) {
-      // ---- phase 3: masked polynomial block P and the normaliser ----------
+      // ---- phase 3: masked polynomial block P ------------------------------
       for (int tt = w; tt < NTT; tt += 4) {
         const int tok = 16 * tt + li;
-        float dsum = 0.0f;
+        bf16x4 bq = {};
+        if constexpr (BF) bq = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&Xqb[tok][4 * g]));
         const int ktmax = min(tt | 1, NTT - 1);
         for (int kt = 0; kt <= ktmax; ++kt) {
           float p[4] = {0.f, 0.f, 0.f, 0.f};
           if (kt <= tt) {
             f32x4 s = {0.f, 0.f, 0.f, 0.f};
             if constexpr (BF) {
-              const float4 xk = *reinterpret_cast<const float4*>(&Xk[16 * kt + li][4 * g]);
-              const float4 xq = *reinterpret_cast<const float4*>(&Xq[tok][4 * g]);
-              const bf16x4 ak = {f32_to_bf16(xk.x), f32_to_bf16(xk.y), f32_to_bf16(xk.z), f32_to_bf16(xk.w)};
-              const bf16x4 bq = {f32_to_bf16(xq.x), f32_to_bf16(xq.y), f32_to_bf16(xq.z), f32_to_bf16(xq.w)};
+              const bf16x4 ak = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&Xkb[16 * kt + li][4 * g]));
               s = mfma_bf16_k16(ak, bq, s);
             } else {
 #pragma unroll
@@ -252,39 +370,19 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             }
           }
           if constexpr (BF) {
-            const uint32_t lo = pack_bf16x2(p[0], p[1]), hi = pack_bf16x2(p[2], p[3]);
-            dsum += bf16_lo(lo) + bf16_hi(lo) + bf16_lo(hi) + bf16_hi(hi);
-            *reinterpret_cast<uint2*>(&P[tok][16 * kt + 4 * g]) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(&P[tok][16 * kt + 4 * g]) =
+                make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]));
           } else {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              dsum += p[r];
-              P[tok][16 * kt + 4 * g + r] = p[r];
-            }
+            for (int r = 0; r < 4; ++r) P[tok][16 * kt + 4 * g + r] = p[r];
           }
         }
-        // off-diagonal part of the normaliser: phi_hat(q_t) . T
-        float part = 0.0f;
-        constexpr int FQ = DP / 4;
-        if constexpr (BF) {
-#pragma unroll
-          for (int f = 0; f < FQ; f += 4) {
-            const uint2 u = *reinterpret_cast<const uint2*>(&PhQ[tok][g * FQ + f]);
-            part += bf16_lo(u.x) * Ts[g * FQ + f] + bf16_hi(u.x) * Ts[g * FQ + f + 1] +
-                    bf16_lo(u.y) * Ts[g * FQ + f + 2] + bf16_hi(u.y) * Ts[g * FQ + f + 3];
-          }
-        } else {
-#pragma unroll
-          for (int f = 0; f < FQ; ++f) part += PhQ[tok][g * FQ + f] * Ts[g * FQ + f];
-        }
-        float tot = dsum + part;
-        tot += __shfl_xor(tot, 16);
-        tot += __shfl_xor(tot, 32);
-        if (g == 0) den[tok] = tot;
       }
-      __syncthreads();
+    }
+    __syncthreads();
 
-      // ---- phase 4: Y = phi_hat(Q) S + P V, then o = Y / den -------------
+    if constexpr (FULL) {
+      // ---- phase 4: Y = phi_hat(Q) S + P V and the normaliser --------------
       if constexpr (BF) {
         bf16x8 bs[NFT / 2];
 #pragma unroll
@@ -294,82 +392,109 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             bs[kb][r] = f32_to_bf16(Sacc[2 * kb][r]);
             bs[kb][4 + r] = f32_to_bf16(Sacc[2 * kb + 1][r]);
           }
+        const uint32_t one2 = li == 0 ? 0x3F803F80u : 0u;  // bfloat16 1.0 pair in column 0
+        const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
+        const uint16_t* tsrc = li == 0 ? Thb : Tlb;
+#pragma unroll
         for (int mt = 0; mt < NTT; ++mt) {
           const int tok = 16 * mt + li;
           f32x4 y = {0.f, 0.f, 0.f, 0.f};
+          f32x4 yd = {0.f, 0.f, 0.f, 0.f};
+          const bool mine = (mt & 3) == w;  // this wave produces the normaliser of token tile mt
 #pragma unroll
           for (int kb = 0; kb < NFT / 2; ++kb) {
             const uint2 lo = *reinterpret_cast<const uint2*>(&PhQ[tok][32 * kb + 4 * g]);
             const uint2 hi = *reinterpret_cast<const uint2*>(&PhQ[tok][32 * kb + 16 + 4 * g]);
-            const uint4 a4 = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            y = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a4), bs[kb], y);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            y = mfma_bf16_k32(a, bs[kb], y);
+            if (mine) {
+              // T as B column 0 (high part) and column 1 (low part), same k-slot order
+              uint2 t0 = *reinterpret_cast<const uint2*>(&tsrc[32 * kb + 4 * g]);
+              uint2 t1 = *reinterpret_cast<const uint2*>(&tsrc[32 * kb + 16 + 4 * g]);
+              if (li >= 2) t0 = t1 = make_uint2(0, 0);
+              yd = mfma_bf16_k32(a, __builtin_bit_cast(bf16x8, make_uint4(t0.x, t0.y, t1.x, t1.y)), yd);
+            }
           }
           const int nkb = (16 * mt + 15) / 32 + 1;
           for (int kb = 0; kb < nkb; ++kb) {
-            const uint4 a4 = *reinterpret_cast<const uint4*>(&P[tok][32 * kb + 8 * g]);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&P[tok][32 * kb + 8 * g]));
             const uint4 b4 = *reinterpret_cast<const uint4*>(&Vl[col][32 * kb + 8 * g]);
-            y = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a4), __builtin_bit_cast(bf16x8, b4), y);
+            y = mfma_bf16_k32(a, __builtin_bit_cast(bf16x8, b4), y);
+            if (mine) yd = mfma_bf16_k32(a, ones, yd);  // row sums of P into column 0
           }
+          Y[mt] = y;
+          if (mine) {
+            // lanes li = 0 / 1 hold column 0 / 1 for tokens 16mt + 4g + r
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 16 * mt + 4 * g + r;
-            if (row < nv) Elem<TOUT>::store(o, (tok0 + row) * kDV + col, y[r] / den[row]);
+            for (int r = 0; r < 4; ++r) {
+              const float dn = yd[r] + __shfl_down(yd[r], 1);
+              if (li == 0) invden[16 * mt + 4 * g + r] = 1.0f / dn;
+            }
           }
         }
       } else {
+        const float one = li == 0 ? 1.0f : 0.0f;
+#pragma unroll
         for (int mt = 0; mt < NTT; ++mt) {
           const int tok = 16 * mt + li;
           f32x4 y = {0.f, 0.f, 0.f, 0.f};
+          f32x4 yd = {0.f, 0.f, 0.f, 0.f};
+          const bool mine = (mt & 3) == w;
 #pragma unroll
           for (int ft = 0; ft < NFT; ++ft)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) y = mfma_f32_k4(PhQ[tok][16 * ft + 4 * g + r], Sacc[ft][r], y);
+            for (int r = 0; r < 4; ++r) {
+              const float a = PhQ[tok][16 * ft + 4 * g + r];
+              y = mfma_f32_k4(a, Sacc[ft][r], y);
+              if (mine) yd = mfma_f32_k4(a, li == 0 ? Ts[16 * ft + 4 * g + r] : 0.0f, yd);
+            }
           const int nst = (16 * mt + 16) / 4;
-          for (int st = 0; st < nst; ++st) y = mfma_f32_k4(P[tok][4 * st + g], Vl[4 * st + g][col], y);
+          for (int st = 0; st < nst; ++st) {
+            const float a = P[tok][4 * st + g];
+            y = mfma_f32_k4(a, Vl[4 * st + g][col], y);
+            if (mine) yd = mfma_f32_k4(a, one, yd);
+          }
+          Y[mt] = y;
+          if (mine && li == 0) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = 16 * mt + 4 * g + r;
-            if (row < nv) Elem<TOUT>::store(o, (tok0 + row) * kDV + col, y[r] / den[row]);
+            for (int r = 0; r < 4; ++r) invden[16 * mt + 4 * g + r] = 1.0f / yd[r];
           }
         }
       }
+      prev_t0 = t0;
+      prev_nv = nv;
     }
 
-    // ---- phase 5: A += phi(K)^T [V, 1] -------------------------------------
+    // ---- phase 5: S += phi(K)^T V and T += phi(K)^T 1 ----------------------
     if constexpr (BF) {
+      const uint32_t one2 = li == 0 ? 0x3F803F80u : 0u;
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
 #pragma unroll
       for (int kb = 0; kb < C / 32; ++kb) {
         const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&Vl[col][32 * kb + 8 * g]));
 #pragma unroll
         for (int ft = 0; ft < NFT; ++ft) {
-          const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&PhK[16 * ft + li][32 * kb + 8 * g]));
+          const bf16x8 a =
+              __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&PhK[16 * ft + li][32 * kb + 8 * g]));
           Sacc[ft] = mfma_bf16_k32(a, b, Sacc[ft]);
+          if ((ft & 3) == w) Tacc[ft >> 2] = mfma_bf16_k32(a, ones, Tacc[ft >> 2]);
         }
-      }
-      if (tid < DP) {
-        float s = 0.0f;
-#pragma unroll
-        for (int t = 0; t < C; t += 8) {
-          const uint4 u = *reinterpret_cast<const uint4*>(&PhK[tid][t]);
-          s += bf16_lo(u.x) + bf16_hi(u.x) + bf16_lo(u.y) + bf16_hi(u.y) + bf16_lo(u.z) + bf16_hi(u.z) +
-               bf16_lo(u.w) + bf16_hi(u.w);
-        }
-        Ts[tid] += s;
       }
     } else {
+      const float one = li == 0 ? 1.0f : 0.0f;
       for (int st = 0; st < C / 4; ++st) {
         const float b = Vl[4 * st + g][col];
 #pragma unroll
-        for (int ft = 0; ft < NFT; ++ft) Sacc[ft] = mfma_f32_k4(PhK[4 * st + g][16 * ft + li], b, Sacc[ft]);
-      }
-      if (tid < DP) {
-        float s = 0.0f;
-        for (int t = 0; t < C; ++t) s += PhK[t][tid];
-        Ts[tid] += s;
+        for (int ft = 0; ft < NFT; ++ft) {
+          const float a = PhK[4 * st + g][16 * ft + li];
+          Sacc[ft] = mfma_f32_k4(a, b, Sacc[ft]);
+          if ((ft & 3) == w) Tacc[ft >> 2] = mfma_f32_k4(a, one, Tacc[ft >> 2]);
+        }
       }
     }
     __syncthreads();
   }
+  epilogue();
 
   // ---- write the state out -------------------------------------------------
   const bool write = FULL ? (seg == nseg - 1) : true;
@@ -383,7 +508,15 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
         const int row = 16 * ft + 4 * g + r;
         if (row < D) ds[(size_t)row * kDV + col] = Sacc[ft][r];
       }
-    if (tid < D) dst_T[slot * D + tid] = Ts[tid];
+    if (li == 0) {
+#pragma unroll
+      for (int j = 0; j < Sh::NTW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * (w + 4 * j) + 4 * g + r;
+          if (w + 4 * j < NFT && row < D) dst_T[slot * D + row] = Tacc[j][r];
+        }
+    }
   }
 }
 
