@@ -20,9 +20,9 @@ GOLDEN = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_figures.jso
 
 @pytest.fixture(scope="module")
 def rsp():
-    from recurrent_state_phi_amd import build as B
-    if not os.path.exists(B.LIB):
-        B.build()
+    if not os.path.exists(os.path.join(ROOT, "recurrent_state_phi_amd", "libtaylor_attn.so")):
+        import __graft_entry__
+        __graft_entry__.build()
     import recurrent_state_phi_amd as rsp
     return rsp
 
