@@ -42,6 +42,14 @@ struct PrefillArgs {
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 
+// n = 3, bfloat16 inputs, chunk 64 or 128 (taylor_prefill_n3.hip).
+hipError_t launch_prefill_n3_bf16(const PrefillArgs& a);
+
+// Exclusive scan of the per-segment state sums in place, seeded with the
+// caller's state (taylor_prefill.hip).
+hipError_t launch_segment_scan(const float* st_S, const float* st_T, float* W_S, float* W_T, int D, int nseg, int BH,
+                               hipStream_t stream);
+
 // Whether a (n, chunk, input dtype) combination is compiled.
 bool prefill_supported(int n, int chunk, bool in_bf16);
 

@@ -543,18 +543,35 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restri
     slot0 = W_T + (size_t)bh * nseg * D + (e - nS);
     stride = D;
   }
+  // Blocks of 16 slots: all loads of a block are issued before any store, so
+  // they are in flight together.
   float run = *src;
-  for (int s = 0; s < nseg; ++s) {
-    float* p = slot0 + (size_t)s * stride;
-    const float tmp = (s < nseg - 1) ? *p : 0.0f;
-    *p = run;
-    run += tmp;
+  for (int s0 = 0; s0 < nseg; s0 += 16) {
+    float tmp[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = s0 + i;
+      tmp[i] = (s < nseg - 1) ? slot0[(size_t)s * stride] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = s0 + i;
+      if (s < nseg) slot0[(size_t)s * stride] = run;
+      run += tmp[i];
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
+hipError_t launch_segment_scan(const float* st_S, const float* st_T, float* W_S, float* W_T, int D, int nseg, int BH,
+                               hipStream_t stream) {
+  dim3 sgrid((D * (kDV + 1) + 255) / 256, BH);
+  hipLaunchKernelGGL(segment_scan_kernel, sgrid, dim3(256), 0, stream, st_S, st_T, W_S, W_T, D, nseg);
+  return hipGetLastError();
+}
+
 PrefillPlan plan_prefill(int BH, int N, int n, int chunk) {
   PrefillPlan p;
   if (BH <= 0 || N <= 0 || chunk <= 0) return p;
@@ -593,8 +610,7 @@ static hipError_t launch_prefill_t(const PrefillArgs& a) {
                        a.stream, a.q, a.k, a.v, static_cast<TOUT*>(nullptr), (const float*)nullptr,
                        (const float*)nullptr, 1, W_S, W_T, pl.nseg, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
     if (ev) (void)hipEventRecord(ev[1], a.stream);
-    dim3 sgrid((D * (kDV + 1) + 255) / 256, a.BH);
-    hipLaunchKernelGGL(segment_scan_kernel, sgrid, dim3(256), 0, a.stream, st_S, st_T, W_S, W_T, D, pl.nseg);
+    if (hipError_t e = launch_segment_scan(st_S, st_T, W_S, W_T, D, pl.nseg, a.BH, a.stream)) return e;
     if (ev) (void)hipEventRecord(ev[2], a.stream);
     hipLaunchKernelGGL((prefill_chunk_kernel<NT, BF, C, true, TOUT>), dim3(a.BH * pl.nseg), dim3(256), 0, a.stream,
                        a.q, a.k, a.v, static_cast<TOUT*>(a.o), W_S, W_T, pl.nseg, st_S, st_T, 1, a.N, pl.nseg,
@@ -638,7 +654,9 @@ hipError_t launch_prefill(const PrefillArgs& a) {
   switch (a.n) {
     case 1: return launch_prefill_n<1>(a);
     case 2: return launch_prefill_n<2>(a);
-    case 3: return launch_prefill_n<3>(a);
+    case 3:
+      if (a.in_bf16 && (a.chunk == 64 || a.chunk == 128)) return launch_prefill_n3_bf16(a);
+      return launch_prefill_n<3>(a);
   }
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,588 @@
+// Chunked prefill for n = 3 with bfloat16 q, k, v (section 3.5 of "A Taylor-Series
+// Route to Linear-Time Transformers with a Fixed Number of Recurrent States",
+// arXiv 2610.20637): float32 state, bfloat16 matrix-core operands, float32
+// accumulation.
+//
+// Same three-launch structure as the generic kernel (segment sums, scan of the
+// segment sums, replay of every segment from its prefix), but the work inside a
+// 256-thread workgroup is split so that no feature value is computed twice and
+// the large operands never make a round trip through LDS:
+//
+//  * The state read Y^T = S'^T phi'(Q)^T (the off-diagonal part of Eq. (5)) and
+//    the diagonal block Y^T += [V, 1]^T P^T are split by TOKEN tile: wave w owns
+//    tokens 16w..16w+15 of a 64-token chunk (and 16(w+4).. for 128-token chunks).
+//    The query features are built directly in the MFMA operand registers; the
+//    score block Q K^T, the polynomial P and its row sums never leave registers.
+//  * The state update S' += phi(K)^T [V, 1] (Eq. (6)-(7) summed over the chunk)
+//    is split by FEATURE tile: wave w owns tiles {w, w+4} for all 64 value
+//    columns and half of tile 8 + w/2.  The key features are built in operand
+//    registers from a transposed float32 copy of K; the ones-column T is the
+//    same product against a ones operand, on the matrix cores as well.
+//  * After its update every wave writes its part of the new state as a
+//    bfloat16 copy of S'^T into LDS (double buffered) for the next chunk's read.
+//    One barrier per chunk.
+//
+// Internal feature order ("R1"): 10 tiles of 16 rows.  Tile f < 8 holds the
+// products x_r x_{(r+f) mod 16} for r = 0..15 (every unordered pair {i, j}
+// exactly once: f is the forward distance j - i mod 16 when that is < 8);
+// tile 8 holds x_r x_{r+8} for r < 8, then the constant feature (row 8) and
+// seven zero rows; tile 9 holds the linear features x_r.  Internally the state
+// rows are UNWEIGHTED sums of monomials; the sqrt-multinomial weight of
+// section 3.4 appears squared (2 for i != j) on the query side instead, and is
+// applied when the state is loaded from or stored to the caller's layout.
+//
+// The k-slot order of the state read pairs the tiles (0,2), (1,3), (4,6),
+// (5,7), (8,9) into the five 32-wide k blocks; lane group g = 2*gh + h of the
+// MFMA operand takes rows 8h..8h+7 of the gh-th tile of the pair.  With
+// y = x rotated by 8h and z = x rotated by 8h + 2gh, the lane's 8 features of a
+// k block are y_s z_{(s + d) mod 16} for compile-time s and d, so the query
+// features need no runtime register indexing.
+#include <type_traits>
+
+#include "taylor_device.h"
+#include "taylor_launch.h"
+
+namespace taylor {
+namespace n3 {
+
+constexpr int kD3 = 153;   // state rows in the caller's layout
+constexpr int kNF = 160;   // internal feature rows (10 tiles)
+constexpr int kSS = 168;   // row stride (bf16) of the S'^T copy (84 dwords: conflict-free 16-byte reads)
+constexpr int kQS = 36;    // row stride (bf16) of the doubled q copy
+constexpr int kOnes = 16;  // K^T row holding 1 for valid tokens, 0 for padding
+constexpr int kZero = 17;  // index standing for the zero row (stored once, outside the double buffer)
+constexpr int kKTRows = 17;
+
+template <int C>
+struct Shape {
+  static constexpr int NTT = C / 16;   // 16-token tiles per chunk
+  static constexpr int NKB = C / 32;   // 32-token k blocks per chunk
+  static constexpr int TPW = NTT / 4;  // token tiles per wave
+  static constexpr int VS = C + 8;     // V^T row stride (bf16)
+  static constexpr int KS = C + 4;     // K^T row stride (float)
+};
+
+template <int C, bool FULL>
+struct Lds {
+  alignas(16) uint16_t S[FULL ? 2 : 1][FULL ? 64 : 1][kSS];  // S'^T copy (bf16), k-slot order, swizzled
+  alignas(16) uint16_t T[FULL ? 2 : 1][2][kNF];             // T' in k-slot order: bf16 high, low parts
+  alignas(16) uint16_t Tz[FULL ? kNF : 8];                   // zeros (the other rows of the T operand)
+  alignas(16) uint16_t V[2][64][Shape<C>::VS];               // V^T (bf16), swizzled
+  alignas(16) float K[2][kKTRows][Shape<C>::KS];             // K^T (float) + ones row
+  alignas(16) float Kz[Shape<C>::KS];                        // zero row
+  alignas(16) uint16_t Q[FULL ? 2 : 1][FULL ? C : 1][kQS];   // q twice per row: [x | x]
+};
+
+// 16-byte-chunk XOR swizzle of the rows of V^T: rows c and c + 16 land in
+// different banks.
+__device__ __forceinline__ int swz(int row, int e) { return (((e >> 3) ^ ((row >> 4) & 3)) << 3) | (e & 7); }
+
+// k-slot of internal row rho of tile ft in the state read.
+__device__ __forceinline__ int kslot_of(int ft, int rho) {
+  int kb, gh;
+  if (ft < 8) {
+    kb = (ft >> 2) * 2 + (ft & 1);
+    gh = (ft >> 1) & 1;
+  } else {
+    kb = 4;
+    gh = ft - 8;
+  }
+  return 32 * kb + 8 * (2 * gh + (rho >> 3)) + (rho & 7);
+}
+
+// Row of the caller's layout (m ascending, lexicographic multi-indices) for
+// internal row rho of tile ft, or -1 for a zero row; *w gets the
+// sqrt-multinomial weight of that row.
+// (Written with selects only: it is evaluated per lane next to global loads,
+// which must not end up in divergent branches.)
+__device__ __forceinline__ int abi_row(int ft, int rho, float* w) {
+  const int j = ft < 8 ? ((rho + ft) & 15) : rho + 8;
+  const int lo = rho < j ? rho : j, hi = rho < j ? j : rho;
+  const int quad = 1 + kD + lo * kD - (lo * (lo - 1)) / 2 + (hi - lo);
+  const bool pair = ft < 8 || (ft == 8 && rho < 8);
+  *w = ft == 9 ? 1.0f : (pair ? (ft == 0 ? 1.0f : kSqrt2) : (rho == 8 ? 1.0f : 0.0f));
+  return ft == 9 ? 1 + rho : (pair ? quad : (rho == 8 ? 0 : -1));
+}
+
+// K^T rows whose product is internal row rho of tile ft.
+__device__ __forceinline__ int k_row_j(int ft, int rho) {
+  if (ft < 8) return (rho + ft) & 15;
+  if (ft == 8) return rho < 8 ? rho + 8 : (rho == 8 ? kOnes : kZero);
+  return kOnes;
+}
+
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  const bf16x2 p = {f32_to_bf16(lo), f32_to_bf16(hi)};
+  return __builtin_bit_cast(uint32_t, p);
+}
+__device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+template <int C, bool FULL, typename TOUT>
+__global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    TOUT* __restrict__ o, const float* __restrict__ pre_S, const float* __restrict__ pre_T, int pre_slots,
+    float* __restrict__ dst_S, float* __restrict__ dst_T, int dst_slots, int N, int nseg, int cps, float inv_a) {
+  using Sh = Shape<C>;
+  constexpr int NKB = Sh::NKB;
+  // The chunk buffers, and at the start and the end of the kernel a float
+  // [153 * 65] image of the state in the caller's layout (loaded and stored
+  // with full 16-byte accesses; the lanes then pick their rows from LDS).
+  constexpr int kImg = kD3 * (kDV + 1);
+  __shared__ __align__(16) unsigned char lds_raw[sizeof(Lds<C, FULL>) > kImg * 4 ? sizeof(Lds<C, FULL>) : kImg * 4];
+  Lds<C, FULL>& L = *reinterpret_cast<Lds<C, FULL>*>(lds_raw);
+  float* img = reinterpret_cast<float*>(lds_raw);
+
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  // wave index in a scalar register: every branch around an MFMA is uniform
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int gseg = FULL ? nseg : nseg - 1;
+  const int bh = blockIdx.x / gseg, seg = blockIdx.x % gseg;
+  const int t_begin = seg * cps * C;
+  const int t_end = min(N, t_begin + cps * C);
+  const int nchunks = (t_end - t_begin + C - 1) / C;
+
+  // ---- owned feature tiles: slot 0 = w, slot 1 = w + 4 (all 4 column tiles),
+  //      slot 2 = 8 + w/2 (column tiles ctb, ctb + 1).  T of slot 2 belongs to
+  //      waves 0 (tile 8) and 2 (tile 9).
+  const int ft_of[3] = {w, w + 4, 8 + (w >> 1)};
+  const int ctb = 2 * (w & 1);
+  const bool own_t2 = (w & 1) == 0;
+  int krow_j[3];
+#pragma unroll
+  for (int s = 0; s < 3; ++s) krow_j[s] = k_row_j(ft_of[s], li);
+  // the constant feature (tile 8, row 8): first factor 1 instead of x_8 (the
+  // second factor is the ones row, which masks padding tokens)
+  const bool const_lane = (w >> 1) == 0 && li == 8;
+
+  f32x4 acc[3][4];
+  f32x4 tacc[3];  // T' on the matrix cores: column 0 (lanes li == 0) of a 16x16 tile
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    tacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[s][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  if (FULL && pre_S != nullptr) {  // uniform
+    const size_t slot = (size_t)bh * pre_slots + (pre_slots == 1 ? 0 : seg);
+    const float4* ps4 = reinterpret_cast<const float4*>(pre_S + slot * kD3 * kDV);
+    const float* pt = pre_T + slot * kD3;
+    for (int i = tid; i < kD3 * kDV / 4; i += 256) reinterpret_cast<float4*>(img)[i] = ps4[i];
+    for (int i = tid; i < kD3; i += 256) img[kD3 * kDV + i] = pt[i];
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float wt;
+        const int row = abi_row(ft_of[s], 4 * g + r, &wt);
+        const int rc = max(row, 0);
+        const float sc = row >= 0 ? 1.0f / wt : 0.0f;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          if (s < 2 || ct < 2) acc[s][ct][r] = img[rc * kDV + 16 * (s == 2 ? ctb + ct : ct) + li] * sc;
+        tacc[s][r] = li == 0 ? img[kD3 * kDV + rc] * sc : 0.0f;
+      }
+    __syncthreads();  // the image area is reused by the chunk buffers
+  }
+
+
+  // ---- global loads: 16-byte units.  FULL: [q: 2C | k: 2C | v: 8C];
+  //      otherwise [k: 2C | v: 8C].  Chunk c is loaded into register set c % 2
+  //      two chunks ahead of its use.  Every load is issued unconditionally
+  //      (addresses clamped into the segment, the values of padding tokens are
+  //      zeroed when staged), so the number of loads in flight is the same on
+  //      every path and the waits for them are exact.
+  constexpr int QU = FULL ? 2 * C : 0;
+  constexpr int UNITS = QU + 10 * C;
+  constexpr int NPF = (UNITS + 255) / 256;
+  constexpr int DEPTH = FULL ? 2 : 4;  // chunks in flight ahead of the one being staged
+  uint4 pf[DEPTH][NPF];
+  auto issue_loads = [&](uint4 (&pfs)[NPF], int chunk) {
+    const int c0 = t_begin + min(chunk, nchunks - 1) * C;
+    const int last = min(C, t_end - c0) - 1;
+    const size_t base = (size_t)bh * N + c0;
+#pragma unroll
+    for (int p = 0; p < NPF; ++p) {
+      const int u = min(tid + 256 * p, UNITS - 1);
+      if (u < QU + 2 * C) {
+        const bool isq = u < QU;
+        const int r = isq ? u : u - QU;
+        const int tok = min(r >> 1, last), half = r & 1;
+        pfs[p] = *reinterpret_cast<const uint4*>((isq ? q : k) + (base + tok) * kD + 8 * half);
+      } else {
+        const int r = u - QU - 2 * C;
+        const int tok = min(r >> 3, last), c8 = r & 7;
+        pfs[p] = *reinterpret_cast<const uint4*>(v + (base + tok) * kDV + 8 * c8);
+      }
+    }
+  };
+  auto stage = [&](const uint4 (&pfs)[NPF], int b, int nv) {
+#pragma unroll
+    for (int p = 0; p < NPF; ++p) {
+      const int u = tid + 256 * p;
+      if (u < UNITS) {
+        const int tok_u = u < QU + 2 * C ? (u < QU ? u : u - QU) >> 1 : (u - QU - 2 * C) >> 3;
+        const uint4 raw = tok_u < nv ? pfs[p] : make_uint4(0, 0, 0, 0);
+        if (u < QU) {
+          if constexpr (FULL) {
+            const int tok = u >> 1, half = u & 1;
+            uint16_t* d = &L.Q[b][tok][8 * half];
+            *reinterpret_cast<uint2*>(d) = make_uint2(raw.x, raw.y);
+            *reinterpret_cast<uint2*>(d + 4) = make_uint2(raw.z, raw.w);
+            *reinterpret_cast<uint2*>(d + 16) = make_uint2(raw.x, raw.y);
+            *reinterpret_cast<uint2*>(d + 20) = make_uint2(raw.z, raw.w);
+          }
+        } else if (u < QU + 2 * C) {
+          const int r = u - QU;
+          const int tok = r >> 1, half = r & 1;
+          const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            L.K[b][8 * half + 2 * e][tok] = lo_f(wd[e]);
+            L.K[b][8 * half + 2 * e + 1][tok] = hi_f(wd[e]);
+          }
+          if (half == 0) L.K[b][kOnes][tok] = tok < nv ? 1.0f : 0.0f;
+        } else {
+          const int r = u - QU - 2 * C;
+          const int tok = r >> 3, c8 = r & 7;
+          const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int c0 = 8 * c8 + 2 * e;
+            L.V[b][c0][swz(c0, tok)] = (uint16_t)(wd[e] & 0xFFFFu);
+            L.V[b][c0 + 1][swz(c0 + 1, tok)] = (uint16_t)(wd[e] >> 16);
+          }
+        }
+      }
+    }
+  };
+  // bfloat16 copy of the state (k-slot order) and T for the next state read
+  auto publish = [&](int b) {
+    if constexpr (FULL) {
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        const int ks = kslot_of(ft_of[s], 4 * g);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          if (s < 2 || ct < 2) {
+            const int c = 16 * (s == 2 ? ctb + ct : ct) + li;
+            *reinterpret_cast<uint2*>(&L.S[b][c][ks]) =
+                make_uint2(pack2(acc[s][ct][0], acc[s][ct][1]), pack2(acc[s][ct][2], acc[s][ct][3]));
+          }
+        }
+        if (li == 0 && (s < 2 || own_t2)) {
+          float hi[4], lo[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            hi[r] = (float)f32_to_bf16(tacc[s][r]);
+            lo[r] = tacc[s][r] - hi[r];
+          }
+          *reinterpret_cast<uint2*>(&L.T[b][0][ks]) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
+          *reinterpret_cast<uint2*>(&L.T[b][1][ks]) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+        }
+      }
+    }
+  };
+
+  // zero rows of K^T in both buffers (never overwritten)
+  for (int i = tid; i < C; i += 256) L.Kz[i] = 0.0f;
+  if constexpr (FULL)
+    for (int i = tid; i < kNF; i += 256) L.Tz[i] = 0;
+  // chunk c lives in register set c % DEPTH; chunks 1..DEPTH are in flight
+  // when the loop starts, and body(j) refills the set it stages from with
+  // chunk j + 1 + DEPTH
+  issue_loads(pf[0], 0);
+  stage(pf[0], 0, min(C, t_end - t_begin));
+#pragma unroll
+  for (int c = 1; c <= DEPTH; ++c) issue_loads(pf[c % DEPTH], c);
+  publish(0);
+  __syncthreads();
+
+  const float a2 = inv_a * inv_a;  // 2 * alpha_2: the weight 2 of an off-diagonal monomial times alpha_2
+  const int h = g & 1, gh = g >> 1;
+
+  // Outputs of the chunk computed last, stored at the start of the next
+  // iteration (after that iteration's inputs are staged), so that the wait for
+  // the staged loads never waits for fresh stores.
+  f32x4 yo[FULL ? Sh::TPW : 1][4];
+  float yinv[FULL ? Sh::TPW : 1];
+  int prev_t0 = -1, prev_nv = 0;
+  auto store_prev = [&]() {
+    if constexpr (FULL) {
+      if (prev_t0 >= 0) {
+#pragma unroll
+        for (int tw = 0; tw < Sh::TPW; ++tw) {
+          const int tok = 16 * (w + 4 * tw) + li;
+          if (tok < prev_nv) {
+            TOUT* orow = o + ((size_t)bh * N + prev_t0 + tok) * kDV + 4 * g;
+            const float inv = yinv[tw];
+            if constexpr (std::is_same_v<TOUT, float>) {
+#pragma unroll
+              for (int ct = 0; ct < 4; ++ct)
+                *reinterpret_cast<float4*>(orow + 16 * ct) =
+                    make_float4(yo[tw][ct][0] * inv, yo[tw][ct][1] * inv, yo[tw][ct][2] * inv, yo[tw][ct][3] * inv);
+            } else {
+#pragma unroll
+              for (int ct = 0; ct < 4; ++ct)
+                *reinterpret_cast<uint2*>(orow + 16 * ct) =
+                    make_uint2(pack2(yo[tw][ct][0] * inv, yo[tw][ct][1] * inv),
+                               pack2(yo[tw][ct][2] * inv, yo[tw][ct][3] * inv));
+            }
+          }
+        }
+      }
+    }
+  };
+
+  auto body = [&](int j, uint4 (&pfs)[NPF]) {
+    const int b = j & 1;
+    const int t0 = t_begin + j * C;
+    const int nv = min(C, t_end - t0);
+    if (j + 1 < nchunks) stage(pfs, b ^ 1, min(C, t_end - (t0 + C)));
+    issue_loads(pfs, j + 1 + DEPTH);
+    store_prev();
+
+    if constexpr (FULL) {
+#pragma unroll
+      for (int tw = 0; tw < Sh::TPW; ++tw) {
+        const int tt = w + 4 * tw;  // token tile, wave-uniform
+        const int tok = 16 * tt + li;
+
+        // ---- diagonal block: P = tril(p_3(K Q^T / a)), lane holds P[token li][keys]
+        const bf16x4 bq = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&L.Q[b][tok][4 * g]));
+        bf16x8 pb[NKB];
+#pragma unroll
+        for (int kt = 0; kt < 2 * NKB; ++kt) {
+          float p[4] = {0.f, 0.f, 0.f, 0.f};
+          if (kt <= tt) {
+            const int key0 = 16 * kt + li;
+            const bf16x4 ak = {f32_to_bf16(L.K[b][4 * g][key0]), f32_to_bf16(L.K[b][4 * g + 1][key0]),
+                               f32_to_bf16(L.K[b][4 * g + 2][key0]), f32_to_bf16(L.K[b][4 * g + 3][key0])};
+            const f32x4 s = mfma_bf16_k16(ak, bq, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float y = s[r] * inv_a;
+              p[r] = fmaf(y, fmaf(0.5f, y, 1.0f), 1.0f);
+            }
+            if (kt == tt) {  // diagonal tile: causal mask (key 16kt + 4g + r against token 16tt + li)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= li) ? p[r] : 0.0f;
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pb[kt >> 1][4 * (kt & 1) + r] = f32_to_bf16(p[r]);
+        }
+
+        f32x4 y[5];
+#pragma unroll
+        for (int ct = 0; ct < 5; ++ct) y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // Y^T += [V, 1]^T P^T; row l of column tile ct is value column 16 ct + l, so
+        // lane (li, g) ends up with columns 16 ct + 4g .. 16 ct + 4g + 3 of token li
+        const uint32_t one2 = li == 0 ? 0x3F803F80u : 0u;
+        const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          if (2 * kb <= tt) {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+              const int c = 16 * ct + li;
+              const uint2 v0 = *reinterpret_cast<const uint2*>(&L.V[b][c][swz(c, 32 * kb + 4 * g)]);
+              const uint2 v1 = *reinterpret_cast<const uint2*>(&L.V[b][c][swz(c, 32 * kb + 16 + 4 * g)]);
+              y[ct] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y)), pb[kb], y[ct]);
+            }
+            y[4] = mfma_bf16_k32(ones, pb[kb], y[4]);
+          }
+        }
+
+        // ---- state read: Y^T += S'^T phi'(q)^T, features built in registers
+        float yv[16], zv[16];
+        {
+          const uint16_t* qrow = &L.Q[b][tok][0];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint2 t2 = *reinterpret_cast<const uint2*>(qrow + 8 * h + 4 * e);
+            yv[4 * e] = lo_f(t2.x); yv[4 * e + 1] = hi_f(t2.x);
+            yv[4 * e + 2] = lo_f(t2.y); yv[4 * e + 3] = hi_f(t2.y);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t t1 = *reinterpret_cast<const uint32_t*>(qrow + 8 * h + 2 * gh + 2 * e);
+            zv[2 * e] = lo_f(t1);
+            zv[2 * e + 1] = hi_f(t1);
+          }
+        }
+        float yy[16];
+#pragma unroll
+        for (int s = 0; s < 16; ++s) yy[s] = a2 * yv[s];
+        const float kb0f = gh == 0 ? 0.5f : 1.0f;  // diagonal tile: weight 1 instead of 2
+        const float cA = g == 0 ? 1.0f : 0.0f, cB = g >= 2 ? inv_a : 0.0f, cC = g == 1 ? 1.0f : 0.0f;
+        constexpr int kD0[4] = {0, 1, 4, 5};
+#pragma unroll
+        for (int kb = 0; kb < 5; ++kb) {
+          float f[8];
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            if (kb < 4) {
+              f[s] = yy[s] * zv[(s + kD0[kb]) & 15];
+              if (kb == 0) f[s] *= kb0f;
+            } else {
+              f[s] = cA * yy[s] * zv[(s + 8) & 15] + cB * yv[s] + (s == 0 ? cC : 0.0f);
+            }
+          }
+          const bf16x8 bphi = __builtin_bit_cast(
+              bf16x8, make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])));
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const uint4 a4 = *reinterpret_cast<const uint4*>(&L.S[b][16 * ct + li][32 * kb + 8 * g]);
+            y[ct] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a4), bphi, y[ct]);
+          }
+          // normaliser: rows 0 / 1 of column tile 4 are T' (high / low bfloat16 parts)
+          const uint16_t* trow = li < 2 ? &L.T[b][li][0] : &L.Tz[0];
+          const uint4 tA = *reinterpret_cast<const uint4*>(trow + 32 * kb + 8 * g);
+          y[4] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, tA), bphi, y[4]);
+        }
+
+        // ---- epilogue: o = Y[:d_v] / Y[d_v], stored at the start of the next iteration
+        yinv[tw] = 1.0f / __shfl(y[4][0] + y[4][1], li);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) yo[tw][ct] = y[ct];
+      }
+      prev_t0 = t0;
+      prev_nv = nv;
+    }
+
+    // ---- state update: S' += phi(K)^T V on the owned feature tiles, T' += phi(K)^T 1
+    {
+      const uint32_t one2 = li == 0 ? 0x3F803F80u : 0u;
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int t8 = 32 * kb + 8 * g;
+        float xi[8];
+        {
+          const float4 a0 = *reinterpret_cast<const float4*>(&L.K[b][li][t8]);
+          const float4 a1 = *reinterpret_cast<const float4*>(&L.K[b][li][t8 + 4]);
+          xi[0] = a0.x; xi[1] = a0.y; xi[2] = a0.z; xi[3] = a0.w;
+          xi[4] = a1.x; xi[5] = a1.y; xi[6] = a1.z; xi[7] = a1.w;
+        }
+        bf16x8 vb[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int c = 16 * ct + li;
+          vb[ct] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&L.V[b][c][swz(c, t8)]));
+        }
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+          const float* kj = krow_j[s] == kZero ? &L.Kz[0] : &L.K[b][krow_j[s]][0];
+          const float4 b0 = *reinterpret_cast<const float4*>(kj + t8);
+          const float4 b1 = *reinterpret_cast<const float4*>(kj + t8 + 4);
+          const float xj[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = (s == 2 && const_lane ? 1.0f : xi[e]) * xj[e];
+          const bf16x8 aphi = __builtin_bit_cast(
+              bf16x8, make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])));
+          if (s < 2) {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) acc[s][ct] = mfma_bf16_k32(aphi, vb[ct], acc[s][ct]);
+            tacc[s] = mfma_bf16_k32(aphi, ones, tacc[s]);
+          } else {
+            if (own_t2) tacc[2] = mfma_bf16_k32(aphi, ones, tacc[2]);
+            // column tiles ctb, ctb + 1 (ctb is wave-uniform)
+            if (ctb == 0) {
+              acc[2][0] = mfma_bf16_k32(aphi, vb[0], acc[2][0]);
+              acc[2][1] = mfma_bf16_k32(aphi, vb[1], acc[2][1]);
+            } else {
+              acc[2][0] = mfma_bf16_k32(aphi, vb[2], acc[2][0]);
+              acc[2][1] = mfma_bf16_k32(aphi, vb[3], acc[2][1]);
+            }
+          }
+        }
+      }
+    }
+
+    if (j + 1 < nchunks) publish(b ^ 1);
+    __syncthreads();
+  };
+  for (int j0 = 0; j0 < nchunks; j0 += DEPTH) {
+#pragma unroll
+    for (int i = 0; i < DEPTH; ++i)
+      if (j0 + i < nchunks) body(j0 + i, pf[(i + 1) % DEPTH]);
+  }
+  store_prev();
+
+  // ---- write the state (last segment) or the segment sum, in the caller's layout
+  const bool write = FULL ? (seg == nseg - 1) : true;  // uniform
+  if (write) {
+    // rows of the image: every row is written by exactly one lane group (zero
+    // rows of the internal layout map nowhere)
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float wt;
+        const int row = abi_row(ft_of[s], 4 * g + r, &wt);
+        if (row >= 0) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            if (s < 2 || ct < 2) img[row * kDV + 16 * (s == 2 ? ctb + ct : ct) + li] = acc[s][ct][r] * wt;
+          if (li == 0 && (s < 2 || own_t2)) img[kD3 * kDV + row] = tacc[s][r] * wt;
+        }
+      }
+    }
+    __syncthreads();
+    const size_t slot = (size_t)bh * dst_slots + (dst_slots == 1 ? 0 : seg);
+    float4* ds4 = reinterpret_cast<float4*>(dst_S + slot * kD3 * kDV);
+    float* dt = dst_T + slot * kD3;
+    for (int i = tid; i < kD3 * kDV / 4; i += 256) ds4[i] = reinterpret_cast<const float4*>(img)[i];
+    for (int i = tid; i < kD3; i += 256) dt[i] = img[kD3 * kDV + i];
+  }
+}
+
+template <int C, typename TOUT>
+hipError_t launch(const PrefillArgs& a) {
+  const PrefillPlan& pl = a.plan;
+  float* st_S = a.state;
+  float* st_T = a.state + (size_t)a.BH * kD3 * kDV;
+  const float inv_a = 1.0f / a.a;
+  const uint16_t* q = static_cast<const uint16_t*>(a.q);
+  const uint16_t* k = static_cast<const uint16_t*>(a.k);
+  const uint16_t* v = static_cast<const uint16_t*>(a.v);
+  hipEvent_t* ev = a.events;
+  if (ev) (void)hipEventRecord(ev[0], a.stream);
+  if (pl.nseg > 1) {
+    float* W_S = a.workspace;
+    float* W_T = a.workspace + (size_t)a.BH * pl.nseg * kD3 * kDV;
+    hipLaunchKernelGGL((prefill_n3_kernel<C, false, TOUT>), dim3(a.BH * (pl.nseg - 1)), dim3(256), 0, a.stream, q,
+                       k, v, static_cast<TOUT*>(nullptr), (const float*)nullptr, (const float*)nullptr, 1, W_S, W_T,
+                       pl.nseg, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
+    if (ev) (void)hipEventRecord(ev[1], a.stream);
+    if (hipError_t e = launch_segment_scan(st_S, st_T, W_S, W_T, kD3, pl.nseg, a.BH, a.stream)) return e;
+    if (ev) (void)hipEventRecord(ev[2], a.stream);
+    hipLaunchKernelGGL((prefill_n3_kernel<C, true, TOUT>), dim3(a.BH * pl.nseg), dim3(256), 0, a.stream, q, k, v,
+                       static_cast<TOUT*>(a.o), W_S, W_T, pl.nseg, st_S, st_T, 1, a.N, pl.nseg, pl.chunks_per_seg,
+                       inv_a);
+  } else {
+    if (ev) {
+      (void)hipEventRecord(ev[1], a.stream);
+      (void)hipEventRecord(ev[2], a.stream);
+    }
+    hipLaunchKernelGGL((prefill_n3_kernel<C, true, TOUT>), dim3(a.BH), dim3(256), 0, a.stream, q, k, v,
+                       static_cast<TOUT*>(a.o), st_S, st_T, 1, st_S, st_T, 1, a.N, 1, pl.chunks_per_seg, inv_a);
+  }
+  if (ev) (void)hipEventRecord(ev[3], a.stream);
+  return hipGetLastError();
+}
+
+}  // namespace n3
+
+hipError_t launch_prefill_n3_bf16(const PrefillArgs& a) {
+  switch (a.chunk) {
+    case 64: return a.out_bf16 ? n3::launch<64, uint16_t>(a) : n3::launch<64, float>(a);
+    case 128: return a.out_bf16 ? n3::launch<128, uint16_t>(a) : n3::launch<128, float>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace taylor
