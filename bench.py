@@ -57,6 +57,23 @@ def decode_algorithmic(cfg):
     return heads * (2 * state_bytes + io), heads
 
 
+def measured_traffic():
+    """HBM bytes per launch of the chunk kernel from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None
+    when the kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "prefill_n3_hbm_traffic.md")
+    src = os.path.join(ROOT, "recurrent_state_phi_amd", "csrc", "taylor_prefill_n3.hip")
+    try:
+        fields = dict(l.split(": ", 1) for l in open(path).read().splitlines() if ": " in l and not l.startswith(" "))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if fields.get("kernel_source_sha256", "").strip() != sha:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def make_prefill_inputs(torch, dev):
     import taylor_inputs as TI
     c = PREFILL
@@ -251,8 +268,8 @@ def main():
         "phases_ms": phases,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-            "kernel": "prefill_chunk_kernel<3, bf16, 64, full, float>",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+            "kernel": "prefill_n3_kernel<64, full, float> (replay of every segment from its prefix)",
             "algorithmic_bytes_per_launch": alg_bytes, "bytes_per_head_token": bytes_per_ht,
             "mfma_tflops_algorithmic": alg_flops / t_k / 1e12,
             "mfma_frac_algorithmic": alg_flops / t_k / 1e12 / BF16_MFMA_PEAK_TFLOPS,
