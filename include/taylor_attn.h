@@ -90,10 +90,14 @@ size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n
  *   q, k, v : device, in_dtype (TAYLOR_F32 or TAYLOR_BF16); o : device, out_dtype.
  *   N >= 0 (N = 0 is a no-op), any N (the last chunk may be partial).
  *   a > 0 : temperature.
- *   chunk : 32 or 64 for TAYLOR_F32 inputs; 32, 64 or 128 for TAYLOR_BF16.
- *   in_dtype selects the matrix-core arithmetic: float32 inputs use float32
- *   MFMA throughout; bfloat16 inputs use bfloat16 MFMA with float32
- *   accumulation and a float32 state.
+ *   chunk : n = 1..3: 32 or 64 for TAYLOR_F32 inputs; 32, 64 or 128 for
+ *           TAYLOR_BF16.  n = 4: 32 or 64 for either input type.
+ *   in_dtype selects the matrix-core arithmetic for n = 1..3: float32 inputs
+ *   use float32 MFMA throughout; bfloat16 inputs use bfloat16 MFMA with
+ *   float32 accumulation and a float32 state.  n = 4 computes in float32 for
+ *   both input types (bfloat16 inputs are widened); its 969-row state is
+ *   split into 6 blocks of 176 rows handled by separate workgroups, and the
+ *   workspace then also holds each block's share of the outputs.
  *   workspace : device, at least taylor_prefill_workspace_bytes(...) bytes
  *   (may be NULL when that is 0); it is scratch, its contents are undefined
  *   afterwards.  o must not alias q, k, v or state. */

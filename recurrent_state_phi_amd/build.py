@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libtaylor_attn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["taylor_abi.cpp", "taylor_decode.hip", "taylor_prefill.hip", "taylor_prefill_n3.hip"]
+SOURCES = ["taylor_abi.cpp", "taylor_decode.hip", "taylor_prefill.hip", "taylor_prefill_n3.hip", "taylor_prefill_fb.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", CSRC, "-I", INCLUDE]

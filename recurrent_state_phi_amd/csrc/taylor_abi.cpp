@@ -103,8 +103,8 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, fl
     return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: only d=16, d_v=64, n in 1..4 are built");
   const bool in_bf16 = in_dtype == TAYLOR_BF16, out_bf16 = out_dtype == TAYLOR_BF16;
   if (!taylor::prefill_supported(n, chunk, in_bf16))
-    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: unsupported (n, chunk, in_dtype): chunk must be 32/64 "
-                                     "(float32) or 32/64/128 (bfloat16), n in 1..3");
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: unsupported (n, chunk, in_dtype): for n in 1..3 chunk "
+                                     "must be 32/64 (float32) or 32/64/128 (bfloat16); for n = 4 chunk 32/64");
   if ((int64_t)B * H == 0 || N == 0) return TAYLOR_OK;
   if (!q || !k || !v || !o || !state) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: NULL tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state))

@@ -45,6 +45,11 @@ hipError_t launch_prefill(const PrefillArgs& a);
 // n = 3, bfloat16 inputs, chunk 64 or 128 (taylor_prefill_n3.hip).
 hipError_t launch_prefill_n3_bf16(const PrefillArgs& a);
 
+// n = 4, feature-blocked, chunk 32 or 64 (taylor_prefill_fb.hip), and the
+// floats of its per-block output workspace.
+hipError_t launch_prefill_n4(const PrefillArgs& a);
+size_t prefill_fb_output_floats(int BH, int N);
+
 // Exclusive scan of the per-segment state sums in place, seeded with the
 // caller's state (taylor_prefill.hip).
 hipError_t launch_segment_scan(const float* st_S, const float* st_T, float* W_S, float* W_T, int D, int nseg, int BH,

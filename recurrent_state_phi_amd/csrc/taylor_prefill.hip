@@ -577,18 +577,22 @@ PrefillPlan plan_prefill(int BH, int N, int n, int chunk) {
   if (BH <= 0 || N <= 0 || chunk <= 0) return p;
   p.nchunks = (N + chunk - 1) / chunk;
   // Aim for at least 512 workgroups in the chunk kernel (two per CU on a
-  // 256-CU part) when the heads alone do not provide them.
-  int nseg = (512 + BH - 1) / BH;
+  // 256-CU part) when the heads alone do not provide them.  For n = 4 every
+  // segment is split into 6 feature blocks, one workgroup each.
+  const int blocks = n == 4 ? 6 : 1;
+  int nseg = (512 + BH * blocks - 1) / (BH * blocks);
   if (nseg < 1) nseg = 1;
   if (nseg > p.nchunks) nseg = p.nchunks;
   p.chunks_per_seg = (p.nchunks + nseg - 1) / nseg;
   p.nseg = (p.nchunks + p.chunks_per_seg - 1) / p.chunks_per_seg;
   const int D = n == 1 ? state_width(1) : n == 2 ? state_width(2) : n == 3 ? state_width(3) : state_width(4);
   p.workspace_floats = p.nseg > 1 ? (size_t)BH * p.nseg * D * (kDV + 1) : 0;
+  if (n == 4) p.workspace_floats += prefill_fb_output_floats(BH, N);
   return p;
 }
 
 bool prefill_supported(int n, int chunk, bool in_bf16) {
+  if (n == 4) return chunk == 32 || chunk == 64;
   if (n < 1 || n > 3) return false;
   if (in_bf16) return chunk == 32 || chunk == 64 || chunk == 128;
   return chunk == 32 || chunk == 64;
@@ -657,6 +661,7 @@ hipError_t launch_prefill(const PrefillArgs& a) {
     case 3:
       if (a.in_bf16 && (a.chunk == 64 || a.chunk == 128)) return launch_prefill_n3_bf16(a);
       return launch_prefill_n<3>(a);
+    case 4: return launch_prefill_n4(a);
   }
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,315 @@
+// Chunked prefill for n = 4 (section 3.5 of "A Taylor-Series Route to
+// Linear-Time Transformers with a Fixed Number of Recurrent States",
+// arXiv 2610.20637), where the stacked state has D = 1 + 16 + 136 + 816 = 969
+// rows of d_v + 1 = 65 floats (252 KB per head): more than one workgroup can
+// hold in registers or LDS.
+//
+// The feature rows are therefore split into NFB blocks of 11 tiles (176 rows).
+// Everything the method does is linear in the state rows, so each block is an
+// independent problem:
+//   * segment sums, scan and replay run per (head, segment, feature block),
+//     exactly as in the unblocked kernels (the scan works on rows, so it is
+//     shared);
+//   * the replay of block fb writes the block's share of the unnormalised
+//     outputs, Y_fb = phi_hat(Q)_fb S_fb (+ the masked diagonal block P [V, 1]
+//     for fb = 0), to a workspace; a combine kernel then forms
+//     o = sum_fb Y_fb[:d_v] / sum_fb Y_fb[d_v]  (Eq. (5)).
+// Arithmetic is float32 throughout (16x16x4 float32 MFMA); bfloat16 inputs are
+// widened when staged.  Feature rows follow the caller's layout (m ascending,
+// lexicographic multi-indices, sqrt-multinomial weights) and come from a table.
+//
+// Work inside one 256-thread workgroup (4 waves): wave w owns value columns
+// 16w..16w+15 of the block's state (11 accumulator tiles); the ones-column T of
+// tile ft sits in column 0 of an extra accumulator tile owned by wave ft % 4.
+// Per chunk: stage q, k, v | features of the block and (fb = 0) the masked
+// polynomial block P into LDS | state read and update on MFMA.
+#include <type_traits>
+
+#include "taylor_device.h"
+#include "taylor_launch.h"
+
+namespace taylor {
+namespace fb {
+
+constexpr int kN4 = 4;
+constexpr int kD4 = state_width(kN4);        // 969
+constexpr int kFT = 11;                      // feature tiles per block
+constexpr int kBF = 16 * kFT;                // 176 rows per block
+constexpr int kNFB = (kD4 + kBF - 1) / kBF;  // 6 blocks
+constexpr int kPS = kBF + 1;                 // feature row stride in LDS (odd: bank spread)
+constexpr int kNTW = (kFT + 3) / 4;          // T tiles per wave
+
+__constant__ FeatureTable kTab = make_feature_table();
+
+template <int C>
+struct Lds {
+  float Xq[C][kD];
+  float Xk[C][kD];
+  float V[C][kDV + 4];
+  float PhQ[C][kPS];
+  float PhK[C][kPS];
+  float P[C][C + 1];
+  float Ts[kBF];
+};
+
+template <typename IT> __device__ __forceinline__ float ld(const IT* p, size_t i) { return Elem<IT>::load(p, i); }
+
+// p_4(y) = 1 + y + y^2/2 + y^3/6
+__device__ __forceinline__ float poly4(float y) { return 1.0f + y * (1.0f + y * (0.5f + y * (1.0f / 6.0f))); }
+
+template <int C, bool FULL, typename IT>
+__global__ __launch_bounds__(256) void prefill_fb_kernel(const IT* __restrict__ q, const IT* __restrict__ k,
+                                                         const IT* __restrict__ v, float* __restrict__ Yp,
+                                                         const float* __restrict__ pre_S,
+                                                         const float* __restrict__ pre_T, int pre_slots,
+                                                         float* __restrict__ dst_S, float* __restrict__ dst_T,
+                                                         int dst_slots, int BH, int N, int nseg, int cps,
+                                                         float inv_a) {
+  __shared__ __align__(16) Lds<C> L;
+  constexpr int NTT = C / 16;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: guards MFMAs
+  const int fbk = blockIdx.x % kNFB;
+  const int rest = blockIdx.x / kNFB;
+  const int gseg = FULL ? nseg : nseg - 1;
+  const int bh = rest / gseg, seg = rest % gseg;
+  const int F0 = fbk * kBF;
+  const int t_begin = seg * cps * C;
+  const int t_end = min(N, t_begin + cps * C);
+  const int col = 16 * w + li;
+
+  // ---- the segment's starting state (rows F0 .. F0 + 175 of the block)
+  f32x4 Sacc[kFT];
+  f32x4 Tacc[kNTW];
+  {
+    const size_t slot = (size_t)bh * pre_slots + (pre_slots == 1 ? 0 : seg);
+    const float* ps = (FULL && pre_S) ? pre_S + slot * kD4 * kDV : nullptr;
+    const float* pt = (FULL && pre_T) ? pre_T + slot * kD4 : nullptr;
+#pragma unroll
+    for (int ft = 0; ft < kFT; ++ft)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = F0 + 16 * ft + 4 * g + r;
+        Sacc[ft][r] = ps ? ps[(size_t)min(row, kD4 - 1) * kDV + col] : 0.0f;
+        if (row >= kD4) Sacc[ft][r] = 0.0f;
+      }
+#pragma unroll
+    for (int j = 0; j < kNTW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ft = w + 4 * j;
+        const int row = F0 + 16 * ft + 4 * g + r;
+        const float t = pt ? pt[min(row, kD4 - 1)] : 0.0f;
+        Tacc[j][r] = (li == 0 && ft < kFT && row < kD4) ? t : 0.0f;
+      }
+  }
+
+  const float a2 = inv_a * inv_a;
+  const float4 alpha_q = make_float4(1.0f, inv_a, 0.5f * a2, a2 * inv_a * (1.0f / 6.0f));
+  const float4 alpha_k = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+
+  for (int t0 = t_begin; t0 < t_end; t0 += C) {
+    const int nv = min(C, t_end - t0);
+    const size_t base = (size_t)bh * N + t0;
+
+    // ---- stage q, k, v (float), zero for padding tokens; publish T of the block
+    for (int i = tid; i < C * kD; i += 256) {
+      const int tok = i / kD, j = i % kD;
+      L.Xk[tok][j] = tok < nv ? ld(k, (base + tok) * kD + j) : 0.0f;
+      if (FULL) L.Xq[tok][j] = tok < nv ? ld(q, (base + tok) * kD + j) : 0.0f;
+    }
+    for (int i = tid; i < C * kDV; i += 256) {
+      const int tok = i / kDV, j = i % kDV;
+      L.V[tok][j] = tok < nv ? ld(v, (base + tok) * kDV + j) : 0.0f;
+    }
+    if (FULL && li == 0) {
+#pragma unroll
+      for (int j = 0; j < kNTW; ++j) {
+        const int ft = w + 4 * j;
+        if (ft < kFT) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) L.Ts[16 * ft + 4 * g + r] = Tacc[j][r];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- features of the block (query side scaled by alpha_m), and P for block 0
+    for (int i = tid; i < C * kBF; i += 256) {
+      const int tok = i / kBF, fl = i % kBF, f = F0 + fl;
+      float fk = 0.0f, fq = 0.0f;
+      if (f < kD4) {
+        fk = feature_value(kTab, f, &L.Xk[tok][0], alpha_k);
+        if (f == 0) fk = tok < nv ? 1.0f : 0.0f;  // the constant feature of a padding token is 0
+        if (FULL) fq = feature_value(kTab, f, &L.Xq[tok][0], alpha_q);
+      }
+      L.PhK[tok][fl] = fk;
+      if (FULL) L.PhQ[tok][fl] = fq;
+    }
+    if (FULL && fbk == 0) {
+      for (int i = tid; i < C * C; i += 256) {
+        const int tq = i / C, tk = i % C;
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kD; ++j) s += L.Xq[tq][j] * L.Xk[tk][j];
+        L.P[tq][tk] = tk <= tq ? poly4(s * inv_a) : 0.0f;
+      }
+    }
+    __syncthreads();
+
+    // ---- this block's share of the outputs: Y = phi_hat(Q)_fb S_fb (+ P [V, 1])
+    if constexpr (FULL) {
+      const float one = li == 0 ? 1.0f : 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < NTT; ++mt) {
+        const int tok = 16 * mt + li;
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+        f32x4 yd = {0.f, 0.f, 0.f, 0.f};
+        const bool mine = (mt & 3) == w;  // wave-uniform
+#pragma unroll
+        for (int ft = 0; ft < kFT; ++ft)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float a = L.PhQ[tok][16 * ft + 4 * g + r];
+            y = mfma_f32_k4(a, Sacc[ft][r], y);
+            if (mine) yd = mfma_f32_k4(a, li == 0 ? L.Ts[16 * ft + 4 * g + r] : 0.0f, yd);
+          }
+        if (fbk == 0) {  // uniform
+          for (int st = 0; st < C / 4; ++st) {
+            const float a = L.P[tok][4 * st + g];
+            y = mfma_f32_k4(a, L.V[4 * st + g][col], y);
+            if (mine) yd = mfma_f32_k4(a, one, yd);
+          }
+        }
+        // lane holds Y[token 16mt + 4g + r][col]
+        float* yrow = Yp + ((size_t)fbk * BH * N + base) * (kDV + 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * mt + 4 * g + r;
+          if (t < nv) {
+            yrow[(size_t)t * (kDV + 1) + col] = y[r];
+            if (mine && li == 0) yrow[(size_t)t * (kDV + 1) + kDV] = yd[r];
+          }
+        }
+      }
+    }
+
+    // ---- state update: S_fb += phi(K)_fb^T V, T_fb += phi(K)_fb^T 1
+    {
+      const float one = li == 0 ? 1.0f : 0.0f;
+      for (int st = 0; st < C / 4; ++st) {
+        const float b = L.V[4 * st + g][col];
+#pragma unroll
+        for (int ft = 0; ft < kFT; ++ft) {
+          const float a = L.PhK[4 * st + g][16 * ft + li];
+          Sacc[ft] = mfma_f32_k4(a, b, Sacc[ft]);
+          if ((ft & 3) == w) Tacc[ft >> 2] = mfma_f32_k4(a, one, Tacc[ft >> 2]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- write the block's rows of the state (last segment) or of the segment sum
+  const bool write = FULL ? (seg == nseg - 1) : true;
+  if (write) {
+    const size_t slot = (size_t)bh * dst_slots + (dst_slots == 1 ? 0 : seg);
+    float* ds = dst_S + slot * kD4 * kDV;
+    float* dt = dst_T + slot * kD4;
+#pragma unroll
+    for (int ft = 0; ft < kFT; ++ft)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = F0 + 16 * ft + 4 * g + r;
+        if (row < kD4) ds[(size_t)row * kDV + col] = Sacc[ft][r];
+      }
+    if (li == 0) {
+#pragma unroll
+      for (int j = 0; j < kNTW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ft = w + 4 * j;
+          const int row = F0 + 16 * ft + 4 * g + r;
+          if (ft < kFT && row < kD4) dt[row] = Tacc[j][r];
+        }
+    }
+  }
+}
+
+// o = sum over blocks of the numerators / sum of the normalisers (Eq. (5)).
+template <typename TOUT>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Yp, TOUT* __restrict__ o,
+                                                      size_t rows) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * kDV) return;
+  const size_t row = i / kDV;
+  const int c = (int)(i % kDV);
+  float num = 0.0f, den = 0.0f;
+#pragma unroll
+  for (int b = 0; b < kNFB; ++b) {
+    const float* y = Yp + ((size_t)b * rows + row) * (kDV + 1);
+    num += y[c];
+    den += y[kDV];
+  }
+  Elem<TOUT>::store(o, i, num / den);
+}
+
+template <int C, typename IT, typename TOUT>
+hipError_t launch(const PrefillArgs& a) {
+  const PrefillPlan& pl = a.plan;
+  float* st_S = a.state;
+  float* st_T = a.state + (size_t)a.BH * kD4 * kDV;
+  const float inv_a = 1.0f / a.a;
+  const IT* q = static_cast<const IT*>(a.q);
+  const IT* k = static_cast<const IT*>(a.k);
+  const IT* v = static_cast<const IT*>(a.v);
+  // workspace: [segment sums / prefixes when nseg > 1][block outputs]
+  const size_t agg = pl.nseg > 1 ? (size_t)a.BH * pl.nseg * kD4 * (kDV + 1) : 0;
+  float* W_S = a.workspace;
+  float* W_T = a.workspace + (size_t)a.BH * pl.nseg * kD4 * kDV;
+  float* Yp = a.workspace + agg;
+  hipEvent_t* ev = a.events;
+  if (ev) (void)hipEventRecord(ev[0], a.stream);
+  if (pl.nseg > 1) {
+    hipLaunchKernelGGL((prefill_fb_kernel<C, false, IT>), dim3(a.BH * (pl.nseg - 1) * kNFB), dim3(256), 0, a.stream,
+                       q, k, v, (float*)nullptr, (const float*)nullptr, (const float*)nullptr, 1, W_S, W_T, pl.nseg,
+                       a.BH, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
+    if (ev) (void)hipEventRecord(ev[1], a.stream);
+    if (hipError_t e = launch_segment_scan(st_S, st_T, W_S, W_T, kD4, pl.nseg, a.BH, a.stream)) return e;
+    if (ev) (void)hipEventRecord(ev[2], a.stream);
+    hipLaunchKernelGGL((prefill_fb_kernel<C, true, IT>), dim3(a.BH * pl.nseg * kNFB), dim3(256), 0, a.stream, q, k,
+                       v, Yp, W_S, W_T, pl.nseg, st_S, st_T, 1, a.BH, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
+  } else {
+    if (ev) {
+      (void)hipEventRecord(ev[1], a.stream);
+      (void)hipEventRecord(ev[2], a.stream);
+    }
+    hipLaunchKernelGGL((prefill_fb_kernel<C, true, IT>), dim3(a.BH * kNFB), dim3(256), 0, a.stream, q, k, v, Yp,
+                       st_S, st_T, 1, st_S, st_T, 1, a.BH, a.N, 1, pl.chunks_per_seg, inv_a);
+  }
+  const size_t rows = (size_t)a.BH * a.N;
+  hipLaunchKernelGGL((combine_kernel<TOUT>), dim3((unsigned)((rows * kDV + 255) / 256)), dim3(256), 0, a.stream, Yp,
+                     static_cast<TOUT*>(a.o), rows);
+  if (ev) (void)hipEventRecord(ev[3], a.stream);
+  return hipGetLastError();
+}
+
+template <int C>
+hipError_t launch_c(const PrefillArgs& a) {
+  if (a.in_bf16) return a.out_bf16 ? launch<C, uint16_t, uint16_t>(a) : launch<C, uint16_t, float>(a);
+  return a.out_bf16 ? launch<C, float, uint16_t>(a) : launch<C, float, float>(a);
+}
+
+}  // namespace fb
+
+size_t prefill_fb_output_floats(int BH, int N) { return (size_t)fb::kNFB * BH * N * (kDV + 1); }
+
+hipError_t launch_prefill_n4(const PrefillArgs& a) {
+  switch (a.chunk) {
+    case 32: return fb::launch_c<32>(a);
+    case 64: return fb::launch_c<64>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace taylor

@@ -61,6 +61,15 @@ def test_state_width_closed_form(rsp):
     assert rsp.state_width(0, 3) == -1 and rsp.state_width(16, 0) == -1
 
 
+def test_workspace_sizing_n4(rsp):
+    """n = 4: segment sums of 969 x 65 floats per segment plus 6 blocks of 65 floats per head-token."""
+    BH, N = 2 * 8, 4096
+    ws = rsp.prefill_workspace_bytes(2, 8, N, 4, 32)
+    out = 6 * BH * N * 65 * 4
+    assert ws >= out and (ws - out) % (BH * 969 * 65 * 4) == 0
+    assert rsp.prefill_workspace_bytes(1, 1, 10, 4, 32) == 6 * 10 * 65 * 4  # one segment: outputs only
+
+
 def test_workspace_sizing(rsp):
     # one segment per head when the heads alone fill the GPU: no workspace
     assert rsp.prefill_workspace_bytes(64, 8, 4096, 3, 64) == 0
@@ -85,6 +94,7 @@ def test_invalid_arguments_are_rejected_before_launch(rsp):
     assert _prefill_rc(lib, d=32) == -2                 # shape not built
     assert _prefill_rc(lib, d_v=128) == -2
     assert _prefill_rc(lib, n=5) == -2
+    assert _prefill_rc(lib, n=4, chunk=128, ind=1) == -2   # n = 4: chunk 32 or 64
     assert _prefill_rc(lib, chunk=48) == -2
     assert _prefill_rc(lib, chunk=128, ind=0) == -2     # float32 path stops at chunk 64
     assert _prefill_rc(lib, a=0.0) == -1

@@ -100,6 +100,36 @@ def test_prefill_ragged_vs_oracle(rsp, n, dtype, chunk):
     assert np.abs(T - A[..., 64]).max() <= tol * scale.max()
 
 
+@pytest.mark.parametrize("dtype,chunk", [("f32", 32), ("f32", 64), ("bf16", 32), ("bf16", 64)])
+def test_prefill_n4_ragged_vs_oracle(rsp, dtype, chunk):
+    """n = 4: the 969-row state is split into feature blocks; outputs and state against the oracle."""
+    say("prefill n=4 ragged", dtype, chunk)
+    q, k, v = TI.make_qkv(78, 2, 3, 700, 16, 64, dtype=dtype)
+    ref = oracle.taylor_direct(q, k, v, 4, 1.0)
+    got, st = run_prefill(rsp, q, k, v, 4, 1.0, chunk, dtype)
+    assert oracle.rel_err_rowwise(got, ref) <= TOL["f32"]  # float32 arithmetic for both input types
+    S, T = (x.cpu().numpy().astype(np.float64) for x in rsp.state_views(st, 2, 3, 4))
+    A = oracle_state(k, v, 4)
+    scale = np.abs(A).max()
+    assert np.abs(S - A[..., :64]).max() <= 1e-5 * scale
+    assert np.abs(T - A[..., 64]).max() <= 1e-5 * scale
+
+
+@pytest.mark.parametrize("N", [1, 17, 65, 300])
+def test_prefill_n4_short_and_split(rsp, N):
+    say("prefill n=4 short/split", N)
+    q, k, v = TI.make_qkv(79, 1, 2, N, 16, 64)
+    ref = oracle.taylor_direct(q, k, v, 4, 0.9)
+    whole, st_w = run_prefill(rsp, q, k, v, 4, 0.9, 32, "f32")
+    assert oracle.rel_err_rowwise(whole, ref) <= TOL["f32"]
+    t1 = N // 3
+    if t1 > 0:
+        a_out, st = run_prefill(rsp, q[:, :, :t1], k[:, :, :t1], v[:, :, :t1], 4, 0.9, 32, "f32")
+        b_out, st = run_prefill(rsp, q[:, :, t1:], k[:, :, t1:], v[:, :, t1:], 4, 0.9, 32, "f32", state=st)
+        assert oracle.rel_err_rowwise(np.concatenate([a_out, b_out], axis=2), ref) <= TOL["f32"]
+        assert np.abs(st.cpu().numpy() - st_w.cpu().numpy()).max() <= 1e-5 * np.abs(st_w.cpu().numpy()).max()
+
+
 @pytest.mark.parametrize("N", [1, 2, 15, 17, 33, 64, 65, 129])
 def test_prefill_short_lengths(rsp, N):
     say("prefill short", N)
@@ -207,13 +237,13 @@ def test_prefill_workload_sampled(rsp):
     assert np.abs(S[:1, :2] - A[..., :64]).max() <= 2e-2 * np.abs(A[..., :64]).max()
 
 
-@pytest.mark.parametrize("n", [1, 2, 3])
+@pytest.mark.parametrize("n", [1, 2, 3, 4])
 def test_order_sweep_workload(rsp, n):
     """B=2, H=8, N=4096, float32, a=1: all rows against the oracle."""
     say("order sweep", n)
     B, H, N = 2, 8, 4096
     q, k, v = TI.make_qkv(TI.SEEDS["order_sweep"], B, H, N, 16, 64)
-    got, _ = run_prefill(rsp, q, k, v, n, 1.0, 64, "f32")
+    got, _ = run_prefill(rsp, q, k, v, n, 1.0, 64 if n < 4 else 32, "f32")
     rows = sample_rows(B, H, N, 256, 64)
     ref = oracle.taylor_direct(q, k, v, n, 1.0, rows=rows)
     assert oracle.rel_err_rowwise(got.reshape(-1, 64)[rows], ref) <= TOL["f32"]
