@@ -177,6 +177,85 @@ def time_decode(torch, rsp, dev, use_graph=True):
     return eager_us, graph_us
 
 
+ORDER_SWEEP = dict(B=2, H=8, N=4096, d=16, d_v=64, a=1.0)
+LONG = dict(B=1, H=16, N=65536, d=16, d_v=64, n=3, a=1.0, chunk=128)
+
+
+def _gpu_inputs(torch, dev, B, H, N, d, dv, seed, dtype, normalize=True, scale=1.0):
+    g = torch.Generator(device=dev).manual_seed(seed)
+    q = torch.randn(B, H, N, d, device=dev, generator=g, dtype=torch.float32)
+    k = torch.randn(B, H, N, d, device=dev, generator=g, dtype=torch.float32)
+    v = torch.randn(B, H, N, dv, device=dev, generator=g, dtype=torch.float32)
+    if normalize:
+        q, k = q / q.norm(dim=-1, keepdim=True), k / k.norm(dim=-1, keepdim=True)
+    else:
+        q, k = q * scale, k * scale
+    return q.to(dtype).contiguous(), k.to(dtype).contiguous(), v.to(dtype).contiguous()
+
+
+def _time_calls(torch, fn, reps, warmup=2):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def order_sweep(torch, rsp, dev, reps=10):
+    """B=2, H=8, N=4096, float32, a=1: prefill throughput per n and the error of the
+    n-term outputs against exact causal softmax (float64 reference computed with
+    torch on the GPU; Frobenius-relative over the whole output)."""
+    c = ORDER_SWEEP
+    B, H, N = c["B"], c["H"], c["N"]
+    q, k, v = _gpu_inputs(torch, dev, B, H, N, c["d"], c["d_v"], 1004, torch.float32)
+    s = (q.double() @ k.double().transpose(-1, -2).contiguous()) / c["a"]
+    s = s.masked_fill(torch.ones(N, N, device=dev, dtype=torch.bool).triu(1), float("-inf"))
+    ref = torch.softmax(s, dim=-1) @ v.double()
+    del s
+    out = {}
+    for n in (1, 2, 3, 4):
+        chunk = 64 if n < 4 else 32
+        ws = torch.empty(max(rsp.prefill_workspace_bytes(B, H, N, n, chunk) // 4, 1), device=dev)
+        o = torch.empty(B, H, N, c["d_v"], device=dev)
+
+        def call():
+            st = rsp.new_state(B, H, n, device=dev)
+            rsp.prefill(q, k, v, st, n, c["a"], chunk=chunk, out=o, workspace=ws)
+
+        ms = _time_calls(torch, call, reps)
+        err = float((o.double() - ref).norm() / ref.norm())
+        out[f"n{n}"] = {"tokens_per_s": B * N / (ms * 1e-3), "ms": ms, "chunk": chunk,
+                        "err_vs_softmax_frobenius": err}
+        del ws, o
+    return {"workload": "order sweep B=2 H=8 N=4096 d=16 d_v=64 a=1, float32 q/k/v/out, normalised Gaussian q,k",
+            "per_n": out}
+
+
+def long_prefill(torch, rsp, dev, reps=5):
+    """B=1, H=16, N=65536, n=3, chunk=128, bfloat16 inputs, float32 state and output."""
+    c = LONG
+    q, k, v = _gpu_inputs(torch, dev, c["B"], c["H"], c["N"], c["d"], c["d_v"], 1005, torch.bfloat16)
+    ws = torch.empty(max(rsp.prefill_workspace_bytes(c["B"], c["H"], c["N"], c["n"], c["chunk"]) // 4, 1), device=dev)
+    o = torch.empty(c["B"], c["H"], c["N"], c["d_v"], device=dev)
+    st = rsp.new_state(c["B"], c["H"], c["n"], device=dev)
+
+    def call():
+        rsp.prefill(q, k, v, st, c["n"], c["a"], chunk=c["chunk"], out=o, workspace=ws)
+
+    ms = _time_calls(torch, call, reps)
+    D = state_width(c["d"], c["n"])
+    ht = c["B"] * c["H"] * c["N"]
+    alg = ht * (2 * (2 * c["d"] + c["d_v"]) + 4 * c["d_v"]) + 4.0 * c["B"] * c["H"] * D * (c["d_v"] + 1)
+    return {"workload": "long prefill B=1 H=16 N=65536 d=16 d_v=64 n=3 a=1 chunk=128, bf16 q/k/v, fp32 state/out",
+            "tokens_per_s": c["B"] * c["N"] / (ms * 1e-3), "ms_per_call": ms,
+            "whole_call_hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def cpu_baseline(qkv_host, sample_every=4):
     """The float64 oracle on every `sample_every`-th query row of the prefill
     workload, all heads; time extrapolated to the whole job by the number of
@@ -214,6 +293,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the order-sweep and long-prefill lines")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -289,6 +369,10 @@ def main():
                          "unit": "GB/s", "frac": dbytes / (best * 1e-6) / 1e9 / HBM_PEAK_GBS,
                          "algorithmic_bytes_per_step": dbytes},
         }
+    if args.only == "all" and not args.no_secondary:
+        print("[bench] order sweep n=1..4 and long prefill", file=sys.stderr, flush=True)
+        result["order_sweep"] = order_sweep(torch, rsp, dev)
+        result["long_prefill"] = long_prefill(torch, rsp, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (float64 oracle, sampled rows)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(host)
