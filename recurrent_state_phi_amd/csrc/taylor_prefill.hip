@@ -522,36 +522,18 @@ __global__ __launch_bounds__(256, (PrefillShape<NT, BF, C>::MIN_WAVES)) void pre
 
 // Exclusive scan of the segment sums, in place, seeded with the caller's state:
 // slot s <- state + sum_{s' < s} (segment sum s').  Slot nseg-1 never holds a
-// sum (the last segment's total is not needed), only its prefix.
-__global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restrict__ st_S,
-                                                           const float* __restrict__ st_T,
-                                                           float* __restrict__ W_S, float* __restrict__ W_T,
-                                                           int D, int nseg) {
-  const int bh = blockIdx.y;
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  const int nS = D * kDV;
-  if (e >= nS + D) return;
-  const float* src;
-  float* slot0;
-  size_t stride;
-  if (e < nS) {
-    src = st_S + (size_t)bh * nS + e;
-    slot0 = W_S + (size_t)bh * nseg * nS + e;
-    stride = nS;
-  } else {
-    src = st_T + (size_t)bh * D + (e - nS);
-    slot0 = W_T + (size_t)bh * nseg * D + (e - nS);
-    stride = D;
-  }
-  // Blocks of 16 slots: all loads of a block are issued before any store, so
-  // they are in flight together.
-  float run = *src;
+// sum (the last segment's total is not needed), only its prefix.  One float
+// per thread; the loads of a block of 16 slots are issued before any store, so
+// they are in flight together.
+template <typename VT>
+__device__ __forceinline__ void scan_slots(const VT* src, VT* slot0, size_t stride, int nseg) {
+  VT run = *src;
   for (int s0 = 0; s0 < nseg; s0 += 16) {
-    float tmp[16];
+    VT tmp[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int s = s0 + i;
-      tmp[i] = (s < nseg - 1) ? slot0[(size_t)s * stride] : 0.0f;
+      tmp[i] = (s < nseg - 1) ? slot0[(size_t)s * stride] : VT{};
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -560,6 +542,20 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restri
       run += tmp[i];
     }
   }
+}
+
+__global__ __launch_bounds__(256) void segment_scan_kernel(const float* __restrict__ st_S,
+                                                           const float* __restrict__ st_T,
+                                                           float* __restrict__ W_S, float* __restrict__ W_T,
+                                                           int D, int nseg) {
+  const int bh = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int nS = D * kDV;
+  if (e >= nS + D) return;
+  if (e < nS)
+    scan_slots(st_S + (size_t)bh * nS + e, W_S + (size_t)bh * nseg * nS + e, (size_t)nS, nseg);
+  else
+    scan_slots(st_T + (size_t)bh * D + (e - nS), W_T + (size_t)bh * nseg * D + (e - nS), (size_t)D, nseg);
 }
 
 // ---------------------------------------------------------------------------

@@ -226,12 +226,18 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
         const uint4 raw = tok_u < nv ? pfs[p] : make_uint4(0, 0, 0, 0);
         if (u < QU) {
           if constexpr (FULL) {
+            // q / a, rounded to bfloat16 (exact for a = 1): then q.k comes out
+            // already divided by a, and the query features need no scaling
             const int tok = u >> 1, half = u & 1;
+            const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+            uint32_t sc[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sc[e] = pack2(lo_f(wd[e]) * inv_a, hi_f(wd[e]) * inv_a);
             uint16_t* d = &L.Q[b][tok][8 * half];
-            *reinterpret_cast<uint2*>(d) = make_uint2(raw.x, raw.y);
-            *reinterpret_cast<uint2*>(d + 4) = make_uint2(raw.z, raw.w);
-            *reinterpret_cast<uint2*>(d + 16) = make_uint2(raw.x, raw.y);
-            *reinterpret_cast<uint2*>(d + 20) = make_uint2(raw.z, raw.w);
+            *reinterpret_cast<uint2*>(d) = make_uint2(sc[0], sc[1]);
+            *reinterpret_cast<uint2*>(d + 4) = make_uint2(sc[2], sc[3]);
+            *reinterpret_cast<uint2*>(d + 16) = make_uint2(sc[0], sc[1]);
+            *reinterpret_cast<uint2*>(d + 20) = make_uint2(sc[2], sc[3]);
           }
         } else if (u < QU + 2 * C) {
           const int r = u - QU;
@@ -299,7 +305,6 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
   publish(0);
   __syncthreads();
 
-  const float a2 = inv_a * inv_a;  // 2 * alpha_2: the weight 2 of an off-diagonal monomial times alpha_2
   const int h = g & 1, gh = g >> 1;
 
   // Outputs of the chunk computed last, stored at the start of the next
@@ -317,17 +322,18 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
           if (tok < prev_nv) {
             TOUT* orow = o + ((size_t)bh * N + prev_t0 + tok) * kDV + 4 * g;
             const float inv = yinv[tw];
+            // non-temporal: the outputs are not read again by this kernel
             if constexpr (std::is_same_v<TOUT, float>) {
 #pragma unroll
               for (int ct = 0; ct < 4; ++ct)
-                *reinterpret_cast<float4*>(orow + 16 * ct) =
-                    make_float4(yo[tw][ct][0] * inv, yo[tw][ct][1] * inv, yo[tw][ct][2] * inv, yo[tw][ct][3] * inv);
+                __builtin_nontemporal_store(yo[tw][ct] * inv, reinterpret_cast<f32x4*>(orow + 16 * ct));
             } else {
+              typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 #pragma unroll
               for (int ct = 0; ct < 4; ++ct)
-                *reinterpret_cast<uint2*>(orow + 16 * ct) =
-                    make_uint2(pack2(yo[tw][ct][0] * inv, yo[tw][ct][1] * inv),
-                               pack2(yo[tw][ct][2] * inv, yo[tw][ct][3] * inv));
+                __builtin_nontemporal_store(u32x2{pack2(yo[tw][ct][0] * inv, yo[tw][ct][1] * inv),
+                                                  pack2(yo[tw][ct][2] * inv, yo[tw][ct][3] * inv)},
+                                            reinterpret_cast<u32x2*>(orow + 16 * ct));
             }
           }
         }
@@ -361,10 +367,7 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
                                f32_to_bf16(L.K[b][4 * g + 2][key0]), f32_to_bf16(L.K[b][4 * g + 3][key0])};
             const f32x4 s = mfma_bf16_k16(ak, bq, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float y = s[r] * inv_a;
-              p[r] = fmaf(y, fmaf(0.5f, y, 1.0f), 1.0f);
-            }
+            for (int r = 0; r < 4; ++r) p[r] = fmaf(s[r], fmaf(0.5f, s[r], 1.0f), 1.0f);  // s = q.k / a
             if (kt == tt) {  // diagonal tile: causal mask (key 16kt + 4g + r against token 16tt + li)
 #pragma unroll
               for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= li) ? p[r] : 0.0f;
@@ -412,11 +415,11 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
             zv[2 * e + 1] = hi_f(t1);
           }
         }
-        float yy[16];
-#pragma unroll
-        for (int s = 0; s < 16; ++s) yy[s] = a2 * yv[s];
+        // q is staged as q / a: the products y_s z_t already carry 2 alpha_2 = 1 / a^2,
+        // y_s carries alpha_1 = 1 / a
+        const float* yy = yv;
         const float kb0f = gh == 0 ? 0.5f : 1.0f;  // diagonal tile: weight 1 instead of 2
-        const float cA = g == 0 ? 1.0f : 0.0f, cB = g >= 2 ? inv_a : 0.0f, cC = g == 1 ? 1.0f : 0.0f;
+        const float cA = g == 0 ? 1.0f : 0.0f, cB = g >= 2 ? 1.0f : 0.0f, cC = g == 1 ? 1.0f : 0.0f;
         constexpr int kD0[4] = {0, 1, 4, 5};
 #pragma unroll
         for (int kb = 0; kb < 5; ++kb) {
@@ -535,8 +538,9 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
     const size_t slot = (size_t)bh * dst_slots + (dst_slots == 1 ? 0 : seg);
     float4* ds4 = reinterpret_cast<float4*>(dst_S + slot * kD3 * kDV);
     float* dt = dst_T + slot * kD3;
-    for (int i = tid; i < kD3 * kDV / 4; i += 256) ds4[i] = reinterpret_cast<const float4*>(img)[i];
-    for (int i = tid; i < kD3; i += 256) dt[i] = img[kD3 * kDV + i];
+    for (int i = tid; i < kD3 * kDV / 4; i += 256)
+      __builtin_nontemporal_store(reinterpret_cast<const f32x4*>(img)[i], reinterpret_cast<f32x4*>(ds4) + i);
+    for (int i = tid; i < kD3; i += 256) __builtin_nontemporal_store(img[kD3 * kDV + i], dt + i);
   }
 }
 
