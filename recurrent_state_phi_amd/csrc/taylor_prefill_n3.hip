@@ -187,78 +187,93 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
   }
 
 
-  // ---- global loads: 16-byte units.  FULL: [q: 2C | k: 2C | v: 8C];
-  //      otherwise [k: 2C | v: 8C].  Chunk c is loaded into register set c % 2
-  //      two chunks ahead of its use.  Every load is issued unconditionally
-  //      (addresses clamped into the segment, the values of padding tokens are
-  //      zeroed when staged), so the number of loads in flight is the same on
-  //      every path and the waits for them are exact.
-  constexpr int QU = FULL ? 2 * C : 0;
-  constexpr int UNITS = QU + 10 * C;
-  constexpr int NPF = (UNITS + 255) / 256;
-  constexpr int DEPTH = FULL ? 2 : 4;  // chunks in flight ahead of the one being staged
+  // ---- global loads.  Wave w loads its own token tiles 16(w + 4i) .. +15:
+  //      lane (li, g) takes columns 8g..8g+7 and 32+8g..+7 of v for token li of
+  //      the tile, and k (g < 2) or q (g >= 2, FULL) dimensions 8(g%2)..+7: the
+  //      natural row-major 16-byte pieces, which are exactly the A operand of
+  //      the transposing MFMAs in `stage`.  Chunk c is loaded into register set
+  //      c % DEPTH, DEPTH chunks ahead of its use.  Every load is issued
+  //      unconditionally (token index clamped into the segment; the values of
+  //      padding tokens are zeroed when staged), so the number of loads in
+  //      flight is the same on every path and the waits for them are exact.
+  constexpr int TPW = Sh::TPW;
+  constexpr int NPF = 3 * TPW;
+  constexpr int DEPTH = (FULL || C > 64) ? 2 : 4;
   uint4 pf[DEPTH][NPF];
   auto issue_loads = [&](uint4 (&pfs)[NPF], int chunk) {
     const int c0 = t_begin + min(chunk, nchunks - 1) * C;
     const int last = min(C, t_end - c0) - 1;
     const size_t base = (size_t)bh * N + c0;
 #pragma unroll
-    for (int p = 0; p < NPF; ++p) {
-      const int u = min(tid + 256 * p, UNITS - 1);
-      if (u < QU + 2 * C) {
-        const bool isq = u < QU;
-        const int r = isq ? u : u - QU;
-        const int tok = min(r >> 1, last), half = r & 1;
-        pfs[p] = *reinterpret_cast<const uint4*>((isq ? q : k) + (base + tok) * kD + 8 * half);
-      } else {
-        const int r = u - QU - 2 * C;
-        const int tok = min(r >> 3, last), c8 = r & 7;
-        pfs[p] = *reinterpret_cast<const uint4*>(v + (base + tok) * kDV + 8 * c8);
-      }
+    for (int i = 0; i < TPW; ++i) {
+      const size_t tok = base + min(16 * (w + 4 * i) + li, last);
+      pfs[3 * i] = *reinterpret_cast<const uint4*>(v + tok * kDV + 8 * g);
+      pfs[3 * i + 1] = *reinterpret_cast<const uint4*>(v + tok * kDV + 32 + 8 * g);
+      const uint16_t* kq = (FULL && g >= 2) ? q + tok * kD + 8 * (g - 2) : k + tok * kD + 8 * (g & 1);
+      pfs[3 * i + 2] = *reinterpret_cast<const uint4*>(kq);
     }
   };
+  // One-hot B operands: sel0 picks k-slots 0..15 and sel1 k-slots 16..31 of a
+  // 16x16x32 product, so that A . sel = the A rows transposed into the
+  // accumulator layout (lane (n, g) then holds rows 4g..4g+3 of column n).
+  // Exact: every product is a bfloat16 value times 1 or 0.
+  bf16x8 sel0, sel1;
+  {
+    uint32_t w0[4], w1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k0 = 8 * g + 2 * e;
+      w0[e] = (k0 == li ? 0x3F80u : 0u) | (k0 + 1 == li ? 0x3F800000u : 0u);
+      w1[e] = (k0 == li + 16 ? 0x3F80u : 0u) | (k0 + 1 == li + 16 ? 0x3F800000u : 0u);
+    }
+    sel0 = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
+    sel1 = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
+  }
   auto stage = [&](const uint4 (&pfs)[NPF], int b, int nv) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int p = 0; p < NPF; ++p) {
-      const int u = tid + 256 * p;
-      if (u < UNITS) {
-        const int tok_u = u < QU + 2 * C ? (u < QU ? u : u - QU) >> 1 : (u - QU - 2 * C) >> 3;
-        const uint4 raw = tok_u < nv ? pfs[p] : make_uint4(0, 0, 0, 0);
-        if (u < QU) {
-          if constexpr (FULL) {
-            // q / a, rounded to bfloat16 (exact for a = 1): then q.k comes out
-            // already divided by a, and the query features need no scaling
-            const int tok = u >> 1, half = u & 1;
-            const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-            uint32_t sc[4];
+    for (int i = 0; i < TPW; ++i) {
+      const int tt = w + 4 * i;
+      const bool valid = 16 * tt + li < nv;  // row li of the A operands
+      const uint4 z4 = make_uint4(0, 0, 0, 0);
+      const bf16x8 v0 = __builtin_bit_cast(bf16x8, valid ? pfs[3 * i] : z4);
+      const bf16x8 v1 = __builtin_bit_cast(bf16x8, valid ? pfs[3 * i + 1] : z4);
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, (valid && g < 2) ? pfs[3 * i + 2] : z4);
+      // V^T: four 16x16 tiles, lane (li, g) gets tokens 16tt + 4g + r of column 16ct + li
+      const f32x4 d0 = mfma_bf16_k32(v0, sel0, zero);
+      const f32x4 d1 = mfma_bf16_k32(v0, sel1, zero);
+      const f32x4 d2 = mfma_bf16_k32(v1, sel0, zero);
+      const f32x4 d3 = mfma_bf16_k32(v1, sel1, zero);
+      const f32x4 dv[4] = {d0, d1, d2, d3};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sc[e] = pack2(lo_f(wd[e]) * inv_a, hi_f(wd[e]) * inv_a);
-            uint16_t* d = &L.Q[b][tok][8 * half];
-            *reinterpret_cast<uint2*>(d) = make_uint2(sc[0], sc[1]);
-            *reinterpret_cast<uint2*>(d + 4) = make_uint2(sc[2], sc[3]);
-            *reinterpret_cast<uint2*>(d + 16) = make_uint2(sc[0], sc[1]);
-            *reinterpret_cast<uint2*>(d + 20) = make_uint2(sc[2], sc[3]);
-          }
-        } else if (u < QU + 2 * C) {
-          const int r = u - QU;
-          const int tok = r >> 1, half = r & 1;
+      for (int ct = 0; ct < 4; ++ct) {
+        const int c = 16 * ct + li;
+        *reinterpret_cast<uint2*>(&L.V[b][c][swz(c, 16 * tt + 4 * g)]) =
+            make_uint2(pack2(dv[ct][0], dv[ct][1]), pack2(dv[ct][2], dv[ct][3]));
+      }
+      // K^T (float): lane (li, g) gets dimension li of tokens 16tt + 4g + r
+      const f32x4 dk = mfma_bf16_k32(ka, sel0, zero);
+      *reinterpret_cast<f32x4*>(&L.K[b][li][16 * tt + 4 * g]) = dk;
+      if (li == 0) {
+        const int t0r = 16 * tt + 4 * g;
+        *reinterpret_cast<f32x4*>(&L.K[b][kOnes][t0r]) =
+            f32x4{t0r < nv ? 1.0f : 0.0f, t0r + 1 < nv ? 1.0f : 0.0f, t0r + 2 < nv ? 1.0f : 0.0f,
+                  t0r + 3 < nv ? 1.0f : 0.0f};
+      }
+      if constexpr (FULL) {
+        if (g >= 2) {
+          // q / a, rounded to bfloat16 (exact for a = 1): then q.k comes out
+          // already divided by a, and the query features need no scaling
+          const uint4 raw = valid ? pfs[3 * i + 2] : z4;
           const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+          uint32_t sc[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            L.K[b][8 * half + 2 * e][tok] = lo_f(wd[e]);
-            L.K[b][8 * half + 2 * e + 1][tok] = hi_f(wd[e]);
-          }
-          if (half == 0) L.K[b][kOnes][tok] = tok < nv ? 1.0f : 0.0f;
-        } else {
-          const int r = u - QU - 2 * C;
-          const int tok = r >> 3, c8 = r & 7;
-          const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c0 = 8 * c8 + 2 * e;
-            L.V[b][c0][swz(c0, tok)] = (uint16_t)(wd[e] & 0xFFFFu);
-            L.V[b][c0 + 1][swz(c0 + 1, tok)] = (uint16_t)(wd[e] >> 16);
-          }
+          for (int e = 0; e < 4; ++e) sc[e] = pack2(lo_f(wd[e]) * inv_a, hi_f(wd[e]) * inv_a);
+          uint16_t* d = &L.Q[b][16 * tt + li][8 * (g - 2)];
+          *reinterpret_cast<uint2*>(d) = make_uint2(sc[0], sc[1]);
+          *reinterpret_cast<uint2*>(d + 4) = make_uint2(sc[2], sc[3]);
+          *reinterpret_cast<uint2*>(d + 16) = make_uint2(sc[0], sc[1]);
+          *reinterpret_cast<uint2*>(d + 20) = make_uint2(sc[2], sc[3]);
         }
       }
     }
