@@ -139,6 +139,19 @@ def test_prefill_short_lengths(rsp, N):
     assert oracle.rel_err_rowwise(got, ref) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("a", [0.7, 2.0, 3.3])
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_bf16_prefill_temperatures(rsp, a, chunk):
+    """The bfloat16 n = 3 path stages q / a: check temperatures other than 1, ragged N, a resumed state."""
+    say("bf16 prefill a", a, "chunk", chunk)
+    q, k, v = TI.make_qkv(80, 2, 2, 777, 16, 64, dtype="bf16")
+    ref = oracle.taylor_direct(q, k, v, 3, a)
+    t1 = 300
+    a_out, st = run_prefill(rsp, q[:, :, :t1], k[:, :, :t1], v[:, :, :t1], 3, a, chunk, "bf16")
+    b_out, st = run_prefill(rsp, q[:, :, t1:], k[:, :, t1:], v[:, :, t1:], 3, a, chunk, "bf16", state=st)
+    assert oracle.rel_err_rowwise(np.concatenate([a_out, b_out], axis=2), ref) <= TOL["bf16"]
+
+
 def test_bf16_output(rsp):
     say("prefill bf16 out")
     q, k, v = TI.make_qkv(6, 1, 4, 700, 16, 64, dtype="bf16")
