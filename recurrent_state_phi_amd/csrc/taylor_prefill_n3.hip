@@ -5,17 +5,20 @@
 //
 // Same three-launch structure as the generic kernel (segment sums, scan of the
 // segment sums, replay of every segment from its prefix), but the work inside a
-// 256-thread workgroup is split so that no feature value is computed twice and
+// workgroup is split so that no feature value is computed twice and
 // the large operands never make a round trip through LDS:
 //
 //  * The state read Y^T = S'^T phi'(Q)^T (the off-diagonal part of Eq. (5)) and
 //    the diagonal block Y^T += [V, 1]^T P^T are split by TOKEN tile: wave w owns
-//    tokens 16w..16w+15 of a 64-token chunk (and 16(w+4).. for 128-token chunks).
+//    tokens 16w..16w+15 (4 waves for 64-token chunks, 8 waves for 128-token
+//    chunks, so that a 128-token workgroup, which fills most of the LDS on its
+//    own, still keeps two waves on every SIMD).
 //    The query features are built directly in the MFMA operand registers; the
 //    score block Q K^T, the polynomial P and its row sums never leave registers.
 //  * The state update S' += phi(K)^T [V, 1] (Eq. (6)-(7) summed over the chunk)
-//    is split by FEATURE tile: wave w owns tiles {w, w+4} for all 64 value
-//    columns and half of tile 8 + w/2.  The key features are built in operand
+//    is split by FEATURE tile: with 4 waves, wave w owns tiles {w, w+4} for all
+//    64 value columns and half of tile 8 + w/2; with 8 waves, tile w and a
+//    quarter of tile 8 + w/4.  The key features are built in operand
 //    registers from a transposed float32 copy of K; the ones-column T is the
 //    same product against a ones operand, on the matrix cores as well.
 //  * After its update every wave writes its part of the new state as a
@@ -55,9 +58,11 @@ constexpr int kKTRows = 17;
 
 template <int C>
 struct Shape {
-  static constexpr int NTT = C / 16;   // 16-token tiles per chunk
-  static constexpr int NKB = C / 32;   // 32-token k blocks per chunk
-  static constexpr int TPW = NTT / 4;  // token tiles per wave
+  static constexpr int NW = C == 128 ? 8 : 4;  // waves per workgroup
+  static constexpr int NTHREADS = 64 * NW;
+  static constexpr int NTT = C / 16;    // 16-token tiles per chunk
+  static constexpr int NKB = C / 32;    // 32-token k blocks per chunk
+  static constexpr int TPW = NTT / NW;  // token tiles per wave (1)
   static constexpr int VS = C + 8;     // V^T row stride (bf16)
   static constexpr int KS = C + 4;     // K^T row stride (float)
 };
@@ -119,7 +124,7 @@ __device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 
 __device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
 template <int C, bool FULL, typename TOUT>
-__global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
+__global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     TOUT* __restrict__ o, const float* __restrict__ pre_S, const float* __restrict__ pre_T, int pre_slots,
     float* __restrict__ dst_S, float* __restrict__ dst_T, int dst_slots, int N, int nseg, int cps, float inv_a) {
@@ -142,18 +147,23 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
   const int t_end = min(N, t_begin + cps * C);
   const int nchunks = (t_end - t_begin + C - 1) / C;
 
-  // ---- owned feature tiles: slot 0 = w, slot 1 = w + 4 (all 4 column tiles),
-  //      slot 2 = 8 + w/2 (column tiles ctb, ctb + 1).  T of slot 2 belongs to
-  //      waves 0 (tile 8) and 2 (tile 9).
-  const int ft_of[3] = {w, w + 4, 8 + (w >> 1)};
-  const int ctb = 2 * (w & 1);
-  const bool own_t2 = (w & 1) == 0;
+  // ---- owned feature tiles.  4 waves: slot 0 = tile w, slot 1 = tile w + 4
+  //      (all 4 column tiles), slot 2 = tile 8 + w/2 (column tiles ctb, ctb+1).
+  //      8 waves: slot 0 = tile w (4 column tiles), no slot 1, slot 2 = tile
+  //      8 + w/4 (column tile ctb = w % 4).  T of a slot-2 tile belongs to the
+  //      first of the waves sharing it.
+  constexpr int NW = Sh::NW, NTHREADS = Sh::NTHREADS;
+  constexpr bool HAS_S1 = NW == 4;
+  constexpr int NCT2 = NW == 4 ? 2 : 1;  // column tiles of slot 2
+  const int ft_of[3] = {w, w + 4, 8 + w / (NW / 2)};
+  const int ctb = (w % (NW / 2)) * NCT2;
+  const bool own_t2 = (w % (NW / 2)) == 0;
   int krow_j[3];
 #pragma unroll
   for (int s = 0; s < 3; ++s) krow_j[s] = k_row_j(ft_of[s], li);
   // the constant feature (tile 8, row 8): first factor 1 instead of x_8 (the
   // second factor is the ones row, which masks padding tokens)
-  const bool const_lane = (w >> 1) == 0 && li == 8;
+  const bool const_lane = w / (NW / 2) == 0 && li == 8;
 
   f32x4 acc[3][4];
   f32x4 tacc[3];  // T' on the matrix cores: column 0 (lanes li == 0) of a 16x16 tile
@@ -167,11 +177,12 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
     const size_t slot = (size_t)bh * pre_slots + (pre_slots == 1 ? 0 : seg);
     const float4* ps4 = reinterpret_cast<const float4*>(pre_S + slot * kD3 * kDV);
     const float* pt = pre_T + slot * kD3;
-    for (int i = tid; i < kD3 * kDV / 4; i += 256) reinterpret_cast<float4*>(img)[i] = ps4[i];
-    for (int i = tid; i < kD3; i += 256) img[kD3 * kDV + i] = pt[i];
+    for (int i = tid; i < kD3 * kDV / 4; i += NTHREADS) reinterpret_cast<float4*>(img)[i] = ps4[i];
+    for (int i = tid; i < kD3; i += NTHREADS) img[kD3 * kDV + i] = pt[i];
     __syncthreads();
 #pragma unroll
-    for (int s = 0; s < 3; ++s)
+    for (int s = 0; s < 3; ++s) {
+      if (s == 1 && !HAS_S1) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float wt;
@@ -180,14 +191,15 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
         const float sc = row >= 0 ? 1.0f / wt : 0.0f;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
-          if (s < 2 || ct < 2) acc[s][ct][r] = img[rc * kDV + 16 * (s == 2 ? ctb + ct : ct) + li] * sc;
+          if (s < 2 || ct < NCT2) acc[s][ct][r] = img[rc * kDV + 16 * (s == 2 ? ctb + ct : ct) + li] * sc;
         tacc[s][r] = li == 0 ? img[kD3 * kDV + rc] * sc : 0.0f;
       }
+    }
     __syncthreads();  // the image area is reused by the chunk buffers
   }
 
 
-  // ---- global loads.  Wave w loads its own token tiles 16(w + 4i) .. +15:
+  // ---- global loads.  Wave w loads its own token tile 16w .. 16w + 15:
   //      lane (li, g) takes columns 8g..8g+7 and 32+8g..+7 of v for token li of
   //      the tile, and k (g < 2) or q (g >= 2, FULL) dimensions 8(g%2)..+7: the
   //      natural row-major 16-byte pieces, which are exactly the A operand of
@@ -206,7 +218,7 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
     const size_t base = (size_t)bh * N + c0;
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const size_t tok = base + min(16 * (w + 4 * i) + li, last);
+      const size_t tok = base + min(16 * (w + NW * i) + li, last);
       pfs[3 * i] = *reinterpret_cast<const uint4*>(v + tok * kDV + 8 * g);
       pfs[3 * i + 1] = *reinterpret_cast<const uint4*>(v + tok * kDV + 32 + 8 * g);
       const uint16_t* kq = (FULL && g >= 2) ? q + tok * kD + 8 * (g - 2) : k + tok * kD + 8 * (g & 1);
@@ -233,7 +245,7 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
-      const int tt = w + 4 * i;
+      const int tt = w + NW * i;
       const bool valid = 16 * tt + li < nv;  // row li of the A operands
       const uint4 z4 = make_uint4(0, 0, 0, 0);
       const bf16x8 v0 = __builtin_bit_cast(bf16x8, valid ? pfs[3 * i] : z4);
@@ -283,10 +295,11 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
     if constexpr (FULL) {
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
+        if (s == 1 && !HAS_S1) continue;
         const int ks = kslot_of(ft_of[s], 4 * g);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          if (s < 2 || ct < 2) {
+          if (s < 2 || ct < NCT2) {
             const int c = 16 * (s == 2 ? ctb + ct : ct) + li;
             *reinterpret_cast<uint2*>(&L.S[b][c][ks]) =
                 make_uint2(pack2(acc[s][ct][0], acc[s][ct][1]), pack2(acc[s][ct][2], acc[s][ct][3]));
@@ -307,9 +320,9 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
   };
 
   // zero rows of K^T in both buffers (never overwritten)
-  for (int i = tid; i < C; i += 256) L.Kz[i] = 0.0f;
+  for (int i = tid; i < C; i += NTHREADS) L.Kz[i] = 0.0f;
   if constexpr (FULL)
-    for (int i = tid; i < kNF; i += 256) L.Tz[i] = 0;
+    for (int i = tid; i < kNF; i += NTHREADS) L.Tz[i] = 0;
   // chunk c lives in register set c % DEPTH; chunks 1..DEPTH are in flight
   // when the loop starts, and body(j) refills the set it stages from with
   // chunk j + 1 + DEPTH
@@ -333,7 +346,7 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
       if (prev_t0 >= 0) {
 #pragma unroll
         for (int tw = 0; tw < Sh::TPW; ++tw) {
-          const int tok = 16 * (w + 4 * tw) + li;
+          const int tok = 16 * (w + NW * tw) + li;
           if (tok < prev_nv) {
             TOUT* orow = o + ((size_t)bh * N + prev_t0 + tok) * kDV + 4 * g;
             const float inv = yinv[tw];
@@ -367,7 +380,7 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
     if constexpr (FULL) {
 #pragma unroll
       for (int tw = 0; tw < Sh::TPW; ++tw) {
-        const int tt = w + 4 * tw;  // token tile, wave-uniform
+        const int tt = w + NW * tw;  // token tile, wave-uniform
         const int tok = 16 * tt + li;
 
         // ---- diagonal block: P = tril(p_3(K Q^T / a)), lane holds P[token li][keys]
@@ -492,6 +505,7 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
         }
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
+          if (s == 1 && !HAS_S1) continue;
           const float* kj = krow_j[s] == kZero ? &L.Kz[0] : &L.K[b][krow_j[s]][0];
           const float4 b0 = *reinterpret_cast<const float4*>(kj + t8);
           const float4 b1 = *reinterpret_cast<const float4*>(kj + t8 + 4);
@@ -507,13 +521,20 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
             tacc[s] = mfma_bf16_k32(aphi, ones, tacc[s]);
           } else {
             if (own_t2) tacc[2] = mfma_bf16_k32(aphi, ones, tacc[2]);
-            // column tiles ctb, ctb + 1 (ctb is wave-uniform)
-            if (ctb == 0) {
-              acc[2][0] = mfma_bf16_k32(aphi, vb[0], acc[2][0]);
-              acc[2][1] = mfma_bf16_k32(aphi, vb[1], acc[2][1]);
+            // column tiles ctb .. ctb + NCT2 - 1 (ctb is wave-uniform)
+            if constexpr (NCT2 == 2) {
+              if (ctb == 0) {
+                acc[2][0] = mfma_bf16_k32(aphi, vb[0], acc[2][0]);
+                acc[2][1] = mfma_bf16_k32(aphi, vb[1], acc[2][1]);
+              } else {
+                acc[2][0] = mfma_bf16_k32(aphi, vb[2], acc[2][0]);
+                acc[2][1] = mfma_bf16_k32(aphi, vb[3], acc[2][1]);
+              }
             } else {
-              acc[2][0] = mfma_bf16_k32(aphi, vb[2], acc[2][0]);
-              acc[2][1] = mfma_bf16_k32(aphi, vb[3], acc[2][1]);
+              if (ctb == 0) acc[2][0] = mfma_bf16_k32(aphi, vb[0], acc[2][0]);
+              else if (ctb == 1) acc[2][0] = mfma_bf16_k32(aphi, vb[1], acc[2][0]);
+              else if (ctb == 2) acc[2][0] = mfma_bf16_k32(aphi, vb[2], acc[2][0]);
+              else acc[2][0] = mfma_bf16_k32(aphi, vb[3], acc[2][0]);
             }
           }
         }
@@ -537,6 +558,7 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
     // rows of the internal layout map nowhere)
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
+      if (s == 1 && !HAS_S1) continue;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float wt;
@@ -544,7 +566,7 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
         if (row >= 0) {
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct)
-            if (s < 2 || ct < 2) img[row * kDV + 16 * (s == 2 ? ctb + ct : ct) + li] = acc[s][ct][r] * wt;
+            if (s < 2 || ct < NCT2) img[row * kDV + 16 * (s == 2 ? ctb + ct : ct) + li] = acc[s][ct][r] * wt;
           if (li == 0 && (s < 2 || own_t2)) img[kD3 * kDV + row] = tacc[s][r] * wt;
         }
       }
@@ -553,9 +575,9 @@ __global__ __launch_bounds__(256, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
     const size_t slot = (size_t)bh * dst_slots + (dst_slots == 1 ? 0 : seg);
     float4* ds4 = reinterpret_cast<float4*>(dst_S + slot * kD3 * kDV);
     float* dt = dst_T + slot * kD3;
-    for (int i = tid; i < kD3 * kDV / 4; i += 256)
+    for (int i = tid; i < kD3 * kDV / 4; i += NTHREADS)
       __builtin_nontemporal_store(reinterpret_cast<const f32x4*>(img)[i], reinterpret_cast<f32x4*>(ds4) + i);
-    for (int i = tid; i < kD3; i += 256) __builtin_nontemporal_store(img[kD3 * kDV + i], dt + i);
+    for (int i = tid; i < kD3; i += NTHREADS) __builtin_nontemporal_store(img[kD3 * kDV + i], dt + i);
   }
 }
 
@@ -573,13 +595,13 @@ hipError_t launch(const PrefillArgs& a) {
   if (pl.nseg > 1) {
     float* W_S = a.workspace;
     float* W_T = a.workspace + (size_t)a.BH * pl.nseg * kD3 * kDV;
-    hipLaunchKernelGGL((prefill_n3_kernel<C, false, TOUT>), dim3(a.BH * (pl.nseg - 1)), dim3(256), 0, a.stream, q,
+    hipLaunchKernelGGL((prefill_n3_kernel<C, false, TOUT>), dim3(a.BH * (pl.nseg - 1)), dim3(Shape<C>::NTHREADS), 0, a.stream, q,
                        k, v, static_cast<TOUT*>(nullptr), (const float*)nullptr, (const float*)nullptr, 1, W_S, W_T,
                        pl.nseg, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
     if (ev) (void)hipEventRecord(ev[1], a.stream);
     if (hipError_t e = launch_segment_scan(st_S, st_T, W_S, W_T, kD3, pl.nseg, a.BH, a.stream)) return e;
     if (ev) (void)hipEventRecord(ev[2], a.stream);
-    hipLaunchKernelGGL((prefill_n3_kernel<C, true, TOUT>), dim3(a.BH * pl.nseg), dim3(256), 0, a.stream, q, k, v,
+    hipLaunchKernelGGL((prefill_n3_kernel<C, true, TOUT>), dim3(a.BH * pl.nseg), dim3(Shape<C>::NTHREADS), 0, a.stream, q, k, v,
                        static_cast<TOUT*>(a.o), W_S, W_T, pl.nseg, st_S, st_T, 1, a.N, pl.nseg, pl.chunks_per_seg,
                        inv_a);
   } else {
@@ -587,7 +609,7 @@ hipError_t launch(const PrefillArgs& a) {
       (void)hipEventRecord(ev[1], a.stream);
       (void)hipEventRecord(ev[2], a.stream);
     }
-    hipLaunchKernelGGL((prefill_n3_kernel<C, true, TOUT>), dim3(a.BH), dim3(256), 0, a.stream, q, k, v,
+    hipLaunchKernelGGL((prefill_n3_kernel<C, true, TOUT>), dim3(a.BH), dim3(Shape<C>::NTHREADS), 0, a.stream, q, k, v,
                        static_cast<TOUT*>(a.o), st_S, st_T, 1, st_S, st_T, 1, a.N, 1, pl.chunks_per_seg, inv_a);
   }
   if (ev) (void)hipEventRecord(ev[3], a.stream);
