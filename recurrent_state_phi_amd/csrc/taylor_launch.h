@@ -22,7 +22,7 @@ struct PrefillPlan {
   int nchunks = 0;
   int nseg = 1;
   int chunks_per_seg = 0;
-  size_t workspace_floats = 0;  // BH * nseg * D * 65 when nseg > 1, else 0
+  size_t workspace_floats = 0;  // 0 when nseg == 1
 };
 
 PrefillPlan plan_prefill(int BH, int N, int n, int chunk);
@@ -42,8 +42,10 @@ struct PrefillArgs {
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 
-// n = 3, bfloat16 inputs, chunk 64 or 128 (taylor_prefill_n3.hip).
+// n = 3, bfloat16 inputs, chunk 64 or 128 (taylor_prefill_n3.hip): one
+// launch with a look-back across segments, and the workspace it needs.
 hipError_t launch_prefill_n3_bf16(const PrefillArgs& a);
+size_t prefill_n3_workspace_floats(int BH, int nseg);
 
 // n = 4, feature-blocked, chunk 32 or 64 (taylor_prefill_fb.hip), and the
 // floats of its per-block output workspace.

@@ -37,6 +37,8 @@
 //   - three barriers per chunk: inputs staged | features and P ready | chunk done.
 #include <type_traits>
 
+#include <algorithm>
+
 #include "taylor_device.h"
 #include "taylor_launch.h"
 
@@ -573,16 +575,21 @@ PrefillPlan plan_prefill(int BH, int N, int n, int chunk) {
   if (BH <= 0 || N <= 0 || chunk <= 0) return p;
   p.nchunks = (N + chunk - 1) / chunk;
   // Aim for at least 512 workgroups in the chunk kernel (two per CU on a
-  // 256-CU part) when the heads alone do not provide them.  For n = 4 every
+  // 256-CU part) when the heads alone do not provide them; 128-token chunks
+  // fill an LDS on their own, so for them aim at one workgroup per CU.  For n = 4 every
   // segment is split into 6 feature blocks, one workgroup each.
   const int blocks = n == 4 ? 6 : 1;
-  int nseg = (512 + BH * blocks - 1) / (BH * blocks);
+  const int target = chunk >= 128 ? 256 : 512;
+  int nseg = (target + BH * blocks - 1) / (BH * blocks);
   if (nseg < 1) nseg = 1;
   if (nseg > p.nchunks) nseg = p.nchunks;
   p.chunks_per_seg = (p.nchunks + nseg - 1) / nseg;
   p.nseg = (p.nchunks + p.chunks_per_seg - 1) / p.chunks_per_seg;
   const int D = n == 1 ? state_width(1) : n == 2 ? state_width(2) : n == 3 ? state_width(3) : state_width(4);
   p.workspace_floats = p.nseg > 1 ? (size_t)BH * p.nseg * D * (kDV + 1) : 0;
+  // n = 3 with bfloat16 inputs takes the look-back kernel, whose workspace is
+  // larger; the size does not depend on the input type, so cover both
+  if (n == 3) p.workspace_floats = std::max(p.workspace_floats, prefill_n3_workspace_floats(BH, p.nseg));
   if (n == 4) p.workspace_floats += prefill_fb_output_floats(BH, N);
   return p;
 }

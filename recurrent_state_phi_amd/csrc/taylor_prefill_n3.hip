@@ -3,10 +3,31 @@
 // arXiv 2610.20637): float32 state, bfloat16 matrix-core operands, float32
 // accumulation.
 //
-// Same three-launch structure as the generic kernel (segment sums, scan of the
-// segment sums, replay of every segment from its prefix), but the work inside a
-// workgroup is split so that no feature value is computed twice and
-// the large operands never make a round trip through LDS:
+// ONE launch.  Every (b, h) sequence is cut into `nseg` segments; one
+// workgroup per segment:
+//
+//  1. segment sum: the workgroup runs the state update over its segment from a
+//     zero state (Eq. (6)-(7) summed over the segment; the states are additive
+//     across chunks, section 3.5).  Segment 0 adds the caller's state to its
+//     sum.  The sum A_s is published to the workspace.
+//  2. prefix: the segments form groups of `gs` consecutive segments.  The last
+//     segment of a group publishes the GROUP sum (its own sum plus those of
+//     the earlier members) in place of its own.  The exclusive prefix of
+//     segment s is then the group sums of the earlier groups plus the sums of
+//     the earlier members of its own group: at most about 2 sqrt(nseg) state
+//     images per workgroup, all published right after step 1.
+//  3. replay: it runs the segment again from its prefix, producing the outputs
+//     (Eq. (5)), and the last segment writes the final state.
+//
+// Workgroups take their segment from an atomic ticket counter, and a workgroup
+// only ever waits for segments with a smaller number, which hold smaller
+// tickets: they started before it, are running (or done), and every wait ends.
+// Each wait is bounded all the same; a wait that runs out records an error
+// code in the workspace.  The replay reads the segment's q, k, v shortly after
+// step 1 read k and v, mostly from cache.
+//
+// Inside a chunk the work of the workgroup is split so that no feature value is
+// computed twice and the large operands never make a round trip through LDS:
 //
 //  * The state read Y^T = S'^T phi'(Q)^T (the off-diagonal part of Eq. (5)) and
 //    the diagonal block Y^T += [V, 1]^T P^T are split by TOKEN tile: wave w owns
@@ -56,6 +77,30 @@ constexpr int kOnes = 16;  // K^T row holding 1 for valid tokens, 0 for padding
 constexpr int kZero = 17;  // index standing for the zero row (stored once, outside the double buffer)
 constexpr int kKTRows = 17;
 
+// Workspace of a multi-segment call (32-bit words):
+//   [0]                    ticket counter
+//   [1]                    error code (nonzero: a look-back wait ran out)
+//   [kHdr + kFlagStride * (b * nseg + s)]  flag of segment s of sequence b:
+//                          nonzero once its image is published (one flag per
+//                          256 bytes: polls of different flags do not queue
+//                          on the same memory line)
+//   then BH*nseg state images: the segment sums (group sums at the last
+//   member of a group)
+// The header (counter, error, flags) is cleared by a small kernel before every
+// call.  A state image is the internal state in the register layout of the
+// owning waves: kImgS floats of S' (every wave's (slot, column tile) pairs,
+// lane-major, 16 bytes per lane) and 384 floats of T'.
+constexpr int kHdr = 64;
+constexpr int kFlagStride = 64;
+constexpr int kImgS = 40 * 64 * 4;       // 40 owned (slot, column tile) pairs per workgroup
+constexpr int kImgFloats = kImgS + 384;  // + T': waves x 3 slots x 4 lane groups x 4 rows (8 waves)
+constexpr int kSpinLimit = 1 << 20;      // polls of one look-back wait (a short sleep each: >= 0.4 s)
+constexpr int kErrWait = 1;
+
+__host__ __device__ constexpr size_t header_words(int BH, int nseg) {
+  return kHdr + (size_t)BH * nseg * kFlagStride;
+}
+
 template <int C>
 struct Shape {
   static constexpr int NW = C == 128 ? 8 : 4;  // waves per workgroup
@@ -63,20 +108,47 @@ struct Shape {
   static constexpr int NTT = C / 16;    // 16-token tiles per chunk
   static constexpr int NKB = C / 32;    // 32-token k blocks per chunk
   static constexpr int TPW = NTT / NW;  // token tiles per wave (1)
-  static constexpr int VS = C + 8;     // V^T row stride (bf16)
-  static constexpr int KS = C + 4;     // K^T row stride (float)
+  static constexpr int VS = C + 8;      // V^T row stride (bf16)
+  static constexpr int KS = C + 4;      // K^T row stride (float)
+  // feature-tile ownership (see Own)
+  static constexpr bool HAS_S1 = NW == 4;
+  static constexpr int NCT2 = NW == 4 ? 2 : 1;          // column tiles of slot 2
+  static constexpr int NCTS = (HAS_S1 ? 8 : 4) + NCT2;  // owned (slot, column tile) pairs per wave
+  static_assert(NW * NCTS == 40, "state image layout");
+  static __device__ __forceinline__ constexpr bool has(int s, int ct) {
+    return s == 0 || (s == 1 && HAS_S1) || (s == 2 && ct < NCT2);
+  }
+  static __device__ __forceinline__ constexpr int pair_index(int s, int ct) {
+    return s == 0 ? ct : s == 1 ? 4 + ct : (HAS_S1 ? 8 : 4) + ct;
+  }
 };
 
-template <int C, bool FULL>
+template <int C>
 struct Lds {
-  alignas(16) uint16_t S[FULL ? 2 : 1][FULL ? 64 : 1][kSS];  // S'^T copy (bf16), k-slot order, swizzled
-  alignas(16) uint16_t T[FULL ? 2 : 1][2][kNF];             // T' in k-slot order: bf16 high, low parts
-  alignas(16) uint16_t Tz[FULL ? kNF : 8];                   // zeros (the other rows of the T operand)
-  alignas(16) uint16_t V[2][64][Shape<C>::VS];               // V^T (bf16), swizzled
-  alignas(16) float K[2][kKTRows][Shape<C>::KS];             // K^T (float) + ones row
-  alignas(16) float Kz[Shape<C>::KS];                        // zero row
-  alignas(16) uint16_t Q[FULL ? 2 : 1][FULL ? C : 1][kQS];   // q twice per row: [x | x]
+  alignas(16) uint16_t S[2][64][kSS];             // S'^T copy (bf16), k-slot order, swizzled
+  alignas(16) uint16_t T[2][2][kNF];              // T' in k-slot order: bf16 high, low parts
+  alignas(16) uint16_t Tz[kNF];                   // zeros (the other rows of the T operand)
+  alignas(16) uint16_t V[2][64][Shape<C>::VS];    // V^T (bf16), swizzled
+  alignas(16) float K[2][kKTRows][Shape<C>::KS];  // K^T (float) + ones row
+  alignas(16) float Kz[Shape<C>::KS];             // zero row
+  alignas(16) uint16_t Q[2][C][kQS];              // q twice per row: [x | x]
 };
+
+// The state of a workgroup in registers: 16x16 accumulator tiles of the owned
+// (feature tile, column tile) pairs, and T' as column 0 of a 16x16 tile.
+struct Acc {
+  f32x4 s[3][4];
+  f32x4 t[3];
+};
+
+__device__ __forceinline__ void zero_acc(Acc& a) {
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    a.t[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) a.s[s][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+}
 
 // 16-byte-chunk XOR swizzle of the rows of V^T: rows c and c + 16 land in
 // different banks.
@@ -123,81 +195,220 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
 __device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
 
-template <int C, bool FULL, typename TOUT>
-__global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    TOUT* __restrict__ o, const float* __restrict__ pre_S, const float* __restrict__ pre_T, int pre_slots,
-    float* __restrict__ dst_S, float* __restrict__ dst_T, int dst_slots, int N, int nseg, int cps, float inv_a) {
-  using Sh = Shape<C>;
-  constexpr int NKB = Sh::NKB;
-  // The chunk buffers, and at the start and the end of the kernel a float
-  // [153 * 65] image of the state in the caller's layout (loaded and stored
-  // with full 16-byte accesses; the lanes then pick their rows from LDS).
-  constexpr int kImg = kD3 * (kDV + 1);
-  __shared__ __align__(16) unsigned char lds_raw[sizeof(Lds<C, FULL>) > kImg * 4 ? sizeof(Lds<C, FULL>) : kImg * 4];
-  Lds<C, FULL>& L = *reinterpret_cast<Lds<C, FULL>*>(lds_raw);
-  float* img = reinterpret_cast<float*>(lds_raw);
-
-  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
-  // wave index in a scalar register: every branch around an MFMA is uniform
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int gseg = FULL ? nseg : nseg - 1;
-  const int bh = blockIdx.x / gseg, seg = blockIdx.x % gseg;
-  const int t_begin = seg * cps * C;
-  const int t_end = min(N, t_begin + cps * C);
-  const int nchunks = (t_end - t_begin + C - 1) / C;
-
-  // ---- owned feature tiles.  4 waves: slot 0 = tile w, slot 1 = tile w + 4
-  //      (all 4 column tiles), slot 2 = tile 8 + w/2 (column tiles ctb, ctb+1).
-  //      8 waves: slot 0 = tile w (4 column tiles), no slot 1, slot 2 = tile
-  //      8 + w/4 (column tile ctb = w % 4).  T of a slot-2 tile belongs to the
-  //      first of the waves sharing it.
-  constexpr int NW = Sh::NW, NTHREADS = Sh::NTHREADS;
-  constexpr bool HAS_S1 = NW == 4;
-  constexpr int NCT2 = NW == 4 ? 2 : 1;  // column tiles of slot 2
-  const int ft_of[3] = {w, w + 4, 8 + w / (NW / 2)};
-  const int ctb = (w % (NW / 2)) * NCT2;
-  const bool own_t2 = (w % (NW / 2)) == 0;
+// Feature tiles and column tiles a wave owns.  4 waves: slot 0 = tile w, slot
+// 1 = tile w + 4 (all 4 column tiles), slot 2 = tile 8 + w/2 (column tiles
+// ctb, ctb + 1).  8 waves: slot 0 = tile w (4 column tiles), no slot 1, slot 2
+// = tile 8 + w/4 (column tile ctb = w % 4).  T' of a slot-2 tile belongs to the
+// first of the waves sharing it.
+template <int C>
+struct Own {
+  int ft[3];
+  int ctb;
+  bool own_t2;
+  bool const_lane;  // lane that builds the constant feature (tile 8, row 8)
   int krow_j[3];
+  __device__ __forceinline__ Own(int w, int li) {
+    constexpr int NW = Shape<C>::NW;
+    ft[0] = w;
+    ft[1] = w + 4;
+    ft[2] = 8 + w / (NW / 2);
+    ctb = (w % (NW / 2)) * Shape<C>::NCT2;
+    own_t2 = (w % (NW / 2)) == 0;
+    const_lane = w / (NW / 2) == 0 && li == 8;
 #pragma unroll
-  for (int s = 0; s < 3; ++s) krow_j[s] = k_row_j(ft_of[s], li);
-  // the constant feature (tile 8, row 8): first factor 1 instead of x_8 (the
-  // second factor is the ones row, which masks padding tokens)
-  const bool const_lane = w / (NW / 2) == 0 && li == 8;
-
-  f32x4 acc[3][4];
-  f32x4 tacc[3];  // T' on the matrix cores: column 0 (lanes li == 0) of a 16x16 tile
-#pragma unroll
-  for (int s = 0; s < 3; ++s) {
-    tacc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[s][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < 3; ++s) krow_j[s] = k_row_j(ft[s], li);
   }
-  if (FULL && pre_S != nullptr) {  // uniform
-    const size_t slot = (size_t)bh * pre_slots + (pre_slots == 1 ? 0 : seg);
-    const float4* ps4 = reinterpret_cast<const float4*>(pre_S + slot * kD3 * kDV);
-    const float* pt = pre_T + slot * kD3;
-    for (int i = tid; i < kD3 * kDV / 4; i += NTHREADS) reinterpret_cast<float4*>(img)[i] = ps4[i];
-    for (int i = tid; i < kD3; i += NTHREADS) img[kD3 * kDV + i] = pt[i];
-    __syncthreads();
+};
+
+// ---- state images in the workspace (register layout, see above) -----------
+// Images and flags move between workgroups that may sit on different XCDs
+// (each with its own L2).  Every image access is a buffer access with the
+// device-scope cache policy (sc1): stores are written through to where all
+// XCDs see them before they count as complete, and loads never hit a stale L2
+// line.  So the handover needs no whole-cache write-back or invalidate: the
+// writer waits for its stores to complete, then raises the flag (a device-scope
+// atomic store); the reader issues its image loads after it has seen the flag.
+constexpr int kSC1 = 16;                    // buffer cache policy: device scope
+constexpr int kBufWord3 = 0x00020000;       // buffer descriptor word 3 (gfx9: 32-bit data, raw)
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t image_rsrc(const float* img) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(img), 0, kImgFloats * 4, kBufWord3);
+}
+
+// Writes a (ADD = false) or a + b (ADD = true).
+template <int C, bool ADD>
+__device__ __forceinline__ void image_store(float* img, const Acc& a, const Acc& b, int w, int lane) {
+  using Sh = Shape<C>;
+  const int li = lane & 15, g = lane >> 4;
+  const __amdgpu_buffer_rsrc_t r = image_rsrc(img);
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      if (Sh::has(s, ct)) {
+        const f32x4 x = ADD ? a.s[s][ct] + b.s[s][ct] : a.s[s][ct];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r,
+                                               ((w * Sh::NCTS + Sh::pair_index(s, ct)) * 64 + lane) * 16, 0, kSC1);
+      }
+  if (li == 0) {
 #pragma unroll
     for (int s = 0; s < 3; ++s) {
-      if (s == 1 && !HAS_S1) continue;
+      const f32x4 x = ADD ? a.t[s] + b.t[s] : a.t[s];
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r,
+                                             (kImgS + ((w * 3 + s) * 4 + g) * 4) * 4, 0, kSC1);
+    }
+  }
+}
+
+// a += the image at img.
+template <int C>
+__device__ __forceinline__ void image_add(const float* img, Acc& a, int w, int lane) {
+  using Sh = Shape<C>;
+  const int li = lane & 15, g = lane >> 4;
+  const __amdgpu_buffer_rsrc_t r = image_rsrc(img);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float wt;
-        const int row = abi_row(ft_of[s], 4 * g + r, &wt);
-        const int rc = max(row, 0);
-        const float sc = row >= 0 ? 1.0f / wt : 0.0f;
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      if (Sh::has(s, ct))
+        a.s[s][ct] += __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       r, ((w * Sh::NCTS + Sh::pair_index(s, ct)) * 64 + lane) * 16, 0, kSC1));
+  if (li == 0) {
+#pragma unroll
+    for (int s = 0; s < 3; ++s)
+      a.t[s] += __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (kImgS + ((w * 3 + s) * 4 + g) * 4) * 4, 0, kSC1));
+  }
+}
+
+// Publish this workgroup's image: every wave waits until its image stores are
+// complete, then (after the barrier) one thread raises the flag.
+__device__ __forceinline__ void raise_flag(int* flag, int value) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait (per wave) until *flag is nonzero and return it; 0 after kSpinLimit
+// polls, with the error recorded.
+__device__ __forceinline__ int wait_flag(const int* flag, int* err) {
+  for (int i = 0; i < kSpinLimit; ++i) {
+    const int v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (v != 0) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      return v;
+    }
+    __builtin_amdgcn_s_sleep(16);
+  }
+  __hip_atomic_store(err, kErrWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return 0;
+}
+
+// ---- the caller's state layout <-> registers ------------------------------
+// The [153 x 64] S and [153] T of one head, with the sqrt-multinomial weights
+// divided out (load) or applied (store).
+constexpr int kAbiImg = kD3 * (kDV + 1);
+
+// The caller's state straight into registers (no LDS, no barrier, so the loads
+// can stay in flight during the first pass): raw values first, then the
+// sqrt-multinomial weights divided out once they are needed.
+template <int C>
+__device__ __forceinline__ void load_caller_state_raw(const float* st_S, const float* st_T, int bh, const Own<C>& own,
+                                                      Acc& a) {
+  using Sh = Shape<C>;
+  const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+  const float* S = st_S + (size_t)bh * kD3 * kDV;
+  const float* T = st_T + (size_t)bh * kD3;
+  zero_acc(a);
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (s == 1 && !Sh::HAS_S1) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float wt;
+      const int rc = max(abi_row(own.ft[s], 4 * g + r, &wt), 0);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        a.s[s][ct][r] = Sh::has(s, ct) ? S[rc * kDV + 16 * (s == 2 ? own.ctb + ct : ct) + li] : 0.0f;
+      a.t[s][r] = T[rc];
+    }
+  }
+}
+
+template <int C>
+__device__ __forceinline__ void unweight_caller_state(const Own<C>& own, Acc& a) {
+  using Sh = Shape<C>;
+  const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    const bool own_t = li == 0 && (s == 0 || (s == 1 && Sh::HAS_S1) || (s == 2 && own.own_t2));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float wt;
+      const int row = abi_row(own.ft[s], 4 * g + r, &wt);
+      const float sc = 1.0f / wt;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        a.s[s][ct][r] = (row >= 0 && Sh::has(s, ct)) ? a.s[s][ct][r] * sc : 0.0f;
+      a.t[s][r] = (row >= 0 && own_t) ? a.t[s][r] * sc : 0.0f;
+    }
+  }
+}
+
+// Stored through LDS as a float image, so that the global stores are full
+// 16-byte accesses.
+template <int C>
+__device__ __forceinline__ void store_caller_state(float* img, float* st_S, float* st_T, int bh, const Own<C>& own,
+                                                   const Acc& a) {
+  using Sh = Shape<C>;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  // every row of the image is written by exactly one lane group (zero rows of
+  // the internal layout map nowhere)
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (s == 1 && !Sh::HAS_S1) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float wt;
+      const int row = abi_row(own.ft[s], 4 * g + r, &wt);
+      if (row >= 0) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
-          if (s < 2 || ct < NCT2) acc[s][ct][r] = img[rc * kDV + 16 * (s == 2 ? ctb + ct : ct) + li] * sc;
-        tacc[s][r] = li == 0 ? img[kD3 * kDV + rc] * sc : 0.0f;
+          if (Sh::has(s, ct)) img[row * kDV + 16 * (s == 2 ? own.ctb + ct : ct) + li] = a.s[s][ct][r] * wt;
+        if (li == 0 && (s < 2 || own.own_t2)) img[kD3 * kDV + row] = a.t[s][r] * wt;
       }
     }
-    __syncthreads();  // the image area is reused by the chunk buffers
   }
+  __syncthreads();
+  float4* ds4 = reinterpret_cast<float4*>(st_S + (size_t)bh * kD3 * kDV);
+  float* dt = st_T + (size_t)bh * kD3;
+  for (int i = tid; i < kD3 * kDV / 4; i += Sh::NTHREADS)
+    __builtin_nontemporal_store(reinterpret_cast<const f32x4*>(img)[i], reinterpret_cast<f32x4*>(ds4) + i);
+  for (int i = tid; i < kD3; i += Sh::NTHREADS) __builtin_nontemporal_store(img[kD3 * kDV + i], dt + i);
+}
 
+// ---- one pass over the chunks [t_begin, t_end) of sequence bh --------------
+// FULL = false: state update only (a += the segment's sum).
+// FULL = true: outputs of every token and the state update.
+template <int C, bool FULL, typename TOUT>
+__device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<C>& own, Acc& a, const uint16_t* __restrict__ q,
+                                             const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                             TOUT* __restrict__ o, int bh, int N, int t_begin, int t_end,
+                                             float inv_a) {
+  using Sh = Shape<C>;
+  constexpr int NKB = Sh::NKB, NW = Sh::NW, NTHREADS = Sh::NTHREADS, NCT2 = Sh::NCT2;
+  constexpr bool HAS_S1 = Sh::HAS_S1;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nchunks = (t_end - t_begin + C - 1) / C;
+  if (nchunks <= 0) return;  // uniform
+  f32x4(&acc)[3][4] = a.s;
+  f32x4(&tacc)[3] = a.t;
+  const int ctb = own.ctb;
+  const bool own_t2 = own.own_t2, const_lane = own.const_lane;
 
   // ---- global loads.  Wave w loads its own token tile 16w .. 16w + 15:
   //      lane (li, g) takes columns 8g..8g+7 and 32+8g..+7 of v for token li of
@@ -296,10 +507,10 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
         if (s == 1 && !HAS_S1) continue;
-        const int ks = kslot_of(ft_of[s], 4 * g);
+        const int ks = kslot_of(own.ft[s], 4 * g);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          if (s < 2 || ct < NCT2) {
+          if (Sh::has(s, ct)) {
             const int c = 16 * (s == 2 ? ctb + ct : ct) + li;
             *reinterpret_cast<uint2*>(&L.S[b][c][ks]) =
                 make_uint2(pack2(acc[s][ct][0], acc[s][ct][1]), pack2(acc[s][ct][2], acc[s][ct][3]));
@@ -319,7 +530,7 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
     }
   };
 
-  // zero rows of K^T in both buffers (never overwritten)
+  // zero rows of K^T and of the T operand (never overwritten)
   for (int i = tid; i < C; i += NTHREADS) L.Kz[i] = 0.0f;
   if constexpr (FULL)
     for (int i = tid; i < kNF; i += NTHREADS) L.Tz[i] = 0;
@@ -338,14 +549,14 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
   // Outputs of the chunk computed last, stored at the start of the next
   // iteration (after that iteration's inputs are staged), so that the wait for
   // the staged loads never waits for fresh stores.
-  f32x4 yo[FULL ? Sh::TPW : 1][4];
-  float yinv[FULL ? Sh::TPW : 1];
+  f32x4 yo[FULL ? TPW : 1][4];
+  float yinv[FULL ? TPW : 1];
   int prev_t0 = -1, prev_nv = 0;
   auto store_prev = [&]() {
     if constexpr (FULL) {
       if (prev_t0 >= 0) {
 #pragma unroll
-        for (int tw = 0; tw < Sh::TPW; ++tw) {
+        for (int tw = 0; tw < TPW; ++tw) {
           const int tok = 16 * (w + NW * tw) + li;
           if (tok < prev_nv) {
             TOUT* orow = o + ((size_t)bh * N + prev_t0 + tok) * kDV + 4 * g;
@@ -379,7 +590,7 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
 
     if constexpr (FULL) {
 #pragma unroll
-      for (int tw = 0; tw < Sh::TPW; ++tw) {
+      for (int tw = 0; tw < TPW; ++tw) {
         const int tt = w + NW * tw;  // token tile, wave-uniform
         const int tok = 16 * tt + li;
 
@@ -445,7 +656,6 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
         }
         // q is staged as q / a: the products y_s z_t already carry 2 alpha_2 = 1 / a^2,
         // y_s carries alpha_1 = 1 / a
-        const float* yy = yv;
         const float kb0f = gh == 0 ? 0.5f : 1.0f;  // diagonal tile: weight 1 instead of 2
         const float cA = g == 0 ? 1.0f : 0.0f, cB = g >= 2 ? 1.0f : 0.0f, cC = g == 1 ? 1.0f : 0.0f;
         constexpr int kD0[4] = {0, 1, 4, 5};
@@ -455,10 +665,10 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
 #pragma unroll
           for (int s = 0; s < 8; ++s) {
             if (kb < 4) {
-              f[s] = yy[s] * zv[(s + kD0[kb]) & 15];
+              f[s] = yv[s] * zv[(s + kD0[kb]) & 15];
               if (kb == 0) f[s] *= kb0f;
             } else {
-              f[s] = cA * yy[s] * zv[(s + 8) & 15] + cB * yv[s] + (s == 0 ? cC : 0.0f);
+              f[s] = cA * yv[s] * zv[(s + 8) & 15] + cB * yv[s] + (s == 0 ? cC : 0.0f);
             }
           }
           const bf16x8 bphi = __builtin_bit_cast(
@@ -506,7 +716,7 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
           if (s == 1 && !HAS_S1) continue;
-          const float* kj = krow_j[s] == kZero ? &L.Kz[0] : &L.K[b][krow_j[s]][0];
+          const float* kj = own.krow_j[s] == kZero ? &L.Kz[0] : &L.K[b][own.krow_j[s]][0];
           const float4 b0 = *reinterpret_cast<const float4*>(kj + t8);
           const float4 b1 = *reinterpret_cast<const float4*>(kj + t8 + 4);
           const float xj[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
@@ -550,35 +760,92 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
       if (j0 + i < nchunks) body(j0 + i, pf[(i + 1) % DEPTH]);
   }
   store_prev();
+}
 
-  // ---- write the state (last segment) or the segment sum, in the caller's layout
-  const bool write = FULL ? (seg == nseg - 1) : true;  // uniform
-  if (write) {
-    // rows of the image: every row is written by exactly one lane group (zero
-    // rows of the internal layout map nowhere)
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      if (s == 1 && !HAS_S1) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float wt;
-        const int row = abi_row(ft_of[s], 4 * g + r, &wt);
-        if (row >= 0) {
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            if (s < 2 || ct < NCT2) img[row * kDV + 16 * (s == 2 ? ctb + ct : ct) + li] = acc[s][ct][r] * wt;
-          if (li == 0 && (s < 2 || own_t2)) img[kD3 * kDV + row] = tacc[s][r] * wt;
-        }
-      }
-    }
+// ---- the kernel -------------------------------------------------------------
+// Grid: BH * nseg workgroups.  sync == nullptr exactly when nseg == 1 (then
+// workgroup b runs sequence b from the caller's state, with no prefix step).
+template <int C, typename TOUT>
+__global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    TOUT* __restrict__ o, float* __restrict__ st_S, float* __restrict__ st_T, int* __restrict__ sync,
+    float* __restrict__ sums, int N, int nseg, int cps, int gs, float inv_a) {
+  // The chunk buffers, and while the final state is stored, a float [153 * 65]
+  // image of it in the caller's layout.
+  __shared__ __align__(16) unsigned char lds_raw[sizeof(Lds<C>) > kAbiImg * 4 ? sizeof(Lds<C>) : kAbiImg * 4];
+  __shared__ int s_ticket;
+  Lds<C>& L = *reinterpret_cast<Lds<C>*>(lds_raw);
+  float* img = reinterpret_cast<float*>(lds_raw);
+
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15;
+  // wave index in a scalar register: every branch around an MFMA is uniform
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  int ticket = blockIdx.x;
+  if (sync != nullptr) {  // uniform
+    if (tid == 0) s_ticket = __hip_atomic_fetch_add(&sync[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
-    const size_t slot = (size_t)bh * dst_slots + (dst_slots == 1 ? 0 : seg);
-    float4* ds4 = reinterpret_cast<float4*>(dst_S + slot * kD3 * kDV);
-    float* dt = dst_T + slot * kD3;
-    for (int i = tid; i < kD3 * kDV / 4; i += NTHREADS)
-      __builtin_nontemporal_store(reinterpret_cast<const f32x4*>(img)[i], reinterpret_cast<f32x4*>(ds4) + i);
-    for (int i = tid; i < kD3; i += NTHREADS) __builtin_nontemporal_store(img[kD3 * kDV + i], dt + i);
+    ticket = __builtin_amdgcn_readfirstlane(s_ticket);
   }
+  const int bh = ticket / nseg, seg = ticket % nseg;
+  const int t_begin = seg * cps * C;
+  const int t_end = min(N, t_begin + cps * C);
+  const Own<C> own(w, li);
+  const size_t head0 = (size_t)bh * nseg;  // slot of segment 0 of this sequence
+  auto flag_of = [&](int j) { return &sync[kHdr + (head0 + j) * kFlagStride]; };
+  auto image_of = [&](int j) { return sums + (head0 + j) * kImgFloats; };
+  const int grp = seg / gs, g0 = grp * gs;
+  // the last member of a group publishes the group's sum, unless no group follows
+  const bool leader = seg == g0 + gs - 1 && seg < nseg - 1;
+
+  // prefix: the caller's state for segment 0 (its loads are in flight during
+  // the first pass), zero elsewhere
+  Acc pre;
+  if (seg == 0) load_caller_state_raw<C>(st_S, st_T, bh, own, pre);
+  else zero_acc(pre);
+  Acc acc;
+  zero_acc(acc);
+  // 1. the segment's own sum (not needed for the last segment)
+  if (seg < nseg - 1) segment_pass<C, false, TOUT>(L, own, acc, q, k, v, o, bh, N, t_begin, t_end, inv_a);
+  if (seg == 0) {
+    unweight_caller_state<C>(own, pre);
+    if (nseg > 1) {  // segment 0's published sum includes the caller's state
+      image_store<C, true>(image_of(0), acc, pre, w, lane);
+      raise_flag(flag_of(0), 1);
+    }
+  } else {
+    if (seg < nseg - 1 && !leader) {
+      image_store<C, false>(image_of(seg), acc, acc, w, lane);
+      raise_flag(flag_of(seg), 1);
+    }
+    // 2. earlier members of the group, then (group sum published) the earlier groups
+    int* err = &sync[1];
+    for (int j = g0; j < seg; ++j)
+      if (wait_flag(flag_of(j), err)) image_add<C>(image_of(j), pre, w, lane);
+    if (leader) {
+      image_store<C, true>(image_of(seg), acc, pre, w, lane);
+      raise_flag(flag_of(seg), 1);
+    }
+    for (int G = 0; G < grp; ++G)
+      if (wait_flag(flag_of(G * gs + gs - 1), err)) image_add<C>(image_of(G * gs + gs - 1), pre, w, lane);
+  }
+  // 3. replay from the prefix
+  segment_pass<C, true, TOUT>(L, own, pre, q, k, v, o, bh, N, t_begin, t_end, inv_a);
+  if (seg == nseg - 1) store_caller_state<C>(img, st_S, st_T, bh, own, pre);
+}
+
+// Clears the ticket counter, the error code and the nslots flags.
+__global__ void clear_flags_kernel(int* sync, int nslots) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < nslots) sync[kHdr + (size_t)i * kFlagStride] = 0;
+  if (i < 2) sync[i] = 0;
+}
+
+// Segments per group: about sqrt(nseg), at least 2.
+inline int group_size(int nseg) {
+  int gs = 2;
+  while (gs * gs < nseg) ++gs;
+  return gs;
 }
 
 template <int C, typename TOUT>
@@ -591,32 +858,33 @@ hipError_t launch(const PrefillArgs& a) {
   const uint16_t* k = static_cast<const uint16_t*>(a.k);
   const uint16_t* v = static_cast<const uint16_t*>(a.v);
   hipEvent_t* ev = a.events;
+  int* sync = nullptr;
+  float* sums = nullptr;
   if (ev) (void)hipEventRecord(ev[0], a.stream);
   if (pl.nseg > 1) {
-    float* W_S = a.workspace;
-    float* W_T = a.workspace + (size_t)a.BH * pl.nseg * kD3 * kDV;
-    hipLaunchKernelGGL((prefill_n3_kernel<C, false, TOUT>), dim3(a.BH * (pl.nseg - 1)), dim3(Shape<C>::NTHREADS), 0, a.stream, q,
-                       k, v, static_cast<TOUT*>(nullptr), (const float*)nullptr, (const float*)nullptr, 1, W_S, W_T,
-                       pl.nseg, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
-    if (ev) (void)hipEventRecord(ev[1], a.stream);
-    if (hipError_t e = launch_segment_scan(st_S, st_T, W_S, W_T, kD3, pl.nseg, a.BH, a.stream)) return e;
-    if (ev) (void)hipEventRecord(ev[2], a.stream);
-    hipLaunchKernelGGL((prefill_n3_kernel<C, true, TOUT>), dim3(a.BH * pl.nseg), dim3(Shape<C>::NTHREADS), 0, a.stream, q, k, v,
-                       static_cast<TOUT*>(a.o), W_S, W_T, pl.nseg, st_S, st_T, 1, a.N, pl.nseg, pl.chunks_per_seg,
-                       inv_a);
-  } else {
-    if (ev) {
-      (void)hipEventRecord(ev[1], a.stream);
-      (void)hipEventRecord(ev[2], a.stream);
-    }
-    hipLaunchKernelGGL((prefill_n3_kernel<C, true, TOUT>), dim3(a.BH), dim3(Shape<C>::NTHREADS), 0, a.stream, q, k, v,
-                       static_cast<TOUT*>(a.o), st_S, st_T, 1, st_S, st_T, 1, a.N, 1, pl.chunks_per_seg, inv_a);
+    const size_t hdr = header_words(a.BH, pl.nseg);
+    sync = reinterpret_cast<int*>(a.workspace);
+    sums = a.workspace + hdr;
+    const int nslots = a.BH * pl.nseg;
+    hipLaunchKernelGGL(clear_flags_kernel, dim3((nslots + 255) / 256), dim3(256), 0, a.stream, sync, nslots);
   }
+  if (ev) {
+    (void)hipEventRecord(ev[1], a.stream);
+    (void)hipEventRecord(ev[2], a.stream);
+  }
+  hipLaunchKernelGGL((prefill_n3_kernel<C, TOUT>), dim3(a.BH * pl.nseg), dim3(Shape<C>::NTHREADS), 0, a.stream, q,
+                     k, v, static_cast<TOUT*>(a.o), st_S, st_T, sync, sums, a.N, pl.nseg, pl.chunks_per_seg,
+                     group_size(pl.nseg), inv_a);
   if (ev) (void)hipEventRecord(ev[3], a.stream);
   return hipGetLastError();
 }
 
 }  // namespace n3
+
+size_t prefill_n3_workspace_floats(int BH, int nseg) {
+  if (nseg <= 1) return 0;
+  return n3::header_words(BH, nseg) + (size_t)BH * nseg * n3::kImgFloats;
+}
 
 hipError_t launch_prefill_n3_bf16(const PrefillArgs& a) {
   switch (a.chunk) {

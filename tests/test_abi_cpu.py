@@ -74,10 +74,18 @@ def test_workspace_sizing(rsp):
     # one segment per head when the heads alone fill the GPU: no workspace
     assert rsp.prefill_workspace_bytes(64, 8, 4096, 3, 64) == 0
     assert rsp.prefill_workspace_bytes(1, 1, 0, 3, 64) == 0
-    ws = rsp.prefill_workspace_bytes(4, 8, 8192, 3, 64)
-    nseg = ws // (4 * 8 * 9945 * 4)
-    assert ws == 4 * 8 * nseg * 9945 * 4 and nseg > 1
+    # n = 2: one [D x 65] float state per segment (segment sums, then prefixes)
+    ws = rsp.prefill_workspace_bytes(4, 8, 8192, 2, 64)
+    nseg = ws // (4 * 8 * 17 * 65 * 4)
+    assert ws == 4 * 8 * nseg * 17 * 65 * 4 and nseg > 1
     assert 4 * 8 * nseg >= 256
+    # n = 3 (single-launch kernel): a header of 64 words plus one 64-word flag
+    # slot per segment, then one state image of 10624 floats per segment
+    nseg = 512 // 32
+    hdr = 64 + 32 * nseg * 64
+    assert rsp.prefill_workspace_bytes(4, 8, 8192, 3, 64) == 4 * (hdr + 32 * nseg * 10624)
+    # which also covers the generic kernel's need (float32 inputs)
+    assert 4 * (hdr + 32 * nseg * 10624) >= 32 * nseg * 153 * 65 * 4
 
 
 def _prefill_rc(lib, **kw):
