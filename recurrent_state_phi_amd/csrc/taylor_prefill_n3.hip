@@ -73,9 +73,7 @@ constexpr int kD3 = 153;   // state rows in the caller's layout
 constexpr int kNF = 160;   // internal feature rows (10 tiles)
 constexpr int kSS = 168;   // row stride (bf16) of the S'^T copy (84 dwords: conflict-free 16-byte reads)
 constexpr int kQS = 36;    // row stride (bf16) of the doubled q copy
-constexpr int kOnes = 16;  // K^T row holding 1 for valid tokens, 0 for padding
-constexpr int kZero = 17;  // index standing for the zero row (stored once, outside the double buffer)
-constexpr int kKTRows = 17;
+constexpr int kKTRows = 16;
 
 // Workspace of a multi-segment call (32-bit words):
 //   [0]                    ticket counter
@@ -127,10 +125,8 @@ template <int C>
 struct Lds {
   alignas(16) uint16_t S[2][64][kSS];             // S'^T copy (bf16), k-slot order, swizzled
   alignas(16) uint16_t T[2][2][kNF];              // T' in k-slot order: bf16 high, low parts
-  alignas(16) uint16_t Tz[kNF];                   // zeros (the other rows of the T operand)
   alignas(16) uint16_t V[2][64][Shape<C>::VS];    // V^T (bf16), swizzled
-  alignas(16) float K[2][kKTRows][Shape<C>::KS];  // K^T (float) + ones row
-  alignas(16) float Kz[Shape<C>::KS];             // zero row
+  alignas(16) float K[2][kKTRows][Shape<C>::KS];  // K^T (float)
   alignas(16) uint16_t Q[2][C][kQS];              // q twice per row: [x | x]
 };
 
@@ -181,11 +177,12 @@ __device__ __forceinline__ int abi_row(int ft, int rho, float* w) {
   return ft == 9 ? 1 + rho : (pair ? quad : (rho == 8 ? 0 : -1));
 }
 
-// K^T rows whose product is internal row rho of tile ft.
-__device__ __forceinline__ int k_row_j(int ft, int rho) {
-  if (ft < 8) return (rho + ft) & 15;
-  if (ft == 8) return rho < 8 ? rho + 8 : (rho == 8 ? kOnes : kZero);
-  return kOnes;
+// Value of v held by lane (l + N) mod 16 of this lane's row of 16 lanes
+// (DPP row rotation: row_ror by 16 - N).
+template <int N>
+__device__ __forceinline__ float from_lane_plus(float v) {
+  static_assert(N > 0 && N < 16, "rotation");
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x120 + (16 - N), 0xF, 0xF, false));
 }
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
@@ -205,8 +202,8 @@ struct Own {
   int ft[3];
   int ctb;
   bool own_t2;
-  bool const_lane;  // lane that builds the constant feature (tile 8, row 8)
-  int krow_j[3];
+  bool tile8;       // slot 2 is tile 8 (else tile 9)
+  int krow0;        // K^T row of the second factor of slot 0: li + w
   __device__ __forceinline__ Own(int w, int li) {
     constexpr int NW = Shape<C>::NW;
     ft[0] = w;
@@ -214,9 +211,8 @@ struct Own {
     ft[2] = 8 + w / (NW / 2);
     ctb = (w % (NW / 2)) * Shape<C>::NCT2;
     own_t2 = (w % (NW / 2)) == 0;
-    const_lane = w / (NW / 2) == 0 && li == 8;
-#pragma unroll
-    for (int s = 0; s < 3; ++s) krow_j[s] = k_row_j(ft[s], li);
+    tile8 = ft[2] == 8;
+    krow0 = (li + w) & 15;
   }
 };
 
@@ -261,9 +257,10 @@ __device__ __forceinline__ void image_store(float* img, const Acc& a, const Acc&
   }
 }
 
-// a += the image at img.
+// This wave's part of the image at img: S' pairs, then T' (lanes li == 0; the
+// other lanes read the start of the image and discard it).
 template <int C>
-__device__ __forceinline__ void image_add(const float* img, Acc& a, int w, int lane) {
+__device__ __forceinline__ void image_load(const float* img, Acc& x, int w, int lane) {
   using Sh = Shape<C>;
   const int li = lane & 15, g = lane >> 4;
   const __amdgpu_buffer_rsrc_t r = image_rsrc(img);
@@ -272,14 +269,25 @@ __device__ __forceinline__ void image_add(const float* img, Acc& a, int w, int l
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
       if (Sh::has(s, ct))
-        a.s[s][ct] += __builtin_bit_cast(
+        x.s[s][ct] = __builtin_bit_cast(
             f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                        r, ((w * Sh::NCTS + Sh::pair_index(s, ct)) * 64 + lane) * 16, 0, kSC1));
-  if (li == 0) {
 #pragma unroll
-    for (int s = 0; s < 3; ++s)
-      a.t[s] += __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (kImgS + ((w * 3 + s) * 4 + g) * 4) * 4, 0, kSC1));
+  for (int s = 0; s < 3; ++s)
+    x.t[s] = __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, li == 0 ? (kImgS + ((w * 3 + s) * 4 + g) * 4) * 4 : 0, 0,
+                                                     kSC1));
+}
+
+template <int C>
+__device__ __forceinline__ void acc_add(Acc& a, const Acc& x, int lane) {
+  using Sh = Shape<C>;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      if (Sh::has(s, ct)) a.s[s][ct] += x.s[s][ct];
+    if ((lane & 15) == 0) a.t[s] += x.t[s];
   }
 }
 
@@ -293,7 +301,8 @@ __device__ __forceinline__ void raise_flag(int* flag, int value) {
 }
 
 // Wait (per wave) until *flag is nonzero and return it; 0 after kSpinLimit
-// polls, with the error recorded.
+// polls, with the error recorded (the caller then reads whatever the image
+// holds: the results are wrong, and the error code says so).
 __device__ __forceinline__ int wait_flag(const int* flag, int* err) {
   for (int i = 0; i < kSpinLimit; ++i) {
     const int v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -399,7 +408,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<C>& own, Acc& 
                                              TOUT* __restrict__ o, int bh, int N, int t_begin, int t_end,
                                              float inv_a) {
   using Sh = Shape<C>;
-  constexpr int NKB = Sh::NKB, NW = Sh::NW, NTHREADS = Sh::NTHREADS, NCT2 = Sh::NCT2;
+  constexpr int NKB = Sh::NKB, NW = Sh::NW, NCT2 = Sh::NCT2;
   constexpr bool HAS_S1 = Sh::HAS_S1;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -408,7 +417,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<C>& own, Acc& 
   f32x4(&acc)[3][4] = a.s;
   f32x4(&tacc)[3] = a.t;
   const int ctb = own.ctb;
-  const bool own_t2 = own.own_t2, const_lane = own.const_lane;
+  const bool own_t2 = own.own_t2;
 
   // ---- global loads.  Wave w loads its own token tile 16w .. 16w + 15:
   //      lane (li, g) takes columns 8g..8g+7 and 32+8g..+7 of v for token li of
@@ -477,12 +486,6 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<C>& own, Acc& 
       // K^T (float): lane (li, g) gets dimension li of tokens 16tt + 4g + r
       const f32x4 dk = mfma_bf16_k32(ka, sel0, zero);
       *reinterpret_cast<f32x4*>(&L.K[b][li][16 * tt + 4 * g]) = dk;
-      if (li == 0) {
-        const int t0r = 16 * tt + 4 * g;
-        *reinterpret_cast<f32x4*>(&L.K[b][kOnes][t0r]) =
-            f32x4{t0r < nv ? 1.0f : 0.0f, t0r + 1 < nv ? 1.0f : 0.0f, t0r + 2 < nv ? 1.0f : 0.0f,
-                  t0r + 3 < nv ? 1.0f : 0.0f};
-      }
       if constexpr (FULL) {
         if (g >= 2) {
           // q / a, rounded to bfloat16 (exact for a = 1): then q.k comes out
@@ -530,10 +533,6 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<C>& own, Acc& 
     }
   };
 
-  // zero rows of K^T and of the T operand (never overwritten)
-  for (int i = tid; i < C; i += NTHREADS) L.Kz[i] = 0.0f;
-  if constexpr (FULL)
-    for (int i = tid; i < kNF; i += NTHREADS) L.Tz[i] = 0;
   // chunk c lives in register set c % DEPTH; chunks 1..DEPTH are in flight
   // when the loop starts, and body(j) refills the set it stages from with
   // chunk j + 1 + DEPTH
@@ -549,18 +548,19 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<C>& own, Acc& 
   // Outputs of the chunk computed last, stored at the start of the next
   // iteration (after that iteration's inputs are staged), so that the wait for
   // the staged loads never waits for fresh stores.
-  f32x4 yo[FULL ? TPW : 1][4];
-  float yinv[FULL ? TPW : 1];
+  f32x4 yo[FULL ? TPW : 1][5];
   int prev_t0 = -1, prev_nv = 0;
   auto store_prev = [&]() {
     if constexpr (FULL) {
-      if (prev_t0 >= 0) {
+      if (prev_t0 >= 0) {  // uniform
 #pragma unroll
         for (int tw = 0; tw < TPW; ++tw) {
+          // o = Y[:d_v] / Y[d_v]: the normaliser of token li sits in rows 0 and 1
+          // of column tile 4 (lanes 0..15); every lane takes part in the shuffle
+          const float inv = 1.0f / __shfl(yo[tw][4][0] + yo[tw][4][1], li);
           const int tok = 16 * (w + NW * tw) + li;
           if (tok < prev_nv) {
             TOUT* orow = o + ((size_t)bh * N + prev_t0 + tok) * kDV + 4 * g;
-            const float inv = yinv[tw];
             // non-temporal: the outputs are not read again by this kernel
             if constexpr (std::is_same_v<TOUT, float>) {
 #pragma unroll
@@ -587,6 +587,88 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<C>& own, Acc& 
     if (j + 1 < nchunks) stage(pfs, b ^ 1, min(C, t_end - (t0 + C)));
     issue_loads(pfs, j + 1 + DEPTH);
     store_prev();
+
+    // The update comes first: the state read below only uses the previous
+    // chunk's copy of the state, and by the time this chunk's copy is
+    // published the update's products have long completed.
+    // ---- state update: S' += phi(K)^T V on the owned feature tiles, T' += phi(K)^T 1
+    //      Lane li holds row li of K^T (x_li) and row li + w (the second factor
+    //      of tile w); the second factors of the other tiles are those rows as
+    //      held by other lanes of the same 16-lane row (DPP rotations), so only
+    //      two rows come from LDS.  Padding tokens have k = 0 and v = 0, so
+    //      every product with x, and every product with v, vanishes for them;
+    //      the constant feature is 1 for every token of the chunk, and its T'
+    //      entry is corrected by the number of padding tokens.
+    {
+      const uint32_t one2 = li == 0 ? 0x3F803F80u : 0u;
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
+      const float pair_m = li < 8 ? 1.0f : 0.0f, const_m = li == 8 ? 1.0f : 0.0f;  // rows of tile 8
+      const bool tile8 = own.tile8;  // wave-uniform
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int t8 = 32 * kb + 8 * g;
+        float xi[8], xa[8];
+        {
+          const float4 a0 = *reinterpret_cast<const float4*>(&L.K[b][li][t8]);
+          const float4 a1 = *reinterpret_cast<const float4*>(&L.K[b][li][t8 + 4]);
+          xi[0] = a0.x; xi[1] = a0.y; xi[2] = a0.z; xi[3] = a0.w;
+          xi[4] = a1.x; xi[5] = a1.y; xi[6] = a1.z; xi[7] = a1.w;
+          const float4 c0 = *reinterpret_cast<const float4*>(&L.K[b][own.krow0][t8]);
+          const float4 c1 = *reinterpret_cast<const float4*>(&L.K[b][own.krow0][t8 + 4]);
+          xa[0] = c0.x; xa[1] = c0.y; xa[2] = c0.z; xa[3] = c0.w;
+          xa[4] = c1.x; xa[5] = c1.y; xa[6] = c1.z; xa[7] = c1.w;
+        }
+        bf16x8 vb[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const int c = 16 * ct + li;
+          vb[ct] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&L.V[b][c][swz(c, t8)]));
+        }
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+          if (s == 1 && !HAS_S1) continue;
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            if (s == 0) {
+              f[e] = xi[e] * xa[e];                       // tile w: x_li x_(li+w)
+            } else if (s == 1) {
+              f[e] = xi[e] * from_lane_plus<4>(xa[e]);    // tile w + 4: x_li x_(li+w+4)
+            } else {
+              // tile 8: x_li x_(li+8) (li < 8), the constant (li == 8), zero rows;
+              // tile 9: x_li.  (A uniform branch: a DPP rotation reads its
+              // source from the other lanes, which must all be executing.)
+              if (tile8) f[e] = fmaf(xi[e] * from_lane_plus<8>(xi[e]), pair_m, const_m);
+              else f[e] = xi[e];
+            }
+          }
+          const bf16x8 aphi = __builtin_bit_cast(
+              bf16x8, make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])));
+          if (s < 2) {
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) acc[s][ct] = mfma_bf16_k32(aphi, vb[ct], acc[s][ct]);
+            tacc[s] = mfma_bf16_k32(aphi, ones, tacc[s]);
+          } else {
+            if (own_t2) tacc[2] = mfma_bf16_k32(aphi, ones, tacc[2]);
+            // column tiles ctb .. ctb + NCT2 - 1 (ctb is wave-uniform)
+            if constexpr (NCT2 == 2) {
+              if (ctb == 0) {
+                acc[2][0] = mfma_bf16_k32(aphi, vb[0], acc[2][0]);
+                acc[2][1] = mfma_bf16_k32(aphi, vb[1], acc[2][1]);
+              } else {
+                acc[2][0] = mfma_bf16_k32(aphi, vb[2], acc[2][0]);
+                acc[2][1] = mfma_bf16_k32(aphi, vb[3], acc[2][1]);
+              }
+            } else {
+              if (ctb == 0) acc[2][0] = mfma_bf16_k32(aphi, vb[0], acc[2][0]);
+              else if (ctb == 1) acc[2][0] = mfma_bf16_k32(aphi, vb[1], acc[2][0]);
+              else if (ctb == 2) acc[2][0] = mfma_bf16_k32(aphi, vb[2], acc[2][0]);
+              else acc[2][0] = mfma_bf16_k32(aphi, vb[3], acc[2][0]);
+            }
+          }
+        }
+      }
+    }
 
     if constexpr (FULL) {
 #pragma unroll
@@ -678,78 +760,25 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<C>& own, Acc& 
             const uint4 a4 = *reinterpret_cast<const uint4*>(&L.S[b][16 * ct + li][32 * kb + 8 * g]);
             y[ct] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a4), bphi, y[ct]);
           }
-          // normaliser: rows 0 / 1 of column tile 4 are T' (high / low bfloat16 parts)
-          const uint16_t* trow = li < 2 ? &L.T[b][li][0] : &L.Tz[0];
-          const uint4 tA = *reinterpret_cast<const uint4*>(trow + 32 * kb + 8 * g);
+          // normaliser: rows 0 / 1 of column tile 4 are T' (high / low bfloat16
+          // parts); rows 2..15 repeat them and are never read (so every lane
+          // reads one of two words per lane group: a broadcast)
+          const uint4 tA = *reinterpret_cast<const uint4*>(&L.T[b][li & 1][32 * kb + 8 * g]);
           y[4] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, tA), bphi, y[4]);
         }
 
-        // ---- epilogue: o = Y[:d_v] / Y[d_v], stored at the start of the next iteration
-        yinv[tw] = 1.0f / __shfl(y[4][0] + y[4][1], li);
+        // ---- epilogue (normalised and stored at the start of the next iteration,
+        //      when the products have long completed)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) yo[tw][ct] = y[ct];
+        for (int ct = 0; ct < 5; ++ct) yo[tw][ct] = y[ct];
       }
       prev_t0 = t0;
       prev_nv = nv;
     }
 
-    // ---- state update: S' += phi(K)^T V on the owned feature tiles, T' += phi(K)^T 1
-    {
-      const uint32_t one2 = li == 0 ? 0x3F803F80u : 0u;
-      const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int t8 = 32 * kb + 8 * g;
-        float xi[8];
-        {
-          const float4 a0 = *reinterpret_cast<const float4*>(&L.K[b][li][t8]);
-          const float4 a1 = *reinterpret_cast<const float4*>(&L.K[b][li][t8 + 4]);
-          xi[0] = a0.x; xi[1] = a0.y; xi[2] = a0.z; xi[3] = a0.w;
-          xi[4] = a1.x; xi[5] = a1.y; xi[6] = a1.z; xi[7] = a1.w;
-        }
-        bf16x8 vb[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const int c = 16 * ct + li;
-          vb[ct] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(&L.V[b][c][swz(c, t8)]));
-        }
-#pragma unroll
-        for (int s = 0; s < 3; ++s) {
-          if (s == 1 && !HAS_S1) continue;
-          const float* kj = own.krow_j[s] == kZero ? &L.Kz[0] : &L.K[b][own.krow_j[s]][0];
-          const float4 b0 = *reinterpret_cast<const float4*>(kj + t8);
-          const float4 b1 = *reinterpret_cast<const float4*>(kj + t8 + 4);
-          const float xj[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-          float f[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = (s == 2 && const_lane ? 1.0f : xi[e]) * xj[e];
-          const bf16x8 aphi = __builtin_bit_cast(
-              bf16x8, make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])));
-          if (s < 2) {
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) acc[s][ct] = mfma_bf16_k32(aphi, vb[ct], acc[s][ct]);
-            tacc[s] = mfma_bf16_k32(aphi, ones, tacc[s]);
-          } else {
-            if (own_t2) tacc[2] = mfma_bf16_k32(aphi, ones, tacc[2]);
-            // column tiles ctb .. ctb + NCT2 - 1 (ctb is wave-uniform)
-            if constexpr (NCT2 == 2) {
-              if (ctb == 0) {
-                acc[2][0] = mfma_bf16_k32(aphi, vb[0], acc[2][0]);
-                acc[2][1] = mfma_bf16_k32(aphi, vb[1], acc[2][1]);
-              } else {
-                acc[2][0] = mfma_bf16_k32(aphi, vb[2], acc[2][0]);
-                acc[2][1] = mfma_bf16_k32(aphi, vb[3], acc[2][1]);
-              }
-            } else {
-              if (ctb == 0) acc[2][0] = mfma_bf16_k32(aphi, vb[0], acc[2][0]);
-              else if (ctb == 1) acc[2][0] = mfma_bf16_k32(aphi, vb[1], acc[2][0]);
-              else if (ctb == 2) acc[2][0] = mfma_bf16_k32(aphi, vb[2], acc[2][0]);
-              else acc[2][0] = mfma_bf16_k32(aphi, vb[3], acc[2][0]);
-            }
-          }
-        }
-      }
-    }
+    // the constant feature counted the padding tokens of a partial chunk:
+    // take them out of its T' entry (row 8 of tile 8: lane 32, element 0)
+    tacc[2][0] -= (own.tile8 && own_t2 && lane == 32) ? (float)(C - nv) : 0.0f;
 
     if (j + 1 < nchunks) publish(b ^ 1);
     __syncthreads();
@@ -798,36 +827,55 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
   // the last member of a group publishes the group's sum, unless no group follows
   const bool leader = seg == g0 + gs - 1 && seg < nseg - 1;
 
-  // prefix: the caller's state for segment 0 (its loads are in flight during
-  // the first pass), zero elsewhere
+  // Every segment's prefix starts from the caller's state; its loads are
+  // issued first and stay in flight during the first pass.
   Acc pre;
-  if (seg == 0) load_caller_state_raw<C>(st_S, st_T, bh, own, pre);
-  else zero_acc(pre);
+  load_caller_state_raw<C>(st_S, st_T, bh, own, pre);
   Acc acc;
   zero_acc(acc);
   // 1. the segment's own sum (not needed for the last segment)
   if (seg < nseg - 1) segment_pass<C, false, TOUT>(L, own, acc, q, k, v, o, bh, N, t_begin, t_end, inv_a);
-  if (seg == 0) {
-    unweight_caller_state<C>(own, pre);
-    if (nseg > 1) {  // segment 0's published sum includes the caller's state
-      image_store<C, true>(image_of(0), acc, pre, w, lane);
-      raise_flag(flag_of(0), 1);
-    }
-  } else {
-    if (seg < nseg - 1 && !leader) {
+  unweight_caller_state<C>(own, pre);
+  // 2. prefix = caller's state + sums of the earlier members of the group +
+  //    group sums of the earlier groups (the leader adds the members' sums to
+  //    its own as well, and publishes that as the group sum)
+  if (nseg > 1) {  // uniform
+    int* err = &sync[1];
+    const int r = seg - g0;  // earlier members
+    auto source = [&](int i) { return i < r ? g0 + i : (i - r) * gs + gs - 1; };
+    if (leader) {
+      Acc x;
+      for (int j = g0; j < seg; ++j) {
+        wait_flag(flag_of(j), err);
+        image_load<C>(image_of(j), x, w, lane);
+        acc_add<C>(pre, x, lane);
+        acc_add<C>(acc, x, lane);
+      }
       image_store<C, false>(image_of(seg), acc, acc, w, lane);
       raise_flag(flag_of(seg), 1);
+      for (int G = 0; G < grp; ++G) {
+        wait_flag(flag_of(G * gs + gs - 1), err);
+        image_load<C>(image_of(G * gs + gs - 1), x, w, lane);
+        acc_add<C>(pre, x, lane);
+      }
+    } else {
+      if (seg < nseg - 1) {
+        image_store<C, false>(image_of(seg), acc, acc, w, lane);
+        raise_flag(flag_of(seg), 1);
+      }
+      // two images in flight at a time
+      const int n = r + grp;
+      for (int i = 0; i < n; i += 2) {
+        const bool two = i + 1 < n;  // uniform
+        Acc x, y;
+        wait_flag(flag_of(source(i)), err);
+        if (two) wait_flag(flag_of(source(i + 1)), err);
+        image_load<C>(image_of(source(i)), x, w, lane);
+        image_load<C>(image_of(two ? source(i + 1) : source(i)), y, w, lane);
+        acc_add<C>(pre, x, lane);
+        if (two) acc_add<C>(pre, y, lane);
+      }
     }
-    // 2. earlier members of the group, then (group sum published) the earlier groups
-    int* err = &sync[1];
-    for (int j = g0; j < seg; ++j)
-      if (wait_flag(flag_of(j), err)) image_add<C>(image_of(j), pre, w, lane);
-    if (leader) {
-      image_store<C, true>(image_of(seg), acc, pre, w, lane);
-      raise_flag(flag_of(seg), 1);
-    }
-    for (int G = 0; G < grp; ++G)
-      if (wait_flag(flag_of(G * gs + gs - 1), err)) image_add<C>(image_of(G * gs + gs - 1), pre, w, lane);
   }
   // 3. replay from the prefix
   segment_pass<C, true, TOUT>(L, own, pre, q, k, v, o, bh, N, t_begin, t_end, inv_a);
