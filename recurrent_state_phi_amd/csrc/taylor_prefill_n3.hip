@@ -99,15 +99,11 @@ __host__ __device__ constexpr size_t header_words(int BH, int nseg) {
   return kHdr + (size_t)BH * nseg * kFlagStride;
 }
 
-template <int C>
-struct Shape {
-  static constexpr int NW = C == 128 ? 8 : 4;  // waves per workgroup
+// Waves of a workgroup: 4 for 64-token chunks, 8 for 128-token chunks.
+template <int NW_>
+struct Waves {
+  static constexpr int NW = NW_;
   static constexpr int NTHREADS = 64 * NW;
-  static constexpr int NTT = C / 16;    // 16-token tiles per chunk
-  static constexpr int NKB = C / 32;    // 32-token k blocks per chunk
-  static constexpr int TPW = NTT / NW;  // token tiles per wave (1)
-  static constexpr int VS = C + 8;      // V^T row stride (bf16)
-  static constexpr int KS = C + 4;      // K^T row stride (float)
   // feature-tile ownership (see Own)
   static constexpr bool HAS_S1 = NW == 4;
   static constexpr int NCT2 = NW == 4 ? 2 : 1;          // column tiles of slot 2
@@ -121,13 +117,27 @@ struct Shape {
   }
 };
 
-template <int C>
+// Chunk geometry of one pass (the segment-sum pass runs twice as many tokens
+// per step as the replay).
+template <int C, int NW>
+struct Shape : Waves<NW> {
+  static constexpr int NTT = C / 16;    // 16-token tiles per chunk
+  static constexpr int NKB = C / 32;    // 32-token k blocks per chunk
+  static constexpr int TPW = NTT / NW;  // token tiles per wave
+  static constexpr int VS = C + 8;      // V^T row stride (bf16)
+  static constexpr int KS = C + 4;      // K^T row stride (float)
+  static_assert(TPW * NW == NTT, "token tiles per wave");
+};
+
+// LDS of one pass; the segment-sum pass (FULL = false) needs no state copy and
+// no q.
+template <int C, bool FULL>
 struct Lds {
-  alignas(16) uint16_t S[2][64][kSS];             // S'^T copy (bf16), k-slot order, swizzled
-  alignas(16) uint16_t T[2][2][kNF];              // T' in k-slot order: bf16 high, low parts
-  alignas(16) uint16_t V[2][64][Shape<C>::VS];    // V^T (bf16), swizzled
-  alignas(16) float K[2][kKTRows][Shape<C>::KS];  // K^T (float)
-  alignas(16) uint16_t Q[2][C][kQS];              // q twice per row: [x | x]
+  alignas(16) uint16_t S[FULL ? 2 : 1][FULL ? 64 : 1][kSS];  // S'^T copy (bf16), k-slot order, swizzled
+  alignas(16) uint16_t T[FULL ? 2 : 1][2][kNF];              // T' in k-slot order: bf16 high, low parts
+  alignas(16) uint16_t V[2][64][C + 8];                      // V^T (bf16), swizzled
+  alignas(16) float K[2][kKTRows][C + 4];                    // K^T (float)
+  alignas(16) uint16_t Q[FULL ? 2 : 1][FULL ? C : 1][kQS];   // q twice per row: [x | x]
 };
 
 // The state of a workgroup in registers: 16x16 accumulator tiles of the owned
@@ -197,7 +207,7 @@ __device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0
 // ctb, ctb + 1).  8 waves: slot 0 = tile w (4 column tiles), no slot 1, slot 2
 // = tile 8 + w/4 (column tile ctb = w % 4).  T' of a slot-2 tile belongs to the
 // first of the waves sharing it.
-template <int C>
+template <int NW>
 struct Own {
   int ft[3];
   int ctb;
@@ -205,11 +215,10 @@ struct Own {
   bool tile8;       // slot 2 is tile 8 (else tile 9)
   int krow0;        // K^T row of the second factor of slot 0: li + w
   __device__ __forceinline__ Own(int w, int li) {
-    constexpr int NW = Shape<C>::NW;
     ft[0] = w;
     ft[1] = w + 4;
     ft[2] = 8 + w / (NW / 2);
-    ctb = (w % (NW / 2)) * Shape<C>::NCT2;
+    ctb = (w % (NW / 2)) * Waves<NW>::NCT2;
     own_t2 = (w % (NW / 2)) == 0;
     tile8 = ft[2] == 8;
     krow0 = (li + w) & 15;
@@ -233,9 +242,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t image_rsrc(const float* img) {
 }
 
 // Writes a (ADD = false) or a + b (ADD = true).
-template <int C, bool ADD>
+template <int NW, bool ADD>
 __device__ __forceinline__ void image_store(float* img, const Acc& a, const Acc& b, int w, int lane) {
-  using Sh = Shape<C>;
+  using Sh = Waves<NW>;
   const int li = lane & 15, g = lane >> 4;
   const __amdgpu_buffer_rsrc_t r = image_rsrc(img);
 #pragma unroll
@@ -259,9 +268,9 @@ __device__ __forceinline__ void image_store(float* img, const Acc& a, const Acc&
 
 // This wave's part of the image at img: S' pairs, then T' (lanes li == 0; the
 // other lanes read the start of the image and discard it).
-template <int C>
+template <int NW>
 __device__ __forceinline__ void image_load(const float* img, Acc& x, int w, int lane) {
-  using Sh = Shape<C>;
+  using Sh = Waves<NW>;
   const int li = lane & 15, g = lane >> 4;
   const __amdgpu_buffer_rsrc_t r = image_rsrc(img);
 #pragma unroll
@@ -279,9 +288,9 @@ __device__ __forceinline__ void image_load(const float* img, Acc& x, int w, int 
                                                      kSC1));
 }
 
-template <int C>
+template <int NW>
 __device__ __forceinline__ void acc_add(Acc& a, const Acc& x, int lane) {
-  using Sh = Shape<C>;
+  using Sh = Waves<NW>;
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
 #pragma unroll
@@ -324,10 +333,10 @@ constexpr int kAbiImg = kD3 * (kDV + 1);
 // The caller's state straight into registers (no LDS, no barrier, so the loads
 // can stay in flight during the first pass): raw values first, then the
 // sqrt-multinomial weights divided out once they are needed.
-template <int C>
-__device__ __forceinline__ void load_caller_state_raw(const float* st_S, const float* st_T, int bh, const Own<C>& own,
+template <int NW>
+__device__ __forceinline__ void load_caller_state_raw(const float* st_S, const float* st_T, int bh, const Own<NW>& own,
                                                       Acc& a) {
-  using Sh = Shape<C>;
+  using Sh = Waves<NW>;
   const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
   const float* S = st_S + (size_t)bh * kD3 * kDV;
   const float* T = st_T + (size_t)bh * kD3;
@@ -347,9 +356,9 @@ __device__ __forceinline__ void load_caller_state_raw(const float* st_S, const f
   }
 }
 
-template <int C>
-__device__ __forceinline__ void unweight_caller_state(const Own<C>& own, Acc& a) {
-  using Sh = Shape<C>;
+template <int NW>
+__device__ __forceinline__ void unweight_caller_state(const Own<NW>& own, Acc& a) {
+  using Sh = Waves<NW>;
   const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int s = 0; s < 3; ++s) {
@@ -369,10 +378,10 @@ __device__ __forceinline__ void unweight_caller_state(const Own<C>& own, Acc& a)
 
 // Stored through LDS as a float image, so that the global stores are full
 // 16-byte accesses.
-template <int C>
-__device__ __forceinline__ void store_caller_state(float* img, float* st_S, float* st_T, int bh, const Own<C>& own,
+template <int NW>
+__device__ __forceinline__ void store_caller_state(float* img, float* st_S, float* st_T, int bh, const Own<NW>& own,
                                                    const Acc& a) {
-  using Sh = Shape<C>;
+  using Sh = Waves<NW>;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   // every row of the image is written by exactly one lane group (zero rows of
   // the internal layout map nowhere)
@@ -402,12 +411,12 @@ __device__ __forceinline__ void store_caller_state(float* img, float* st_S, floa
 // ---- one pass over the chunks [t_begin, t_end) of sequence bh --------------
 // FULL = false: state update only (a += the segment's sum).
 // FULL = true: outputs of every token and the state update.
-template <int C, bool FULL, typename TOUT>
-__device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<C>& own, Acc& a, const uint16_t* __restrict__ q,
+template <int C, int NW_, bool FULL, typename TOUT>
+__device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& own, Acc& a, const uint16_t* __restrict__ q,
                                              const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                              TOUT* __restrict__ o, int bh, int N, int t_begin, int t_end,
                                              float inv_a) {
-  using Sh = Shape<C>;
+  using Sh = Shape<C, NW_>;
   constexpr int NKB = Sh::NKB, NW = Sh::NW, NCT2 = Sh::NCT2;
   constexpr bool HAS_S1 = Sh::HAS_S1;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
@@ -430,7 +439,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<C>& own, Acc& 
   //      flight is the same on every path and the waits for them are exact.
   constexpr int TPW = Sh::TPW;
   constexpr int NPF = 3 * TPW;
-  constexpr int DEPTH = (FULL || C > 64) ? 2 : 4;
+  constexpr int DEPTH = (FULL || C > 64) ? 2 : 4;  // register sets of prefetched loads
   uint4 pf[DEPTH][NPF];
   auto issue_loads = [&](uint4 (&pfs)[NPF], int chunk) {
     const int c0 = t_begin + min(chunk, nchunks - 1) * C;
@@ -794,16 +803,26 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<C>& own, Acc& 
 // ---- the kernel -------------------------------------------------------------
 // Grid: BH * nseg workgroups.  sync == nullptr exactly when nseg == 1 (then
 // workgroup b runs sequence b from the caller's state, with no prefix step).
+template <int C>
+constexpr int waves_for() { return C == 128 ? 8 : 4; }
+
 template <int C, typename TOUT>
-__global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill_n3_kernel(
+__global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefill_n3_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     TOUT* __restrict__ o, float* __restrict__ st_S, float* __restrict__ st_T, int* __restrict__ sync,
     float* __restrict__ sums, int N, int nseg, int cps, int gs, float inv_a) {
-  // The chunk buffers, and while the final state is stored, a float [153 * 65]
-  // image of it in the caller's layout.
-  __shared__ __align__(16) unsigned char lds_raw[sizeof(Lds<C>) > kAbiImg * 4 ? sizeof(Lds<C>) : kAbiImg * 4];
+  constexpr int NW = waves_for<C>();
+  // The segment-sum pass steps over 2C tokens at a time (half the barriers and
+  // twice the independent work per step; it needs no state copy and no q).
+  constexpr int CA = 2 * C;
+  using LA = Lds<CA, false>;
+  using LB = Lds<C, true>;
+  // The chunk buffers of either pass, and while the final state is stored, a
+  // float [153 * 65] image of it in the caller's layout.
+  constexpr size_t kLdsBytes = sizeof(LB) > sizeof(LA) ? (sizeof(LB) > kAbiImg * 4 ? sizeof(LB) : kAbiImg * 4)
+                                                        : (sizeof(LA) > kAbiImg * 4 ? sizeof(LA) : kAbiImg * 4);
+  __shared__ __align__(16) unsigned char lds_raw[kLdsBytes];
   __shared__ int s_ticket;
-  Lds<C>& L = *reinterpret_cast<Lds<C>*>(lds_raw);
   float* img = reinterpret_cast<float*>(lds_raw);
 
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15;
@@ -819,7 +838,7 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
   const int bh = ticket / nseg, seg = ticket % nseg;
   const int t_begin = seg * cps * C;
   const int t_end = min(N, t_begin + cps * C);
-  const Own<C> own(w, li);
+  const Own<NW> own(w, li);
   const size_t head0 = (size_t)bh * nseg;  // slot of segment 0 of this sequence
   auto flag_of = [&](int j) { return &sync[kHdr + (head0 + j) * kFlagStride]; };
   auto image_of = [&](int j) { return sums + (head0 + j) * kImgFloats; };
@@ -830,12 +849,14 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
   // Every segment's prefix starts from the caller's state; its loads are
   // issued first and stay in flight during the first pass.
   Acc pre;
-  load_caller_state_raw<C>(st_S, st_T, bh, own, pre);
+  load_caller_state_raw<NW>(st_S, st_T, bh, own, pre);
   Acc acc;
   zero_acc(acc);
   // 1. the segment's own sum (not needed for the last segment)
-  if (seg < nseg - 1) segment_pass<C, false, TOUT>(L, own, acc, q, k, v, o, bh, N, t_begin, t_end, inv_a);
-  unweight_caller_state<C>(own, pre);
+  if (seg < nseg - 1)
+    segment_pass<CA, NW, false, TOUT>(*reinterpret_cast<LA*>(lds_raw), own, acc, q, k, v, o, bh, N, t_begin, t_end,
+                                      inv_a);
+  unweight_caller_state<NW>(own, pre);
   // 2. prefix = caller's state + sums of the earlier members of the group +
   //    group sums of the earlier groups (the leader adds the members' sums to
   //    its own as well, and publishes that as the group sum)
@@ -847,20 +868,20 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
       Acc x;
       for (int j = g0; j < seg; ++j) {
         wait_flag(flag_of(j), err);
-        image_load<C>(image_of(j), x, w, lane);
-        acc_add<C>(pre, x, lane);
-        acc_add<C>(acc, x, lane);
+        image_load<NW>(image_of(j), x, w, lane);
+        acc_add<NW>(pre, x, lane);
+        acc_add<NW>(acc, x, lane);
       }
-      image_store<C, false>(image_of(seg), acc, acc, w, lane);
+      image_store<NW, false>(image_of(seg), acc, acc, w, lane);
       raise_flag(flag_of(seg), 1);
       for (int G = 0; G < grp; ++G) {
         wait_flag(flag_of(G * gs + gs - 1), err);
-        image_load<C>(image_of(G * gs + gs - 1), x, w, lane);
-        acc_add<C>(pre, x, lane);
+        image_load<NW>(image_of(G * gs + gs - 1), x, w, lane);
+        acc_add<NW>(pre, x, lane);
       }
     } else {
       if (seg < nseg - 1) {
-        image_store<C, false>(image_of(seg), acc, acc, w, lane);
+        image_store<NW, false>(image_of(seg), acc, acc, w, lane);
         raise_flag(flag_of(seg), 1);
       }
       // two images in flight at a time
@@ -870,16 +891,16 @@ __global__ __launch_bounds__(Shape<C>::NTHREADS, (C == 64 ? 2 : 1)) void prefill
         Acc x, y;
         wait_flag(flag_of(source(i)), err);
         if (two) wait_flag(flag_of(source(i + 1)), err);
-        image_load<C>(image_of(source(i)), x, w, lane);
-        image_load<C>(image_of(two ? source(i + 1) : source(i)), y, w, lane);
-        acc_add<C>(pre, x, lane);
-        if (two) acc_add<C>(pre, y, lane);
+        image_load<NW>(image_of(source(i)), x, w, lane);
+        image_load<NW>(image_of(two ? source(i + 1) : source(i)), y, w, lane);
+        acc_add<NW>(pre, x, lane);
+        if (two) acc_add<NW>(pre, y, lane);
       }
     }
   }
   // 3. replay from the prefix
-  segment_pass<C, true, TOUT>(L, own, pre, q, k, v, o, bh, N, t_begin, t_end, inv_a);
-  if (seg == nseg - 1) store_caller_state<C>(img, st_S, st_T, bh, own, pre);
+  segment_pass<C, NW, true, TOUT>(*reinterpret_cast<LB*>(lds_raw), own, pre, q, k, v, o, bh, N, t_begin, t_end, inv_a);
+  if (seg == nseg - 1) store_caller_state<NW>(img, st_S, st_T, bh, own, pre);
 }
 
 // Clears the ticket counter, the error code and the nslots flags.
@@ -920,7 +941,7 @@ hipError_t launch(const PrefillArgs& a) {
     (void)hipEventRecord(ev[1], a.stream);
     (void)hipEventRecord(ev[2], a.stream);
   }
-  hipLaunchKernelGGL((prefill_n3_kernel<C, TOUT>), dim3(a.BH * pl.nseg), dim3(Shape<C>::NTHREADS), 0, a.stream, q,
+  hipLaunchKernelGGL((prefill_n3_kernel<C, TOUT>), dim3(a.BH * pl.nseg), dim3(64 * waves_for<C>()), 0, a.stream, q,
                      k, v, static_cast<TOUT*>(a.o), st_S, st_T, sync, sums, a.N, pl.nseg, pl.chunks_per_seg,
                      group_size(pl.nseg), inv_a);
   if (ev) (void)hipEventRecord(ev[3], a.stream);
