@@ -580,7 +580,9 @@ PrefillPlan plan_prefill(int BH, int N, int n, int chunk) {
   // segment is split into 6 feature blocks, one workgroup each.
   const int blocks = n == 4 ? 6 : 1;
   const int target = chunk >= 128 ? 256 : 512;
-  int nseg = (target + BH * blocks - 1) / (BH * blocks);
+  // n = 4: at most one round of workgroups (a second, partial round would
+  // cost as much as the first)
+  int nseg = n == 4 ? target / (BH * blocks) : (target + BH * blocks - 1) / (BH * blocks);
   if (nseg < 1) nseg = 1;
   if (nseg > p.nchunks) nseg = p.nchunks;
   p.chunks_per_seg = (p.nchunks + nseg - 1) / nseg;

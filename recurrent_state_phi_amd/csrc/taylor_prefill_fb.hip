@@ -58,7 +58,7 @@ template <typename IT> __device__ __forceinline__ float ld(const IT* p, size_t i
 __device__ __forceinline__ float poly4(float y) { return 1.0f + y * (1.0f + y * (0.5f + y * (1.0f / 6.0f))); }
 
 template <int C, bool FULL, typename IT>
-__global__ __launch_bounds__(256) void prefill_fb_kernel(const IT* __restrict__ q, const IT* __restrict__ k,
+__global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const IT* __restrict__ q, const IT* __restrict__ k,
                                                          const IT* __restrict__ v, float* __restrict__ Yp,
                                                          const float* __restrict__ pre_S,
                                                          const float* __restrict__ pre_T, int pre_slots,
