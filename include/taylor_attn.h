@@ -35,12 +35,15 @@
  * - No normalisation of q or k happens inside; the division by the normaliser
  *   has no epsilon and no clamp.
  * - Ownership: the caller owns every buffer.  The library never allocates
- *   device memory and never synchronises; all work is enqueued on `stream`
+ *   device memory and never synchronises (taylor_prefill_check aside, which
+ *   exists to wait for a result); all work is enqueued on `stream`
  *   (0 = the null stream).  Calls are thread-safe; the error string is
  *   thread-local.
  * - Errors: TAYLOR_EINVAL (bad pointer or size, nothing launched),
  *   TAYLOR_EUNSUPPORTED (shape or option not built, nothing launched),
- *   TAYLOR_EHIP (a HIP call failed; the message names it).
+ *   TAYLOR_EHIP (a HIP call failed; the message names it),
+ *   TAYLOR_ETIMEOUT (from taylor_prefill_check only: a bounded wait between
+ *   workgroups ran out).
  *   taylor_last_error() describes the last failure on the calling thread.
  */
 #ifndef TAYLOR_ATTN_H
@@ -62,7 +65,8 @@ enum {
     TAYLOR_OK = 0,
     TAYLOR_EINVAL = -1,
     TAYLOR_EUNSUPPORTED = -2,
-    TAYLOR_EHIP = -3
+    TAYLOR_EHIP = -3,
+    TAYLOR_ETIMEOUT = -4
 };
 
 /* D = sum_{m<n} C(d+m-1, m): rows of the stacked state (section 3.4; Eq. (6)
@@ -100,7 +104,12 @@ size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n
  *   workspace then also holds each block's share of the outputs.
  *   workspace : device, at least taylor_prefill_workspace_bytes(...) bytes
  *   (may be NULL when that is 0); it is scratch, its contents are undefined
- *   afterwards.  o must not alias q, k, v or state. */
+ *   afterwards (any contents are fine on entry).  o must not alias q, k, v or
+ *   state.
+ *   n = 3 with bfloat16 inputs (chunk 64 or 128) runs as one kernel in which
+ *   the workgroups of a sequence's segments pass their state sums to each
+ *   other through the workspace; every such wait is bounded, and
+ *   taylor_prefill_check reports whether one ran out. */
 int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, float* state,
                         int B, int H, int N, int d, int d_v, int n, float a, int chunk,
                         taylor_dtype in_dtype, taylor_dtype out_dtype,
@@ -121,9 +130,28 @@ const char* taylor_last_error(void);
  * taylor_attn_prefill on this thread records events[0] before its first
  * launch, events[1] after the segment-sum kernel, events[2] after the scan
  * kernel and events[3] after the chunk kernel, all on its stream (events of
- * phases that do not run are recorded back to back).  count == 0 turns it
- * off.  The events stay owned by the caller. */
+ * phases that do not run are recorded back to back; for n = 3 with bfloat16
+ * inputs events[1] and events[2] both follow the small kernel that clears the
+ * workspace flags, and events[3] follows the single prefill kernel).
+ * count == 0 turns it off.  The events stay owned by the caller. */
 int taylor_set_phase_events(hipEvent_t* events, int count);
+
+/* Outcome of the waits between workgroups in the last taylor_attn_prefill that
+ * used `workspace` (n = 3, bfloat16 inputs, more than one segment per
+ * sequence).  Waits for the work queued on `stream` (the one call here that
+ * synchronises), then returns TAYLOR_OK, or TAYLOR_ETIMEOUT if a wait ran
+ * out, in which case that call's outputs and state are wrong.  A workspace
+ * that such a call did not use (NULL, too small, or last used by another
+ * path) gives TAYLOR_OK.  A wait can only run out if the device stalls a
+ * running workgroup for longer than the limit (a workgroup only waits for
+ * workgroups that started before it). */
+int taylor_prefill_check(const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Test hook for the time-out path: the number of polls (each followed by a
+ * short sleep) after which a wait between workgroups gives up; default
+ * 1 << 20 (at least 0.4 s).  Process-wide; returns the previous value, or -1
+ * for a negative argument (nothing changed). */
+int taylor_set_wait_limit(int polls);
 
 #ifdef __cplusplus
 }

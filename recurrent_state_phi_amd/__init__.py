@@ -21,17 +21,18 @@ import torch
 __all__ = [
     "LIB_PATH", "TaylorError", "state_width", "state_numel", "new_state", "state_init",
     "state_views", "prefill_workspace_bytes", "prefill", "decode", "set_phase_events",
-    "EXPORTED_SYMBOLS",
+    "prefill_check", "set_wait_limit", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtaylor_attn.so")
 
 TAYLOR_F32, TAYLOR_BF16 = 0, 1
-_CODES = {0: "TAYLOR_OK", -1: "TAYLOR_EINVAL", -2: "TAYLOR_EUNSUPPORTED", -3: "TAYLOR_EHIP"}
+_CODES = {0: "TAYLOR_OK", -1: "TAYLOR_EINVAL", -2: "TAYLOR_EUNSUPPORTED", -3: "TAYLOR_EHIP", -4: "TAYLOR_ETIMEOUT"}
 
 EXPORTED_SYMBOLS = (
     "taylor_state_width", "taylor_state_numel", "taylor_state_init", "taylor_prefill_workspace_bytes",
     "taylor_attn_prefill", "taylor_attn_decode", "taylor_last_error", "taylor_set_phase_events",
+    "taylor_prefill_check", "taylor_set_wait_limit",
 )
 
 
@@ -66,6 +67,10 @@ _lib.taylor_last_error.argtypes = []
 _lib.taylor_last_error.restype = ctypes.c_char_p
 _lib.taylor_set_phase_events.argtypes = [_vp, _i]
 _lib.taylor_set_phase_events.restype = _i
+_lib.taylor_prefill_check.argtypes = [_vp, _sz, _vp]
+_lib.taylor_prefill_check.restype = _i
+_lib.taylor_set_wait_limit.argtypes = [_i]
+_lib.taylor_set_wait_limit.restype = _i
 
 
 def raw_library() -> ctypes.CDLL:
@@ -192,3 +197,20 @@ def set_phase_events(events) -> None:
         return
     arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
     _check(_lib.taylor_set_phase_events(ctypes.cast(arr, ctypes.c_void_p), 4))
+
+
+def prefill_check(workspace: torch.Tensor | None) -> None:
+    """Wait for the current stream and raise TaylorError (TAYLOR_ETIMEOUT) if a wait
+    between workgroups ran out in the last prefill that used ``workspace``."""
+    if workspace is None:
+        return
+    _check(_lib.taylor_prefill_check(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream_ptr(workspace.device)))
+
+
+def set_wait_limit(polls: int) -> int:
+    """Test hook: polls before a wait between workgroups gives up; returns the previous value."""
+    prev = _lib.taylor_set_wait_limit(int(polls))
+    if prev < 0:
+        raise TaylorError(-1, _lib.taylor_last_error().decode())
+    return prev

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdio>
 #include <string>
 
@@ -16,6 +17,7 @@ namespace {
 thread_local std::string g_last_error;
 thread_local hipEvent_t g_phase_events[4] = {nullptr, nullptr, nullptr, nullptr};
 thread_local bool g_phase_events_on = false;
+std::atomic<int> g_wait_limit{1 << 20};
 
 int fail(int code, const std::string& msg) {
   g_last_error = msg;
@@ -120,7 +122,8 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, fl
     if (!aligned16(workspace)) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: workspace must be 16-byte aligned");
   }
   taylor::PrefillArgs args{q, k, v, o, state, static_cast<float*>(workspace), B * H, N, n, chunk, a,
-                           in_bf16, out_bf16, plan, stream, g_phase_events_on ? g_phase_events : nullptr};
+                           in_bf16, out_bf16, plan, stream, g_phase_events_on ? g_phase_events : nullptr,
+                           g_wait_limit.load(std::memory_order_relaxed)};
   const hipError_t e = taylor::launch_prefill(args);
   if (e != hipSuccess) return hip_fail(e, "taylor_attn_prefill: kernel launch");
   return TAYLOR_OK;
@@ -142,6 +145,22 @@ int taylor_attn_decode(const void* q, const void* k, const void* v, void* o, flo
   const hipError_t e = taylor::launch_decode(args);
   if (e != hipSuccess) return hip_fail(e, "taylor_attn_decode: kernel launch");
   return TAYLOR_OK;
+}
+
+int taylor_prefill_check(const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (workspace == nullptr || workspace_bytes < 3 * sizeof(int)) return TAYLOR_OK;
+  int hdr[3] = {0, 0, 0};
+  hipError_t e = hipMemcpyAsync(hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "taylor_prefill_check");
+  if (hdr[2] != taylor::kN3Magic || hdr[1] == 0) return TAYLOR_OK;
+  return fail(TAYLOR_ETIMEOUT, "taylor_prefill_check: a wait between workgroups ran out; that call's outputs and "
+                               "state are wrong");
+}
+
+int taylor_set_wait_limit(int polls) {
+  if (polls < 0) return fail(TAYLOR_EINVAL, "taylor_set_wait_limit: polls must be >= 0"), -1;
+  return g_wait_limit.exchange(polls);
 }
 
 }  // extern "C"

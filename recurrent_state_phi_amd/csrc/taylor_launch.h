@@ -37,6 +37,7 @@ struct PrefillArgs {
   PrefillPlan plan;
   hipStream_t stream;
   hipEvent_t* events;  // 4 phase events or nullptr
+  int wait_limit;      // polls of a wait between workgroups before it gives up
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
@@ -46,6 +47,10 @@ hipError_t launch_prefill(const PrefillArgs& a);
 // launch with a look-back across segments, and the workspace it needs.
 hipError_t launch_prefill_n3_bf16(const PrefillArgs& a);
 size_t prefill_n3_workspace_floats(int BH, int nseg);
+// Header words of that workspace: [1] error code, [2] kN3Magic once the flag-
+// clearing kernel has run.
+constexpr int kN3Magic = 0x54617933;
+constexpr int kN3ErrTimeout = 1;
 
 // n = 4, feature-blocked, chunk 32 or 64 (taylor_prefill_fb.hip), and the
 // floats of its per-block output workspace.

@@ -77,7 +77,8 @@ constexpr int kKTRows = 16;
 
 // Workspace of a multi-segment call (32-bit words):
 //   [0]                    ticket counter
-//   [1]                    error code (nonzero: a look-back wait ran out)
+//   [1]                    error code (kN3ErrTimeout: a wait ran out)
+//   [2]                    kN3Magic (the flags below belong to this kernel)
 //   [kHdr + kFlagStride * (b * nseg + s)]  flag of segment s of sequence b:
 //                          nonzero once its image is published (one flag per
 //                          256 bytes: polls of different flags do not queue
@@ -92,8 +93,6 @@ constexpr int kHdr = 64;
 constexpr int kFlagStride = 64;
 constexpr int kImgS = 40 * 64 * 4;       // 40 owned (slot, column tile) pairs per workgroup
 constexpr int kImgFloats = kImgS + 384;  // + T': waves x 3 slots x 4 lane groups x 4 rows (8 waves)
-constexpr int kSpinLimit = 1 << 20;      // polls of one look-back wait (a short sleep each: >= 0.4 s)
-constexpr int kErrWait = 1;
 
 __host__ __device__ constexpr size_t header_words(int BH, int nseg) {
   return kHdr + (size_t)BH * nseg * kFlagStride;
@@ -309,11 +308,11 @@ __device__ __forceinline__ void raise_flag(int* flag, int value) {
   if (threadIdx.x == 0) __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wait (per wave) until *flag is nonzero and return it; 0 after kSpinLimit
+// Wait (per wave) until *flag is nonzero and return it; 0 after `limit`
 // polls, with the error recorded (the caller then reads whatever the image
 // holds: the results are wrong, and the error code says so).
-__device__ __forceinline__ int wait_flag(const int* flag, int* err) {
-  for (int i = 0; i < kSpinLimit; ++i) {
+__device__ __forceinline__ int wait_flag(const int* flag, int* err, int limit) {
+  for (int i = 0; i < limit; ++i) {
     const int v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     if (v != 0) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -321,7 +320,7 @@ __device__ __forceinline__ int wait_flag(const int* flag, int* err) {
     }
     __builtin_amdgcn_s_sleep(16);
   }
-  __hip_atomic_store(err, kErrWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(err, kN3ErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return 0;
 }
 
@@ -810,7 +809,7 @@ template <int C, typename TOUT>
 __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefill_n3_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     TOUT* __restrict__ o, float* __restrict__ st_S, float* __restrict__ st_T, int* __restrict__ sync,
-    float* __restrict__ sums, int N, int nseg, int cps, int gs, float inv_a) {
+    float* __restrict__ sums, int N, int nseg, int cps, int gs, float inv_a, int wait_limit) {
   constexpr int NW = waves_for<C>();
   // The segment-sum pass steps over 2C tokens at a time (half the barriers and
   // twice the independent work per step; it needs no state copy and no q).
@@ -867,7 +866,7 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
     if (leader) {
       Acc x;
       for (int j = g0; j < seg; ++j) {
-        wait_flag(flag_of(j), err);
+        wait_flag(flag_of(j), err, wait_limit);
         image_load<NW>(image_of(j), x, w, lane);
         acc_add<NW>(pre, x, lane);
         acc_add<NW>(acc, x, lane);
@@ -875,7 +874,7 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
       image_store<NW, false>(image_of(seg), acc, acc, w, lane);
       raise_flag(flag_of(seg), 1);
       for (int G = 0; G < grp; ++G) {
-        wait_flag(flag_of(G * gs + gs - 1), err);
+        wait_flag(flag_of(G * gs + gs - 1), err, wait_limit);
         image_load<NW>(image_of(G * gs + gs - 1), x, w, lane);
         acc_add<NW>(pre, x, lane);
       }
@@ -889,8 +888,8 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
       for (int i = 0; i < n; i += 2) {
         const bool two = i + 1 < n;  // uniform
         Acc x, y;
-        wait_flag(flag_of(source(i)), err);
-        if (two) wait_flag(flag_of(source(i + 1)), err);
+        wait_flag(flag_of(source(i)), err, wait_limit);
+        if (two) wait_flag(flag_of(source(i + 1)), err, wait_limit);
         image_load<NW>(image_of(source(i)), x, w, lane);
         image_load<NW>(image_of(two ? source(i + 1) : source(i)), y, w, lane);
         acc_add<NW>(pre, x, lane);
@@ -903,11 +902,12 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
   if (seg == nseg - 1) store_caller_state<NW>(img, st_S, st_T, bh, own, pre);
 }
 
-// Clears the ticket counter, the error code and the nslots flags.
+// Clears the ticket counter, the error code and the nslots flags, and marks
+// the header as this kernel's.
 __global__ void clear_flags_kernel(int* sync, int nslots) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < nslots) sync[kHdr + (size_t)i * kFlagStride] = 0;
-  if (i < 2) sync[i] = 0;
+  if (i < 3) sync[i] = i == 2 ? kN3Magic : 0;
 }
 
 // Segments per group: about sqrt(nseg), at least 2.
@@ -943,7 +943,7 @@ hipError_t launch(const PrefillArgs& a) {
   }
   hipLaunchKernelGGL((prefill_n3_kernel<C, TOUT>), dim3(a.BH * pl.nseg), dim3(64 * waves_for<C>()), 0, a.stream, q,
                      k, v, static_cast<TOUT*>(a.o), st_S, st_T, sync, sums, a.N, pl.nseg, pl.chunks_per_seg,
-                     group_size(pl.nseg), inv_a);
+                     group_size(pl.nseg), inv_a, a.wait_limit);
   if (ev) (void)hipEventRecord(ev[3], a.stream);
   return hipGetLastError();
 }

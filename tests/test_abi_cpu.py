@@ -125,3 +125,20 @@ def test_invalid_arguments_are_rejected_before_launch(rsp):
     assert lib.taylor_state_init(None, 0, 1, 16, 64, 3, None) == 0
     assert lib.taylor_set_phase_events(None, 4) == -1
     assert lib.taylor_set_phase_events(None, 0) == 0
+
+
+def test_wait_limit_hook_and_check_without_workspace(rsp):
+    """taylor_set_wait_limit returns the previous limit and rejects negative values;
+    taylor_prefill_check has nothing to check without a workspace (no device work)."""
+    lib = rsp.raw_library()
+    prev = lib.taylor_set_wait_limit(5)
+    try:
+        assert prev == 1 << 20
+        assert lib.taylor_set_wait_limit(7) == 5
+        assert lib.taylor_set_wait_limit(-1) == -1
+        assert b"polls" in lib.taylor_last_error()
+        assert lib.taylor_set_wait_limit(7) == 7  # unchanged by the rejected call
+    finally:
+        lib.taylor_set_wait_limit(prev)
+    assert lib.taylor_prefill_check(None, 0, None) == 0
+    assert lib.taylor_prefill_check(None, 1 << 20, None) == 0

@@ -315,3 +315,34 @@ def test_decode_workload_sampled(rsp):
         rows = np.arange(N0, N0 + steps)
         ref = oracle.taylor_direct(q1, k1, v1, n, 1.0, rows=rows)
         assert oracle.rel_err_rowwise(got[:, b, h], ref) <= TOL["f32"], (b, h)
+
+
+# ---------------------------------------------------------------------------
+# the bounded waits between the workgroups of one sequence (n = 3, bf16)
+# ---------------------------------------------------------------------------
+def test_prefill_wait_timeout_is_reported(rsp):
+    """With a limit of zero polls every wait between segment workgroups gives up at
+    once: the call still completes and taylor_prefill_check reports
+    TAYLOR_ETIMEOUT.  With the default limit the same call passes the check and
+    matches the oracle."""
+    say("prefill wait time-out path")
+    B, H, N = 1, 2, 1000  # 16 chunks of 64 per head: one workgroup per chunk-long segment
+    q, k, v = TI.make_qkv(91, B, H, N, 16, 64, dtype="bf16")
+    qd, kd, vd = (to_dev(x, "bf16") for x in (q, k, v))
+    need = rsp.prefill_workspace_bytes(B, H, N, 3, 64)
+    assert need > 0
+    ws = torch.empty(need // 4, dtype=torch.float32, device=DEV)
+    prev = rsp.set_wait_limit(0)
+    try:
+        st = rsp.new_state(B, H, 3, device=DEV)
+        rsp.prefill(qd, kd, vd, st, 3, 1.0, chunk=64, workspace=ws)
+        with pytest.raises(rsp.TaylorError) as e:
+            rsp.prefill_check(ws)
+        assert e.value.code == -4
+    finally:
+        rsp.set_wait_limit(prev)
+    st = rsp.new_state(B, H, 3, device=DEV)
+    o = rsp.prefill(qd, kd, vd, st, 3, 1.0, chunk=64, workspace=ws)
+    rsp.prefill_check(ws)
+    got = o.float().cpu().numpy().astype(np.float64)
+    assert oracle.rel_err_rowwise(got, oracle.taylor_direct(q, k, v, 3, 1.0)) <= TOL["bf16"]
