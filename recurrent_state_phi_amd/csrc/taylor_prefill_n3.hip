@@ -799,6 +799,202 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
   store_prev();
 }
 
+// ---- segment sum in registers ---------------------------------------------
+// A = sum over the segment of phi(k)^T [v, 1], without staging anything in LDS:
+// the waves form NW/2 pairs; the pairs take 32-token groups in turn, and the
+// two waves of a pair split the 10 feature tiles (wave half 0: tiles 0..4,
+// half 1: tiles 5..9).  Each wave loads its group's k and v, transposes them
+// on the matrix cores (one-hot selector products, as in segment_pass) straight
+// into operand registers, builds its features with DPP rotations and keeps its
+// half of the state in 20 accumulator tiles; T of tile f accumulates in column
+// f of one more tile (B operand: ones in column f).  At the end the partial
+// states are added up in LDS (a fixed tree, so the result does not depend on
+// timing) and every wave picks up the tiles it owns in the replay.
+// bytes of the reduction area: max(1, NW/4) slots x 2 halves x 21 tiles
+template <int NW>
+constexpr int sum_lds_bytes() { return (NW / 4 > 1 ? NW / 4 : 1) * 2 * (5 * 4 + 1) * 64 * 16; }
+
+template <int NW>
+__device__ __forceinline__ void segment_sum_regs(unsigned char* lds_raw, const Own<NW>& own, Acc& a,
+                                                 const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                 int bh, int N, int t_begin, int t_end) {
+  constexpr int NP = NW / 2;
+  const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int pr = w >> 1, h = w & 1;  // pair, feature half (wave-uniform)
+  const int ngroups = (t_end - t_begin + 31) / 32;
+
+  f32x4 F[5][4], Tp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tl = 0; tl < 5; ++tl)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) F[tl][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // loads of group G: per 16-token tile, v columns 8g..+7 and 32+8g..+7 and
+  // (lanes g < 2) k dimensions 8g..+7 of token li; clamped into the segment
+  auto issue = [&](uint4 (&r)[6], int G) {
+    const int base = t_begin + 32 * min(G, ngroups - 1);
+    const int last = t_end - 1;
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const size_t tok = (size_t)bh * N + min(base + 16 * x + li, last);
+      r[3 * x] = *reinterpret_cast<const uint4*>(v + tok * kDV + 8 * g);
+      r[3 * x + 1] = *reinterpret_cast<const uint4*>(v + tok * kDV + 32 + 8 * g);
+      r[3 * x + 2] = *reinterpret_cast<const uint4*>(k + tok * kD + 8 * (g & 1));
+    }
+  };
+  bf16x8 sel0, sel1;
+  {
+    uint32_t w0[4], w1[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k0 = 8 * g + 2 * e;
+      w0[e] = (k0 == li ? 0x3F80u : 0u) | (k0 + 1 == li ? 0x3F800000u : 0u);
+      w1[e] = (k0 == li + 16 ? 0x3F80u : 0u) | (k0 + 1 == li + 16 ? 0x3F800000u : 0u);
+    }
+    sel0 = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
+    sel1 = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
+  }
+  const float pair_m = li < 8 ? 1.0f : 0.0f, const_m = li == 8 ? 1.0f : 0.0f;  // rows of tile 8
+  int pad = 0;  // padding tokens seen (their constant feature is 1)
+
+  // group G from the loaded registers r; `refill` is called once r has been
+  // consumed (it issues the loads of the next group into r)
+  auto group = [&](uint4 (&r)[6], int G, auto&& refill) {
+    const int nvalid = min(32, t_end - (t_begin + 32 * G));
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const uint4 z4 = make_uint4(0, 0, 0, 0);
+    uint32_t vw[4][4];  // B operands of the 4 column tiles, built in place
+    float xi[8];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const bool valid = 16 * x + li < nvalid;  // row li of the A operands
+      const bf16x8 v0 = __builtin_bit_cast(bf16x8, valid ? r[3 * x] : z4);
+      const bf16x8 v1 = __builtin_bit_cast(bf16x8, valid ? r[3 * x + 1] : z4);
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, (valid && g < 2) ? r[3 * x + 2] : z4);
+      const f32x4 d0 = mfma_bf16_k32(v0, sel0, zero), d1 = mfma_bf16_k32(v0, sel1, zero);
+      const f32x4 d2 = mfma_bf16_k32(v1, sel0, zero), d3 = mfma_bf16_k32(v1, sel1, zero);
+      const f32x4 dv[4] = {d0, d1, d2, d3};
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        vw[ct][2 * x] = pack2(dv[ct][0], dv[ct][1]);
+        vw[ct][2 * x + 1] = pack2(dv[ct][2], dv[ct][3]);
+      }
+      // lane (li, g): dimension li of tokens 16x + 4g .. 16x + 4g + 3
+      const f32x4 dk = mfma_bf16_k32(ka, sel0, zero);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xi[4 * x + e] = dk[e];
+    }
+    refill();
+    // k-slots of lane group g: tokens 4g..4g+3 and 16+4g..16+4g+3 of the group
+    bf16x8 vb[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) vb[ct] = __builtin_bit_cast(bf16x8, make_uint4(vw[ct][0], vw[ct][1], vw[ct][2], vw[ct][3]));
+    auto tile = [&](int tl, int f, const float (&fx)[8]) {
+      const bf16x8 aphi = __builtin_bit_cast(
+          bf16x8, make_uint4(pack2(fx[0], fx[1]), pack2(fx[2], fx[3]), pack2(fx[4], fx[5]), pack2(fx[6], fx[7])));
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) F[tl][ct] = mfma_bf16_k32(aphi, vb[ct], F[tl][ct]);
+      // ones in column f of the T tile (rebuilt here on purpose: ten such
+      // operands kept across the loop would not fit in registers)
+      uint32_t one2 = li == f ? 0x3F803F80u : 0u;
+      asm volatile("" : "+v"(one2));
+      Tp = mfma_bf16_k32(aphi, __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2)), Tp);
+    };
+    float fx[8];
+    if (h == 0) {  // tiles 0..4: x_li x_(li+f)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * xi[e];
+      tile(0, 0, fx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<1>(xi[e]);
+      tile(1, 1, fx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<2>(xi[e]);
+      tile(2, 2, fx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<3>(xi[e]);
+      tile(3, 3, fx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<4>(xi[e]);
+      tile(4, 4, fx);
+    } else {  // tiles 5..7, tile 8 (pairs at distance 8, the constant), tile 9 (linear)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<5>(xi[e]);
+      tile(0, 5, fx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<6>(xi[e]);
+      tile(1, 6, fx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<7>(xi[e]);
+      tile(2, 7, fx);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fx[e] = fmaf(xi[e] * from_lane_plus<8>(xi[e]), pair_m, const_m);
+      tile(3, 8, fx);
+      tile(4, 9, xi);
+      pad += 32 - nvalid;
+    }
+  };
+
+  // the next group's loads are in flight while this group's products run
+  uint4 ra[6];
+  issue(ra, pr);
+  for (int G = pr; G < ngroups; G += NP) group(ra, G, [&] { issue(ra, G + NP); });
+  // the constant feature counted padding tokens: take them out of its T entry
+  // (column 8 = tile 8, row 8: lane 40, element 0)
+  Tp[0] -= (lane == 40) ? (float)pad : 0.0f;
+
+  // ---- add the partial states of the pairs (tree over pairs), then hand
+  //      every wave the tiles it owns
+  f32x4* R = reinterpret_cast<f32x4*>(lds_raw);  // [slot][half 2][21 tiles][64 lanes]
+  auto at = [&](int slot, int hh, int t) { return R + ((slot * 2 + hh) * 21 + t) * 64 + lane; };
+  __syncthreads();  // the LDS area may still be in use by earlier code
+#pragma unroll
+  for (int step = NP / 2; step >= 1; step /= 2) {
+    if (pr >= step && pr < 2 * step) {  // uniform
+#pragma unroll
+      for (int tl = 0; tl < 5; ++tl)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) *at(pr - step, h, 4 * tl + ct) = F[tl][ct];
+      *at(pr - step, h, 20) = Tp;
+    }
+    __syncthreads();
+    if (pr < step) {
+#pragma unroll
+      for (int tl = 0; tl < 5; ++tl)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) F[tl][ct] += *at(pr, h, 4 * tl + ct);
+      Tp += *at(pr, h, 20);
+    }
+    __syncthreads();
+  }
+  if (pr == 0) {
+#pragma unroll
+    for (int tl = 0; tl < 5; ++tl)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) *at(0, h, 4 * tl + ct) = F[tl][ct];
+    *at(0, h, 20) = Tp;
+  }
+  __syncthreads();
+  using Wv = Waves<NW>;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (s == 1 && !Wv::HAS_S1) {
+      a.t[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+      continue;
+    }
+    const int ft = own.ft[s], hh = ft < 5 ? 0 : 1, tl = ft - 5 * hh;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+      if (Wv::has(s, ct)) a.s[s][ct] = *at(0, hh, 4 * tl + (s == 2 ? own.ctb + ct : ct));
+    // T of tile ft: column ft of the T tile, i.e. lane (li = ft, g) of it
+    const f32x4 tcol = R[((0 * 2 + hh) * 21 + 20) * 64 + 16 * g + ft];
+    const bool own_t = li == 0 && (s < 2 || own.own_t2);
+    a.t[s] = own_t ? tcol : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();  // the area is reused by the replay's buffers
+}
+
 // ---- the kernel -------------------------------------------------------------
 // Grid: BH * nseg workgroups.  sync == nullptr exactly when nseg == 1 (then
 // workgroup b runs sequence b from the caller's state, with no prefix step).
@@ -811,15 +1007,12 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
     TOUT* __restrict__ o, float* __restrict__ st_S, float* __restrict__ st_T, int* __restrict__ sync,
     float* __restrict__ sums, int N, int nseg, int cps, int gs, float inv_a, int wait_limit) {
   constexpr int NW = waves_for<C>();
-  // The segment-sum pass steps over 2C tokens at a time (half the barriers and
-  // twice the independent work per step; it needs no state copy and no q).
-  constexpr int CA = 2 * C;
-  using LA = Lds<CA, false>;
   using LB = Lds<C, true>;
-  // The chunk buffers of either pass, and while the final state is stored, a
-  // float [153 * 65] image of it in the caller's layout.
-  constexpr size_t kLdsBytes = sizeof(LB) > sizeof(LA) ? (sizeof(LB) > kAbiImg * 4 ? sizeof(LB) : kAbiImg * 4)
-                                                        : (sizeof(LA) > kAbiImg * 4 ? sizeof(LA) : kAbiImg * 4);
+  // The replay's chunk buffers, the sum pass's reduction area, and while the
+  // final state is stored, a float [153 * 65] image of it in the caller's
+  // layout.
+  constexpr size_t kA = sizeof(LB) > (size_t)sum_lds_bytes<NW>() ? sizeof(LB) : (size_t)sum_lds_bytes<NW>();
+  constexpr size_t kLdsBytes = kA > kAbiImg * 4 ? kA : kAbiImg * 4;
   __shared__ __align__(16) unsigned char lds_raw[kLdsBytes];
   __shared__ int s_ticket;
   float* img = reinterpret_cast<float*>(lds_raw);
@@ -845,16 +1038,14 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
   // the last member of a group publishes the group's sum, unless no group follows
   const bool leader = seg == g0 + gs - 1 && seg < nseg - 1;
 
-  // Every segment's prefix starts from the caller's state; its loads are
-  // issued first and stay in flight during the first pass.
+  // 1. the segment's own sum (not needed for the last segment)
+  Acc acc;
+  if (seg < nseg - 1) segment_sum_regs<NW>(lds_raw, own, acc, k, v, bh, N, t_begin, t_end);
+  else zero_acc(acc);
+  // Every segment's prefix starts from the caller's state (its loads overlap
+  // with the publication and the waits below).
   Acc pre;
   load_caller_state_raw<NW>(st_S, st_T, bh, own, pre);
-  Acc acc;
-  zero_acc(acc);
-  // 1. the segment's own sum (not needed for the last segment)
-  if (seg < nseg - 1)
-    segment_pass<CA, NW, false, TOUT>(*reinterpret_cast<LA*>(lds_raw), own, acc, q, k, v, o, bh, N, t_begin, t_end,
-                                      inv_a);
   unweight_caller_state<NW>(own, pre);
   // 2. prefix = caller's state + sums of the earlier members of the group +
   //    group sums of the earlier groups (the leader adds the members' sums to
