@@ -1042,8 +1042,13 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
   Acc acc;
   if (seg < nseg - 1) segment_sum_regs<NW>(lds_raw, own, acc, k, v, bh, N, t_begin, t_end);
   else zero_acc(acc);
-  // Every segment's prefix starts from the caller's state (its loads overlap
-  // with the publication and the waits below).
+  // a segment that is not the last of its group publishes its sum at once
+  if (nseg > 1 && !leader && seg < nseg - 1) {  // uniform
+    image_store<NW, false>(image_of(seg), acc, acc, w, lane);
+    raise_flag(flag_of(seg), 1);
+  }
+  // Every segment's prefix starts from the caller's state (loaded after the
+  // publication, which waits for all outstanding memory operations).
   Acc pre;
   load_caller_state_raw<NW>(st_S, st_T, bh, own, pre);
   unweight_caller_state<NW>(own, pre);
@@ -1070,10 +1075,6 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
         acc_add<NW>(pre, x, lane);
       }
     } else {
-      if (seg < nseg - 1) {
-        image_store<NW, false>(image_of(seg), acc, acc, w, lane);
-        raise_flag(flag_of(seg), 1);
-      }
       // two images in flight at a time
       const int n = r + grp;
       for (int i = 0; i < n; i += 2) {
