@@ -318,7 +318,7 @@ __device__ __forceinline__ int wait_flag(const int* flag, int* err, int limit) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       return v;
     }
-    __builtin_amdgcn_s_sleep(16);
+    __builtin_amdgcn_s_sleep(4);
   }
   __hip_atomic_store(err, kN3ErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return 0;
@@ -1047,11 +1047,16 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
     image_store<NW, false>(image_of(seg), acc, acc, w, lane);
     raise_flag(flag_of(seg), 1);
   }
-  // Every segment's prefix starts from the caller's state (loaded after the
-  // publication, which waits for all outstanding memory operations).
+  // Every segment's prefix starts from the caller's state, loaded after the
+  // publication (which waits for all outstanding memory operations); a leader
+  // loads it only after it has published the group sum.
   Acc pre;
-  load_caller_state_raw<NW>(st_S, st_T, bh, own, pre);
-  unweight_caller_state<NW>(own, pre);
+  if (leader) {
+    zero_acc(pre);
+  } else {
+    load_caller_state_raw<NW>(st_S, st_T, bh, own, pre);
+    unweight_caller_state<NW>(own, pre);
+  }
   // 2. prefix = caller's state + sums of the earlier members of the group +
   //    group sums of the earlier groups (the leader adds the members' sums to
   //    its own as well, and publishes that as the group sum)
@@ -1060,15 +1065,26 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
     const int r = seg - g0;  // earlier members
     auto source = [&](int i) { return i < r ? g0 + i : (i - r) * gs + gs - 1; };
     if (leader) {
-      Acc x;
-      for (int j = g0; j < seg; ++j) {
+      for (int j = g0; j < seg; j += 2) {
+        const bool two = j + 1 < seg;  // uniform
+        Acc x, y;
         wait_flag(flag_of(j), err, wait_limit);
+        if (two) wait_flag(flag_of(j + 1), err, wait_limit);
         image_load<NW>(image_of(j), x, w, lane);
+        image_load<NW>(image_of(two ? j + 1 : j), y, w, lane);
         acc_add<NW>(pre, x, lane);
         acc_add<NW>(acc, x, lane);
+        if (two) {
+          acc_add<NW>(pre, y, lane);
+          acc_add<NW>(acc, y, lane);
+        }
       }
       image_store<NW, false>(image_of(seg), acc, acc, w, lane);
       raise_flag(flag_of(seg), 1);
+      Acc x;
+      load_caller_state_raw<NW>(st_S, st_T, bh, own, x);
+      unweight_caller_state<NW>(own, x);
+      acc_add<NW>(pre, x, lane);
       for (int G = 0; G < grp; ++G) {
         wait_flag(flag_of(G * gs + gs - 1), err, wait_limit);
         image_load<NW>(image_of(G * gs + gs - 1), x, w, lane);
