@@ -686,24 +686,24 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
 
         // ---- diagonal block: P = tril(p_3(K Q^T / a)), lane holds P[token li][keys]
         const bf16x4 bq = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&L.Q[b][tok][4 * g]));
+        // Every key tile of the chunk, without branches (the products are
+        // cheap, and straight-line code lets the key reads, the products and
+        // the polynomial of different key tiles overlap); tiles after the
+        // token tile are masked to zero, the diagonal tile causally (key
+        // 16 kt + 4g + r against token 16 tt + li).
         bf16x8 pb[NKB];
 #pragma unroll
         for (int kt = 0; kt < 2 * NKB; ++kt) {
-          float p[4] = {0.f, 0.f, 0.f, 0.f};
-          if (kt <= tt) {
-            const int key0 = 16 * kt + li;
-            const bf16x4 ak = {f32_to_bf16(L.K[b][4 * g][key0]), f32_to_bf16(L.K[b][4 * g + 1][key0]),
-                               f32_to_bf16(L.K[b][4 * g + 2][key0]), f32_to_bf16(L.K[b][4 * g + 3][key0])};
-            const f32x4 s = mfma_bf16_k16(ak, bq, f32x4{0.f, 0.f, 0.f, 0.f});
+          const int key0 = 16 * kt + li;
+          const bf16x4 ak = {f32_to_bf16(L.K[b][4 * g][key0]), f32_to_bf16(L.K[b][4 * g + 1][key0]),
+                             f32_to_bf16(L.K[b][4 * g + 2][key0]), f32_to_bf16(L.K[b][4 * g + 3][key0])};
+          const f32x4 s = mfma_bf16_k16(ak, bq, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = fmaf(s[r], fmaf(0.5f, s[r], 1.0f), 1.0f);  // s = q.k / a
-            if (kt == tt) {  // diagonal tile: causal mask (key 16kt + 4g + r against token 16tt + li)
-#pragma unroll
-              for (int r = 0; r < 4; ++r) p[r] = (4 * g + r <= li) ? p[r] : 0.0f;
-            }
+          for (int r = 0; r < 4; ++r) {
+            const float p = fmaf(s[r], fmaf(0.5f, s[r], 1.0f), 1.0f);  // s = q.k / a
+            const bool keep = kt < tt || (kt == tt && 4 * g + r <= li);
+            pb[kt >> 1][4 * (kt & 1) + r] = f32_to_bf16(keep ? p : 0.0f);
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pb[kt >> 1][4 * (kt & 1) + r] = f32_to_bf16(p[r]);
         }
 
         f32x4 y[5];
