@@ -610,6 +610,7 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
     {
       const uint32_t one2 = li == 0 ? 0x3F803F80u : 0u;
       const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
+      const bf16x8 zeros = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
       const float pair_m = li < 8 ? 1.0f : 0.0f, const_m = li == 8 ? 1.0f : 0.0f;  // rows of tile 8
       const bool tile8 = own.tile8;  // wave-uniform
 #pragma unroll
@@ -644,10 +645,11 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
               f[e] = xi[e] * from_lane_plus<4>(xa[e]);    // tile w + 4: x_li x_(li+w+4)
             } else {
               // tile 8: x_li x_(li+8) (li < 8), the constant (li == 8), zero rows;
-              // tile 9: x_li.  (A uniform branch: a DPP rotation reads its
-              // source from the other lanes, which must all be executing.)
-              if (tile8) f[e] = fmaf(xi[e] * from_lane_plus<8>(xi[e]), pair_m, const_m);
-              else f[e] = xi[e];
+              // tile 9: x_li.  (A select, not a branch: the DPP rotation reads
+              // its source from the other lanes, which must all be executing,
+              // and straight-line code schedules better.)
+              const float f8 = fmaf(xi[e] * from_lane_plus<8>(xi[e]), pair_m, const_m);
+              f[e] = tile8 ? f8 : xi[e];
             }
           }
           const bf16x8 aphi = __builtin_bit_cast(
@@ -657,21 +659,17 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
             for (int ct = 0; ct < 4; ++ct) acc[s][ct] = mfma_bf16_k32(aphi, vb[ct], acc[s][ct]);
             tacc[s] = mfma_bf16_k32(aphi, ones, tacc[s]);
           } else {
-            if (own_t2) tacc[2] = mfma_bf16_k32(aphi, ones, tacc[2]);
-            // column tiles ctb .. ctb + NCT2 - 1 (ctb is wave-uniform)
+            // (every wave runs the T product, against zeros where it does not
+            // own T of the tile: no branch in the loop)
+            tacc[2] = mfma_bf16_k32(aphi, own_t2 ? ones : zeros, tacc[2]);
+            // column tiles ctb .. ctb + NCT2 - 1 (ctb is wave-uniform; operands
+            // selected, not branched on)
             if constexpr (NCT2 == 2) {
-              if (ctb == 0) {
-                acc[2][0] = mfma_bf16_k32(aphi, vb[0], acc[2][0]);
-                acc[2][1] = mfma_bf16_k32(aphi, vb[1], acc[2][1]);
-              } else {
-                acc[2][0] = mfma_bf16_k32(aphi, vb[2], acc[2][0]);
-                acc[2][1] = mfma_bf16_k32(aphi, vb[3], acc[2][1]);
-              }
+              acc[2][0] = mfma_bf16_k32(aphi, ctb == 0 ? vb[0] : vb[2], acc[2][0]);
+              acc[2][1] = mfma_bf16_k32(aphi, ctb == 0 ? vb[1] : vb[3], acc[2][1]);
             } else {
-              if (ctb == 0) acc[2][0] = mfma_bf16_k32(aphi, vb[0], acc[2][0]);
-              else if (ctb == 1) acc[2][0] = mfma_bf16_k32(aphi, vb[1], acc[2][0]);
-              else if (ctb == 2) acc[2][0] = mfma_bf16_k32(aphi, vb[2], acc[2][0]);
-              else acc[2][0] = mfma_bf16_k32(aphi, vb[3], acc[2][0]);
+              acc[2][0] = mfma_bf16_k32(aphi, ctb == 0 ? vb[0] : ctb == 1 ? vb[1] : ctb == 2 ? vb[2] : vb[3],
+                                        acc[2][0]);
             }
           }
         }
