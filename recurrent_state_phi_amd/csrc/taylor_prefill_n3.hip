@@ -745,7 +745,7 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
         // q is staged as q / a: the products y_s z_t already carry 2 alpha_2 = 1 / a^2,
         // y_s carries alpha_1 = 1 / a
         const float kb0f = gh == 0 ? 0.5f : 1.0f;  // diagonal tile: weight 1 instead of 2
-        const float cA = g == 0 ? 1.0f : 0.0f, cB = g >= 2 ? 1.0f : 0.0f, cC = g == 1 ? 1.0f : 0.0f;
+        const float cB = g >= 2 ? 1.0f : 0.0f, cC = g == 1 ? 1.0f : 0.0f;
         constexpr int kD0[4] = {0, 1, 4, 5};
 #pragma unroll
         for (int kb = 0; kb < 5; ++kb) {
@@ -756,7 +756,10 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
               f[s] = yv[s] * zv[(s + kD0[kb]) & 15];
               if (kb == 0) f[s] *= kb0f;
             } else {
-              f[s] = cA * yv[s] * zv[(s + 8) & 15] + cB * yv[s] + (s == 0 ? cC : 0.0f);
+              // lane groups: 0 pairs at distance 8, 1 the constant (k-slot 0),
+              // 2 and 3 linear: one select and one product per feature
+              const float m = g == 0 ? zv[(s + 8) & 15] : cB;
+              f[s] = s == 0 ? fmaf(yv[s], m, cC) : yv[s] * m;
             }
           }
           const bf16x8 bphi = __builtin_bit_cast(
