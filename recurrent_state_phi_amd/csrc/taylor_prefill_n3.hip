@@ -802,34 +802,32 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
 
 // ---- segment sum in registers ---------------------------------------------
 // A = sum over the segment of phi(k)^T [v, 1], without staging anything in LDS:
-// the waves form NW/2 pairs; the pairs take 32-token groups in turn, and the
-// two waves of a pair split the 10 feature tiles (wave half 0: tiles 0..4,
-// half 1: tiles 5..9).  Each wave loads its group's k and v, transposes them
-// on the matrix cores (one-hot selector products, as in segment_pass) straight
-// into operand registers, builds its features with DPP rotations and keeps its
-// half of the state in 20 accumulator tiles; T of tile f accumulates in column
-// f of one more tile (B operand: ones in column f).  At the end the partial
-// states are added up in LDS (a fixed tree, so the result does not depend on
-// timing) and every wave picks up the tiles it owns in the replay.
-// bytes of the reduction area: max(1, NW/4) slots x 2 halves x 21 tiles
+// every wave takes whole 32-token groups (wave w: groups w, w + NW, ...) and
+// keeps a full partial state in registers: 10 feature tiles x 4 column tiles
+// of accumulators, and T of tile f in column f of one more tile (B operand:
+// ones in column f).  It loads the group's k and v once, transposes them on
+// the matrix cores (one-hot selector products, as in segment_pass) straight
+// into operand registers and builds the features with DPP rotations.  At the
+// end the partial states are added up in LDS, one wave's state at a time (a
+// fixed order, so the result does not depend on timing), and every wave picks
+// up the tiles it owns in the replay.
+// bytes of the reduction area: one state of 41 tiles
 template <int NW>
-constexpr int sum_lds_bytes() { return (NW / 4 > 1 ? NW / 4 : 1) * 2 * (5 * 4 + 1) * 64 * 16; }
+constexpr int sum_lds_bytes() { return 41 * 64 * 16; }
 
 template <int NW>
 __device__ __forceinline__ void segment_sum_regs(unsigned char* lds_raw, const Own<NW>& own, Acc& a,
                                                  const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                                  int bh, int N, int t_begin, int t_end) {
-  constexpr int NP = NW / 2;
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int pr = w >> 1, h = w & 1;  // pair, feature half (wave-uniform)
   const int ngroups = (t_end - t_begin + 31) / 32;
 
-  f32x4 F[5][4], Tp = {0.f, 0.f, 0.f, 0.f};
+  f32x4 F[10][4], Tp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int tl = 0; tl < 5; ++tl)
+  for (int f = 0; f < 10; ++f)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) F[tl][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < 4; ++ct) F[f][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // loads of group G: per 16-token tile, v columns 8g..+7 and 32+8g..+7 and
   // (lanes g < 2) k dimensions 8g..+7 of token li; clamped into the segment
@@ -891,90 +889,69 @@ __device__ __forceinline__ void segment_sum_regs(unsigned char* lds_raw, const O
     bf16x8 vb[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) vb[ct] = __builtin_bit_cast(bf16x8, make_uint4(vw[ct][0], vw[ct][1], vw[ct][2], vw[ct][3]));
-    auto tile = [&](int tl, int f, const float (&fx)[8]) {
+    // features of tile f (compile-time: the DPP rotation is an immediate)
+    auto tile = [&](auto fc) {
+      constexpr int f = decltype(fc)::value;
+      float fx[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (f == 0) fx[e] = xi[e] * xi[e];                        // x_li^2
+        else if constexpr (f < 8) fx[e] = xi[e] * from_lane_plus<f>(xi[e]);  // x_li x_(li+f)
+        else if constexpr (f == 8) fx[e] = fmaf(xi[e] * from_lane_plus<8>(xi[e]), pair_m, const_m);
+        else fx[e] = xi[e];                                                   // linear
+      }
       const bf16x8 aphi = __builtin_bit_cast(
           bf16x8, make_uint4(pack2(fx[0], fx[1]), pack2(fx[2], fx[3]), pack2(fx[4], fx[5]), pack2(fx[6], fx[7])));
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) F[tl][ct] = mfma_bf16_k32(aphi, vb[ct], F[tl][ct]);
+      for (int ct = 0; ct < 4; ++ct) F[f][ct] = mfma_bf16_k32(aphi, vb[ct], F[f][ct]);
       // ones in column f of the T tile (rebuilt here on purpose: ten such
       // operands kept across the loop would not fit in registers)
       uint32_t one2 = li == f ? 0x3F803F80u : 0u;
       asm volatile("" : "+v"(one2));
       Tp = mfma_bf16_k32(aphi, __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2)), Tp);
     };
-    float fx[8];
-    if (h == 0) {  // tiles 0..4: x_li x_(li+f)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * xi[e];
-      tile(0, 0, fx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<1>(xi[e]);
-      tile(1, 1, fx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<2>(xi[e]);
-      tile(2, 2, fx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<3>(xi[e]);
-      tile(3, 3, fx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<4>(xi[e]);
-      tile(4, 4, fx);
-    } else {  // tiles 5..7, tile 8 (pairs at distance 8, the constant), tile 9 (linear)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<5>(xi[e]);
-      tile(0, 5, fx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<6>(xi[e]);
-      tile(1, 6, fx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fx[e] = xi[e] * from_lane_plus<7>(xi[e]);
-      tile(2, 7, fx);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) fx[e] = fmaf(xi[e] * from_lane_plus<8>(xi[e]), pair_m, const_m);
-      tile(3, 8, fx);
-      tile(4, 9, xi);
-      pad += 32 - nvalid;
-    }
+    tile(std::integral_constant<int, 0>{});
+    tile(std::integral_constant<int, 1>{});
+    tile(std::integral_constant<int, 2>{});
+    tile(std::integral_constant<int, 3>{});
+    tile(std::integral_constant<int, 4>{});
+    tile(std::integral_constant<int, 5>{});
+    tile(std::integral_constant<int, 6>{});
+    tile(std::integral_constant<int, 7>{});
+    tile(std::integral_constant<int, 8>{});
+    tile(std::integral_constant<int, 9>{});
+    pad += 32 - nvalid;
   };
 
   // the next group's loads are in flight while this group's products run
   uint4 ra[6];
-  issue(ra, pr);
-  for (int G = pr; G < ngroups; G += NP) group(ra, G, [&] { issue(ra, G + NP); });
+  issue(ra, w);
+  for (int G = w; G < ngroups; G += NW) group(ra, G, [&] { issue(ra, G + NW); });
   // the constant feature counted padding tokens: take them out of its T entry
   // (column 8 = tile 8, row 8: lane 40, element 0)
   Tp[0] -= (lane == 40) ? (float)pad : 0.0f;
 
-  // ---- add the partial states of the pairs (tree over pairs), then hand
-  //      every wave the tiles it owns
-  f32x4* R = reinterpret_cast<f32x4*>(lds_raw);  // [slot][half 2][21 tiles][64 lanes]
-  auto at = [&](int slot, int hh, int t) { return R + ((slot * 2 + hh) * 21 + t) * 64 + lane; };
+  // ---- add up the waves' partial states in LDS, one wave at a time, then
+  //      hand every wave the tiles it owns
+  f32x4* R = reinterpret_cast<f32x4*>(lds_raw);  // [41 tiles][64 lanes]
+  auto at = [&](int t) { return R + t * 64 + lane; };
   __syncthreads();  // the LDS area may still be in use by earlier code
+  if (w == 0) {  // uniform
 #pragma unroll
-  for (int step = NP / 2; step >= 1; step /= 2) {
-    if (pr >= step && pr < 2 * step) {  // uniform
+    for (int f = 0; f < 10; ++f)
 #pragma unroll
-      for (int tl = 0; tl < 5; ++tl)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) *at(pr - step, h, 4 * tl + ct) = F[tl][ct];
-      *at(pr - step, h, 20) = Tp;
-    }
-    __syncthreads();
-    if (pr < step) {
-#pragma unroll
-      for (int tl = 0; tl < 5; ++tl)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) F[tl][ct] += *at(pr, h, 4 * tl + ct);
-      Tp += *at(pr, h, 20);
-    }
-    __syncthreads();
+      for (int ct = 0; ct < 4; ++ct) *at(4 * f + ct) = F[f][ct];
+    *at(40) = Tp;
   }
-  if (pr == 0) {
+  for (int src = 1; src < NW; ++src) {
+    __syncthreads();
+    if (w == src) {  // uniform
 #pragma unroll
-    for (int tl = 0; tl < 5; ++tl)
+      for (int f = 0; f < 10; ++f)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) *at(0, h, 4 * tl + ct) = F[tl][ct];
-    *at(0, h, 20) = Tp;
+        for (int ct = 0; ct < 4; ++ct) *at(4 * f + ct) += F[f][ct];
+      *at(40) += Tp;
+    }
   }
   __syncthreads();
   using Wv = Waves<NW>;
@@ -984,12 +961,12 @@ __device__ __forceinline__ void segment_sum_regs(unsigned char* lds_raw, const O
       a.t[s] = f32x4{0.f, 0.f, 0.f, 0.f};
       continue;
     }
-    const int ft = own.ft[s], hh = ft < 5 ? 0 : 1, tl = ft - 5 * hh;
+    const int ft = own.ft[s];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
-      if (Wv::has(s, ct)) a.s[s][ct] = *at(0, hh, 4 * tl + (s == 2 ? own.ctb + ct : ct));
+      if (Wv::has(s, ct)) a.s[s][ct] = *at(4 * ft + (s == 2 ? own.ctb + ct : ct));
     // T of tile ft: column ft of the T tile, i.e. lane (li = ft, g) of it
-    const f32x4 tcol = R[((0 * 2 + hh) * 21 + 20) * 64 + 16 * g + ft];
+    const f32x4 tcol = R[40 * 64 + 16 * g + ft];
     const bool own_t = li == 0 && (s < 2 || own.own_t2);
     a.t[s] = own_t ? tcol : f32x4{0.f, 0.f, 0.f, 0.f};
   }
