@@ -250,6 +250,26 @@ def test_prefill_workload_sampled(rsp):
     assert np.abs(S[:1, :2] - A[..., :64]).max() <= 2e-2 * np.abs(A[..., :64]).max()
 
 
+@pytest.mark.parametrize("chunk", [64, 128])
+def test_one_head_many_segments(rsp, chunk):
+    """B=1, H=1, N=32731 (ragged last chunk), bfloat16: the planner cuts the one
+    head into 512 (chunk 64) or 256 (chunk 128) segments, so the prefix step
+    runs with groups of 23 (16) segments, a short last group and the largest
+    number of images per workgroup; sampled rows and the final state against
+    the oracle."""
+    say("one head, many segments, chunk", chunk)
+    B, H, N = 1, 1, 32731
+    q, k, v = TI.make_qkv(97, B, H, N, 16, 64, dtype="bf16")
+    got, st = run_prefill(rsp, q, k, v, 3, 1.0, chunk, "bf16")
+    rows = sample_rows(B, H, N, 96, chunk)
+    ref = oracle.taylor_direct(q, k, v, 3, 1.0, rows=rows)
+    assert oracle.rel_err_rowwise(got.reshape(-1, 64)[rows], ref) <= TOL["bf16"]
+    S, T = (x.cpu().numpy().astype(np.float64) for x in rsp.state_views(st, B, H, 3))
+    A = oracle_state(k, v, 3)
+    assert np.abs(T - A[..., 64]).max() <= 2e-2 * np.abs(A[..., 64]).max()
+    assert np.abs(S - A[..., :64]).max() <= 2e-2 * np.abs(A[..., :64]).max()
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 4])
 def test_order_sweep_workload(rsp, n):
     """B=2, H=8, N=4096, float32, a=1: all rows against the oracle."""
