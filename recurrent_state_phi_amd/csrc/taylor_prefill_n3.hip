@@ -128,15 +128,14 @@ struct Shape : Waves<NW> {
   static_assert(TPW * NW == NTT, "token tiles per wave");
 };
 
-// LDS of one pass; the segment-sum pass (FULL = false) needs no state copy and
-// no q.
-template <int C, bool FULL>
+// LDS of the replay (every array double buffered by chunk parity).
+template <int C>
 struct Lds {
-  alignas(16) uint16_t S[FULL ? 2 : 1][FULL ? 64 : 1][kSS];  // S'^T copy (bf16), k-slot order, swizzled
-  alignas(16) uint16_t T[FULL ? 2 : 1][2][kNF];              // T' in k-slot order: bf16 high, low parts
-  alignas(16) uint16_t V[2][64][C + 8];                      // V^T (bf16), swizzled
-  alignas(16) float K[2][kKTRows][C + 4];                    // K^T (float)
-  alignas(16) uint16_t Q[FULL ? 2 : 1][FULL ? C : 1][kQS];   // q twice per row: [x | x]
+  alignas(16) uint16_t S[2][64][kSS];          // S'^T copy (bf16), k-slot order, swizzled
+  alignas(16) uint16_t T[2][2][kNF];           // T' in k-slot order: bf16 high, low parts
+  alignas(16) uint16_t V[2][64][C + 8];        // V^T (bf16), swizzled
+  alignas(16) float K[2][kKTRows][C + 4];      // K^T (float)
+  alignas(16) uint16_t Q[2][C][kQS];           // q twice per row: [x | x]
 };
 
 // The state of a workgroup in registers: 16x16 accumulator tiles of the owned
@@ -407,11 +406,10 @@ __device__ __forceinline__ void store_caller_state(float* img, float* st_S, floa
   for (int i = tid; i < kD3; i += Sh::NTHREADS) __builtin_nontemporal_store(img[kD3 * kDV + i], dt + i);
 }
 
-// ---- one pass over the chunks [t_begin, t_end) of sequence bh --------------
-// FULL = false: state update only (a += the segment's sum).
-// FULL = true: outputs of every token and the state update.
-template <int C, int NW_, bool FULL, typename TOUT>
-__device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& own, Acc& a, const uint16_t* __restrict__ q,
+// ---- the replay: one pass over the chunks [t_begin, t_end) of sequence bh ---
+// from the state a: the outputs of every token, and a += the segment's sum.
+template <int C, int NW_, typename TOUT>
+__device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc& a, const uint16_t* __restrict__ q,
                                              const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                              TOUT* __restrict__ o, int bh, int N, int t_begin, int t_end,
                                              float inv_a) {
@@ -429,7 +427,7 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
 
   // ---- global loads.  Wave w loads its own token tile 16w .. 16w + 15:
   //      lane (li, g) takes columns 8g..8g+7 and 32+8g..+7 of v for token li of
-  //      the tile, and k (g < 2) or q (g >= 2, FULL) dimensions 8(g%2)..+7: the
+  //      the tile, and k (g < 2) or q (g >= 2) dimensions 8(g%2)..+7: the
   //      natural row-major 16-byte pieces, which are exactly the A operand of
   //      the transposing MFMAs in `stage`.  Chunk c is loaded into register set
   //      c % DEPTH, DEPTH chunks ahead of its use.  Every load is issued
@@ -438,7 +436,7 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
   //      flight is the same on every path and the waits for them are exact.
   constexpr int TPW = Sh::TPW;
   constexpr int NPF = 3 * TPW;
-  constexpr int DEPTH = (FULL || C > 64) ? 2 : 4;  // register sets of prefetched loads
+  constexpr int DEPTH = 2;  // register sets of prefetched loads
   uint4 pf[DEPTH][NPF];
   auto issue_loads = [&](uint4 (&pfs)[NPF], int chunk) {
     const int c0 = t_begin + min(chunk, nchunks - 1) * C;
@@ -449,7 +447,7 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
       const size_t tok = base + min(16 * (w + NW * i) + li, last);
       pfs[3 * i] = *reinterpret_cast<const uint4*>(v + tok * kDV + 8 * g);
       pfs[3 * i + 1] = *reinterpret_cast<const uint4*>(v + tok * kDV + 32 + 8 * g);
-      const uint16_t* kq = (FULL && g >= 2) ? q + tok * kD + 8 * (g - 2) : k + tok * kD + 8 * (g & 1);
+      const uint16_t* kq = g >= 2 ? q + tok * kD + 8 * (g - 2) : k + tok * kD + 8 * (g & 1);
       pfs[3 * i + 2] = *reinterpret_cast<const uint4*>(kq);
     }
   };
@@ -494,49 +492,45 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
       // K^T (float): lane (li, g) gets dimension li of tokens 16tt + 4g + r
       const f32x4 dk = mfma_bf16_k32(ka, sel0, zero);
       *reinterpret_cast<f32x4*>(&L.K[b][li][16 * tt + 4 * g]) = dk;
-      if constexpr (FULL) {
-        if (g >= 2) {
-          // q / a, rounded to bfloat16 (exact for a = 1): then q.k comes out
-          // already divided by a, and the query features need no scaling
-          const uint4 raw = valid ? pfs[3 * i + 2] : z4;
-          const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
-          uint32_t sc[4];
+      if (g >= 2) {
+        // q / a, rounded to bfloat16 (exact for a = 1): then q.k comes out
+        // already divided by a, and the query features need no scaling
+        const uint4 raw = valid ? pfs[3 * i + 2] : z4;
+        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+        uint32_t sc[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sc[e] = pack2(lo_f(wd[e]) * inv_a, hi_f(wd[e]) * inv_a);
-          uint16_t* d = &L.Q[b][16 * tt + li][8 * (g - 2)];
-          *reinterpret_cast<uint2*>(d) = make_uint2(sc[0], sc[1]);
-          *reinterpret_cast<uint2*>(d + 4) = make_uint2(sc[2], sc[3]);
-          *reinterpret_cast<uint2*>(d + 16) = make_uint2(sc[0], sc[1]);
-          *reinterpret_cast<uint2*>(d + 20) = make_uint2(sc[2], sc[3]);
-        }
+        for (int e = 0; e < 4; ++e) sc[e] = pack2(lo_f(wd[e]) * inv_a, hi_f(wd[e]) * inv_a);
+        uint16_t* d = &L.Q[b][16 * tt + li][8 * (g - 2)];
+        *reinterpret_cast<uint2*>(d) = make_uint2(sc[0], sc[1]);
+        *reinterpret_cast<uint2*>(d + 4) = make_uint2(sc[2], sc[3]);
+        *reinterpret_cast<uint2*>(d + 16) = make_uint2(sc[0], sc[1]);
+        *reinterpret_cast<uint2*>(d + 20) = make_uint2(sc[2], sc[3]);
       }
     }
   };
   // bfloat16 copy of the state (k-slot order) and T for the next state read
   auto publish = [&](int b) {
-    if constexpr (FULL) {
 #pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        if (s == 1 && !HAS_S1) continue;
-        const int ks = kslot_of(own.ft[s], 4 * g);
+    for (int s = 0; s < 3; ++s) {
+      if (s == 1 && !HAS_S1) continue;
+      const int ks = kslot_of(own.ft[s], 4 * g);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          if (Sh::has(s, ct)) {
-            const int c = 16 * (s == 2 ? ctb + ct : ct) + li;
-            *reinterpret_cast<uint2*>(&L.S[b][c][ks]) =
-                make_uint2(pack2(acc[s][ct][0], acc[s][ct][1]), pack2(acc[s][ct][2], acc[s][ct][3]));
-          }
+      for (int ct = 0; ct < 4; ++ct) {
+        if (Sh::has(s, ct)) {
+          const int c = 16 * (s == 2 ? ctb + ct : ct) + li;
+          *reinterpret_cast<uint2*>(&L.S[b][c][ks]) =
+              make_uint2(pack2(acc[s][ct][0], acc[s][ct][1]), pack2(acc[s][ct][2], acc[s][ct][3]));
         }
-        if (li == 0 && (s < 2 || own_t2)) {
-          float hi[4], lo[4];
+      }
+      if (li == 0 && (s < 2 || own_t2)) {
+        float hi[4], lo[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            hi[r] = (float)f32_to_bf16(tacc[s][r]);
-            lo[r] = tacc[s][r] - hi[r];
-          }
-          *reinterpret_cast<uint2*>(&L.T[b][0][ks]) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
-          *reinterpret_cast<uint2*>(&L.T[b][1][ks]) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
+        for (int r = 0; r < 4; ++r) {
+          hi[r] = (float)f32_to_bf16(tacc[s][r]);
+          lo[r] = tacc[s][r] - hi[r];
         }
+        *reinterpret_cast<uint2*>(&L.T[b][0][ks]) = make_uint2(pack2(hi[0], hi[1]), pack2(hi[2], hi[3]));
+        *reinterpret_cast<uint2*>(&L.T[b][1][ks]) = make_uint2(pack2(lo[0], lo[1]), pack2(lo[2], lo[3]));
       }
     }
   };
@@ -556,32 +550,30 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
   // Outputs of the chunk computed last, stored at the start of the next
   // iteration (after that iteration's inputs are staged), so that the wait for
   // the staged loads never waits for fresh stores.
-  f32x4 yo[FULL ? TPW : 1][5];
+  f32x4 yo[TPW][5];
   int prev_t0 = -1, prev_nv = 0;
   auto store_prev = [&]() {
-    if constexpr (FULL) {
-      if (prev_t0 >= 0) {  // uniform
+    if (prev_t0 >= 0) {  // uniform
 #pragma unroll
-        for (int tw = 0; tw < TPW; ++tw) {
-          // o = Y[:d_v] / Y[d_v]: the normaliser of token li sits in rows 0 and 1
-          // of column tile 4 (lanes 0..15); every lane takes part in the shuffle
-          const float inv = 1.0f / __shfl(yo[tw][4][0] + yo[tw][4][1], li);
-          const int tok = 16 * (w + NW * tw) + li;
-          if (tok < prev_nv) {
-            TOUT* orow = o + ((size_t)bh * N + prev_t0 + tok) * kDV + 4 * g;
-            // non-temporal: the outputs are not read again by this kernel
-            if constexpr (std::is_same_v<TOUT, float>) {
+      for (int tw = 0; tw < TPW; ++tw) {
+        // o = Y[:d_v] / Y[d_v]: the normaliser of token li sits in rows 0 and 1
+        // of column tile 4 (lanes 0..15); every lane takes part in the shuffle
+        const float inv = 1.0f / __shfl(yo[tw][4][0] + yo[tw][4][1], li);
+        const int tok = 16 * (w + NW * tw) + li;
+        if (tok < prev_nv) {
+          TOUT* orow = o + ((size_t)bh * N + prev_t0 + tok) * kDV + 4 * g;
+          // non-temporal: the outputs are not read again by this kernel
+          if constexpr (std::is_same_v<TOUT, float>) {
 #pragma unroll
-              for (int ct = 0; ct < 4; ++ct)
-                __builtin_nontemporal_store(yo[tw][ct] * inv, reinterpret_cast<f32x4*>(orow + 16 * ct));
-            } else {
-              typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+            for (int ct = 0; ct < 4; ++ct)
+              __builtin_nontemporal_store(yo[tw][ct] * inv, reinterpret_cast<f32x4*>(orow + 16 * ct));
+          } else {
+            typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 #pragma unroll
-              for (int ct = 0; ct < 4; ++ct)
-                __builtin_nontemporal_store(u32x2{pack2(yo[tw][ct][0] * inv, yo[tw][ct][1] * inv),
-                                                  pack2(yo[tw][ct][2] * inv, yo[tw][ct][3] * inv)},
-                                            reinterpret_cast<u32x2*>(orow + 16 * ct));
-            }
+            for (int ct = 0; ct < 4; ++ct)
+              __builtin_nontemporal_store(u32x2{pack2(yo[tw][ct][0] * inv, yo[tw][ct][1] * inv),
+                                                pack2(yo[tw][ct][2] * inv, yo[tw][ct][3] * inv)},
+                                          reinterpret_cast<u32x2*>(orow + 16 * ct));
           }
         }
       }
@@ -676,114 +668,112 @@ __device__ __forceinline__ void segment_pass(Lds<C, FULL>& L, const Own<NW_>& ow
       }
     }
 
-    if constexpr (FULL) {
 #pragma unroll
-      for (int tw = 0; tw < TPW; ++tw) {
-        const int tt = w + NW * tw;  // token tile, wave-uniform
-        const int tok = 16 * tt + li;
+    for (int tw = 0; tw < TPW; ++tw) {
+      const int tt = w + NW * tw;  // token tile, wave-uniform
+      const int tok = 16 * tt + li;
 
-        // ---- diagonal block: P = tril(p_3(K Q^T / a)), lane holds P[token li][keys]
-        const bf16x4 bq = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&L.Q[b][tok][4 * g]));
-        // Every key tile of the chunk, without branches (the products are
-        // cheap, and straight-line code lets the key reads, the products and
-        // the polynomial of different key tiles overlap); tiles after the
-        // token tile are masked to zero, the diagonal tile causally (key
-        // 16 kt + 4g + r against token 16 tt + li).
-        bf16x8 pb[NKB];
+      // ---- diagonal block: P = tril(p_3(K Q^T / a)), lane holds P[token li][keys]
+      const bf16x4 bq = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&L.Q[b][tok][4 * g]));
+      // Every key tile of the chunk, without branches (the products are
+      // cheap, and straight-line code lets the key reads, the products and
+      // the polynomial of different key tiles overlap); tiles after the
+      // token tile are masked to zero, the diagonal tile causally (key
+      // 16 kt + 4g + r against token 16 tt + li).
+      bf16x8 pb[NKB];
 #pragma unroll
-        for (int kt = 0; kt < 2 * NKB; ++kt) {
-          const int key0 = 16 * kt + li;
-          const bf16x4 ak = {f32_to_bf16(L.K[b][4 * g][key0]), f32_to_bf16(L.K[b][4 * g + 1][key0]),
-                             f32_to_bf16(L.K[b][4 * g + 2][key0]), f32_to_bf16(L.K[b][4 * g + 3][key0])};
-          const f32x4 s = mfma_bf16_k16(ak, bq, f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int kt = 0; kt < 2 * NKB; ++kt) {
+        const int key0 = 16 * kt + li;
+        const bf16x4 ak = {f32_to_bf16(L.K[b][4 * g][key0]), f32_to_bf16(L.K[b][4 * g + 1][key0]),
+                           f32_to_bf16(L.K[b][4 * g + 2][key0]), f32_to_bf16(L.K[b][4 * g + 3][key0])};
+        const f32x4 s = mfma_bf16_k16(ak, bq, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = fmaf(s[r], fmaf(0.5f, s[r], 1.0f), 1.0f);  // s = q.k / a
-            const bool keep = kt < tt || (kt == tt && 4 * g + r <= li);
-            pb[kt >> 1][4 * (kt & 1) + r] = f32_to_bf16(keep ? p : 0.0f);
-          }
+        for (int r = 0; r < 4; ++r) {
+          const float p = fmaf(s[r], fmaf(0.5f, s[r], 1.0f), 1.0f);  // s = q.k / a
+          const bool keep = kt < tt || (kt == tt && 4 * g + r <= li);
+          pb[kt >> 1][4 * (kt & 1) + r] = f32_to_bf16(keep ? p : 0.0f);
         }
+      }
 
-        f32x4 y[5];
+      f32x4 y[5];
 #pragma unroll
-        for (int ct = 0; ct < 5; ++ct) y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // Y^T += [V, 1]^T P^T; row l of column tile ct is value column 16 ct + l, so
-        // lane (li, g) ends up with columns 16 ct + 4g .. 16 ct + 4g + 3 of token li
-        const uint32_t one2 = li == 0 ? 0x3F803F80u : 0u;
-        const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
+      for (int ct = 0; ct < 5; ++ct) y[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // Y^T += [V, 1]^T P^T; row l of column tile ct is value column 16 ct + l, so
+      // lane (li, g) ends up with columns 16 ct + 4g .. 16 ct + 4g + 3 of token li
+      const uint32_t one2 = li == 0 ? 0x3F803F80u : 0u;
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          if (2 * kb <= tt) {
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-              const int c = 16 * ct + li;
-              const uint2 v0 = *reinterpret_cast<const uint2*>(&L.V[b][c][swz(c, 32 * kb + 4 * g)]);
-              const uint2 v1 = *reinterpret_cast<const uint2*>(&L.V[b][c][swz(c, 32 * kb + 16 + 4 * g)]);
-              y[ct] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y)), pb[kb], y[ct]);
-            }
-            y[4] = mfma_bf16_k32(ones, pb[kb], y[4]);
-          }
-        }
-
-        // ---- state read: Y^T += S'^T phi'(q)^T, features built in registers
-        float yv[16], zv[16];
-        {
-          const uint16_t* qrow = &L.Q[b][tok][0];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint2 t2 = *reinterpret_cast<const uint2*>(qrow + 8 * h + 4 * e);
-            yv[4 * e] = lo_f(t2.x); yv[4 * e + 1] = hi_f(t2.x);
-            yv[4 * e + 2] = lo_f(t2.y); yv[4 * e + 3] = hi_f(t2.y);
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t t1 = *reinterpret_cast<const uint32_t*>(qrow + 8 * h + 2 * gh + 2 * e);
-            zv[2 * e] = lo_f(t1);
-            zv[2 * e + 1] = hi_f(t1);
-          }
-        }
-        // q is staged as q / a: the products y_s z_t already carry 2 alpha_2 = 1 / a^2,
-        // y_s carries alpha_1 = 1 / a
-        const float kb0f = gh == 0 ? 0.5f : 1.0f;  // diagonal tile: weight 1 instead of 2
-        const float cB = g >= 2 ? 1.0f : 0.0f, cC = g == 1 ? 1.0f : 0.0f;
-        constexpr int kD0[4] = {0, 1, 4, 5};
-#pragma unroll
-        for (int kb = 0; kb < 5; ++kb) {
-          float f[8];
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            if (kb < 4) {
-              f[s] = yv[s] * zv[(s + kD0[kb]) & 15];
-              if (kb == 0) f[s] *= kb0f;
-            } else {
-              // lane groups: 0 pairs at distance 8, 1 the constant (k-slot 0),
-              // 2 and 3 linear: one select and one product per feature
-              const float m = g == 0 ? zv[(s + 8) & 15] : cB;
-              f[s] = s == 0 ? fmaf(yv[s], m, cC) : yv[s] * m;
-            }
-          }
-          const bf16x8 bphi = __builtin_bit_cast(
-              bf16x8, make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])));
+      for (int kb = 0; kb < NKB; ++kb) {
+        if (2 * kb <= tt) {
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) {
-            const uint4 a4 = *reinterpret_cast<const uint4*>(&L.S[b][16 * ct + li][32 * kb + 8 * g]);
-            y[ct] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a4), bphi, y[ct]);
+            const int c = 16 * ct + li;
+            const uint2 v0 = *reinterpret_cast<const uint2*>(&L.V[b][c][swz(c, 32 * kb + 4 * g)]);
+            const uint2 v1 = *reinterpret_cast<const uint2*>(&L.V[b][c][swz(c, 32 * kb + 16 + 4 * g)]);
+            y[ct] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, make_uint4(v0.x, v0.y, v1.x, v1.y)), pb[kb], y[ct]);
           }
-          // normaliser: rows 0 / 1 of column tile 4 are T' (high / low bfloat16
-          // parts); rows 2..15 repeat them and are never read (so every lane
-          // reads one of two words per lane group: a broadcast)
-          const uint4 tA = *reinterpret_cast<const uint4*>(&L.T[b][li & 1][32 * kb + 8 * g]);
-          y[4] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, tA), bphi, y[4]);
+          y[4] = mfma_bf16_k32(ones, pb[kb], y[4]);
         }
-
-        // ---- epilogue (normalised and stored at the start of the next iteration,
-        //      when the products have long completed)
-#pragma unroll
-        for (int ct = 0; ct < 5; ++ct) yo[tw][ct] = y[ct];
       }
-      prev_t0 = t0;
-      prev_nv = nv;
+
+      // ---- state read: Y^T += S'^T phi'(q)^T, features built in registers
+      float yv[16], zv[16];
+      {
+        const uint16_t* qrow = &L.Q[b][tok][0];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint2 t2 = *reinterpret_cast<const uint2*>(qrow + 8 * h + 4 * e);
+          yv[4 * e] = lo_f(t2.x); yv[4 * e + 1] = hi_f(t2.x);
+          yv[4 * e + 2] = lo_f(t2.y); yv[4 * e + 3] = hi_f(t2.y);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t t1 = *reinterpret_cast<const uint32_t*>(qrow + 8 * h + 2 * gh + 2 * e);
+          zv[2 * e] = lo_f(t1);
+          zv[2 * e + 1] = hi_f(t1);
+        }
+      }
+      // q is staged as q / a: the products y_s z_t already carry 2 alpha_2 = 1 / a^2,
+      // y_s carries alpha_1 = 1 / a
+      const float kb0f = gh == 0 ? 0.5f : 1.0f;  // diagonal tile: weight 1 instead of 2
+      const float cB = g >= 2 ? 1.0f : 0.0f, cC = g == 1 ? 1.0f : 0.0f;
+      constexpr int kD0[4] = {0, 1, 4, 5};
+#pragma unroll
+      for (int kb = 0; kb < 5; ++kb) {
+        float f[8];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          if (kb < 4) {
+            f[s] = yv[s] * zv[(s + kD0[kb]) & 15];
+            if (kb == 0) f[s] *= kb0f;
+          } else {
+            // lane groups: 0 pairs at distance 8, 1 the constant (k-slot 0),
+            // 2 and 3 linear: one select and one product per feature
+            const float m = g == 0 ? zv[(s + 8) & 15] : cB;
+            f[s] = s == 0 ? fmaf(yv[s], m, cC) : yv[s] * m;
+          }
+        }
+        const bf16x8 bphi = __builtin_bit_cast(
+            bf16x8, make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])));
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const uint4 a4 = *reinterpret_cast<const uint4*>(&L.S[b][16 * ct + li][32 * kb + 8 * g]);
+          y[ct] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a4), bphi, y[ct]);
+        }
+        // normaliser: rows 0 / 1 of column tile 4 are T' (high / low bfloat16
+        // parts); rows 2..15 repeat them and are never read (so every lane
+        // reads one of two words per lane group: a broadcast)
+        const uint4 tA = *reinterpret_cast<const uint4*>(&L.T[b][li & 1][32 * kb + 8 * g]);
+        y[4] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, tA), bphi, y[4]);
+      }
+
+      // ---- epilogue (normalised and stored at the start of the next iteration,
+      //      when the products have long completed)
+#pragma unroll
+      for (int ct = 0; ct < 5; ++ct) yo[tw][ct] = y[ct];
     }
+    prev_t0 = t0;
+    prev_nv = nv;
 
     // the constant feature counted the padding tokens of a partial chunk:
     // take them out of its T' entry (row 8 of tile 8: lane 32, element 0)
@@ -985,7 +975,7 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
     TOUT* __restrict__ o, float* __restrict__ st_S, float* __restrict__ st_T, int* __restrict__ sync,
     float* __restrict__ sums, int N, int nseg, int cps, int gs, float inv_a, int wait_limit) {
   constexpr int NW = waves_for<C>();
-  using LB = Lds<C, true>;
+  using LB = Lds<C>;
   // The replay's chunk buffers, the sum pass's reduction area, and while the
   // final state is stored, a float [153 * 65] image of it in the caller's
   // layout.
@@ -1084,7 +1074,7 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
     }
   }
   // 3. replay from the prefix
-  segment_pass<C, NW, true, TOUT>(*reinterpret_cast<LB*>(lds_raw), own, pre, q, k, v, o, bh, N, t_begin, t_end, inv_a);
+  segment_pass<C, NW, TOUT>(*reinterpret_cast<LB*>(lds_raw), own, pre, q, k, v, o, bh, N, t_begin, t_end, inv_a);
   if (seg == nseg - 1) store_caller_state<NW>(img, st_S, st_T, bh, own, pre);
 }
 
