@@ -11,6 +11,9 @@
 // One 256-thread workgroup per (b, h).  Thread layout for the S block
 // [D][64]: 16 threads cover one 256-byte row with float4 accesses, 16 rows are
 // in flight per pass, so every wave reads four full rows per instruction.
+// For n <= 3 (at most 153 rows, 10 per thread) every thread issues all of its
+// state loads first, so they are in flight while q, k and v are fetched and
+// the features are formed; the larger n = 4 state is streamed in a loop.
 #include "taylor_device.h"
 #include "taylor_launch.h"
 
@@ -24,9 +27,42 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIN* __restrict_
                                                           float* __restrict__ S, float* __restrict__ T,
                                                           float inv_a) {
   constexpr int D = state_width(NT);
+  constexpr int kRows = (D + 15) / 16;      // rows per thread in the S block
+  constexpr bool kPrefetch = kRows <= 12;   // whole share held in registers
+  static_assert(!kPrefetch || D <= 256, "one feature row and one T entry per thread");
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  float* __restrict__ Sh = S + (size_t)bh * D * kDV;
+  float* __restrict__ Th = T + (size_t)bh * D;
+  const int c4 = tid & 15, rg = tid >> 4;
+
+  // Loads in issue order: this thread's element of q, k or v and its feature
+  // row (waited for first), then its share of the state (waited for last).
+  float xin = 0.f;
+  if (tid < kD) xin = Elem<TIN>::load(q, (size_t)bh * kD + tid);
+  else if (tid < 2 * kD) xin = Elem<TIN>::load(k, (size_t)bh * kD + tid - kD);
+  else if (tid < 2 * kD + kDV) xin = Elem<TIN>::load(v, (size_t)bh * kDV + tid - 2 * kD);
+  uint32_t fcode = 0;
+  float fweight = 0.f;
+  // Every load below is issued unconditionally (row indices past the state are
+  // clamped to its last row, and those values are not used), so the waits
+  // that follow count exactly the loads ahead of them.
+  const int frow = tid < D ? tid : D - 1;
+  if constexpr (kPrefetch) {
+    fcode = kFeatTab.code[frow];
+    fweight = kFeatTab.weight[frow];
+  }
+  float4 sv[kPrefetch ? kRows : 1];
+  float tv = 0.f;
+  if constexpr (kPrefetch) {
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int r = rg + 16 * i < D ? rg + 16 * i : D - 1;
+      sv[i] = *reinterpret_cast<const float4*>(Sh + (size_t)r * kDV + 4 * c4);
+    }
+    tv = Th[frow];
+  }
 
   __shared__ float xq[kD], xk[kD];
   __shared__ __align__(16) float vs[kDV];
@@ -34,42 +70,58 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIN* __restrict_
   __shared__ __align__(16) float red[4][kDV];
   __shared__ float red_den[4];
 
-  if (tid < kD) xq[tid] = Elem<TIN>::load(q, (size_t)bh * kD + tid);
-  else if (tid < 2 * kD) xk[tid - kD] = Elem<TIN>::load(k, (size_t)bh * kD + tid - kD);
-  else if (tid < 2 * kD + kDV) vs[tid - 2 * kD] = Elem<TIN>::load(v, (size_t)bh * kDV + tid - 2 * kD);
+  if (tid < kD) xq[tid] = xin;
+  else if (tid < 2 * kD) xk[tid - kD] = xin;
+  else if (tid < 2 * kD + kDV) vs[tid - 2 * kD] = xin;
   __syncthreads();
 
   const float a2 = inv_a * inv_a;
   const float4 alpha_q = make_float4(1.0f, inv_a, 0.5f * a2, a2 * inv_a * (1.0f / 6.0f));
   const float4 alpha_k = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-  for (int f = tid; f < D; f += 256) {
-    phq[f] = feature_value(kFeatTab, f, xq, alpha_q);
-    phk[f] = feature_value(kFeatTab, f, xk, alpha_k);
+  if constexpr (kPrefetch) {
+    if (tid < D) {
+      phq[tid] = feature_value(fcode, fweight, xq, alpha_q);
+      phk[tid] = feature_value(fcode, fweight, xk, alpha_k);
+    }
+  } else {
+    for (int f = tid; f < D; f += 256) {
+      phq[f] = feature_value(kFeatTab, f, xq, alpha_q);
+      phk[f] = feature_value(kFeatTab, f, xk, alpha_k);
+    }
   }
   __syncthreads();
 
   // S block: rank-one update then read, one pass over [D][64].
-  float* __restrict__ Sh = S + (size_t)bh * D * kDV;
-  const int c4 = tid & 15, rg = tid >> 4;
   const float4 vv = *reinterpret_cast<const float4*>(&vs[4 * c4]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int r = rg; r < D; r += 16) {
-    float4* p = reinterpret_cast<float4*>(Sh + (size_t)r * kDV + 4 * c4);
-    float4 s = *p;
+  auto update_read = [&](int r, float4 s) {
     const float pk = phk[r];
     s.x += pk * vv.x; s.y += pk * vv.y; s.z += pk * vv.z; s.w += pk * vv.w;
-    *p = s;
+    *reinterpret_cast<float4*>(Sh + (size_t)r * kDV + 4 * c4) = s;
     const float pq = phq[r];
     acc.x += pq * s.x; acc.y += pq * s.y; acc.z += pq * s.z; acc.w += pq * s.w;
-  }
-  // T block (the ones-column): same update and read.
-  float* __restrict__ Th = T + (size_t)bh * D;
+  };
   float dacc = 0.f;
-  for (int r = tid; r < D; r += 256) {
-    const float t = Th[r] + phk[r];
-    Th[r] = t;
-    dacc += phq[r] * t;
+  if constexpr (kPrefetch) {
+#pragma unroll
+    for (int i = 0; i < kRows; ++i) {
+      const int r = rg + 16 * i;
+      if (r < D) update_read(r, sv[i]);
+    }
+    // T block (the ones-column): same update and read.
+    if (tid < D) {
+      const float t = tv + phk[tid];
+      Th[tid] = t;
+      dacc = phq[tid] * t;
+    }
+  } else {
+#pragma unroll 4
+    for (int r = rg; r < D; r += 16) update_read(r, *reinterpret_cast<const float4*>(Sh + (size_t)r * kDV + 4 * c4));
+    for (int r = tid; r < D; r += 256) {
+      const float t = Th[r] + phk[r];
+      Th[r] = t;
+      dacc += phq[r] * t;
+    }
   }
 
   // Reduce the 16 row groups: 4 inside a wave (lanes 16 apart), then 4 waves.

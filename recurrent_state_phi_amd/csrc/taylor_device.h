@@ -66,15 +66,19 @@ constexpr FeatureTable make_feature_table() {
 // Value of stacked-basis row f at x (kD floats in LDS), scaled by the factor
 // of its order: alpha = {alpha_0, alpha_1, alpha_2, alpha_3} with
 // alpha_m = 1/(m! a^m) on the query side and all ones on the key side.
-__device__ inline float feature_value(const FeatureTable& tab, int f, const float* x, float4 alpha) {
-  const uint32_t c = tab.code[f];
+// Same, from a row's code and weight already read from the table.
+__device__ inline float feature_value(uint32_t c, float weight, const float* x, float4 alpha) {
   const int m = c & 3;
   const float am = m == 0 ? alpha.x : m == 1 ? alpha.y : m == 2 ? alpha.z : alpha.w;
-  float v = tab.weight[f] * am;
+  float v = weight * am;
   if (m >= 1) v *= x[(c >> 2) & 15];
   if (m >= 2) v *= x[(c >> 6) & 15];
   if (m >= 3) v *= x[(c >> 10) & 15];
   return v;
+}
+
+__device__ inline float feature_value(const FeatureTable& tab, int f, const float* x, float4 alpha) {
+  return feature_value(tab.code[f], tab.weight[f], x, alpha);
 }
 
 // Compile-time enumeration of rows [F0, F1) of the stacked basis for n <= 3,
