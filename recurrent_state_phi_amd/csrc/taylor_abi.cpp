@@ -33,7 +33,7 @@ int64_t binom(int64_t n, int64_t k) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Shapes compiled into this build.
-bool shape_supported(int d, int d_v, int n) { return d == taylor::kD && d_v == taylor::kDV && n >= 1 && n <= 4; }
+bool shape_supported(int d, int d_v, int n) { return d == taylor::kD && d_v == taylor::kDV && n >= 1 && n <= 6; }
 
 int check_dtypes(taylor_dtype in, taylor_dtype out) {
   if ((in != TAYLOR_F32 && in != TAYLOR_BF16) || (out != TAYLOR_F32 && out != TAYLOR_BF16))
@@ -80,7 +80,7 @@ int taylor_set_phase_events(hipEvent_t* events, int count) {
 
 int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStream_t stream) {
   if (B < 0 || H < 0) return fail(TAYLOR_EINVAL, "taylor_state_init: B and H must be >= 0");
-  if (!shape_supported(d, d_v, n)) return fail(TAYLOR_EUNSUPPORTED, "taylor_state_init: only d=16, d_v=64, n in 1..4");
+  if (!shape_supported(d, d_v, n)) return fail(TAYLOR_EUNSUPPORTED, "taylor_state_init: only d=16, d_v=64, n in 1..6");
   const size_t bytes = (size_t)B * H * taylor_state_numel(d, d_v, n) * sizeof(float);
   if (bytes == 0) return TAYLOR_OK;
   if (state == nullptr) return fail(TAYLOR_EINVAL, "taylor_state_init: state is NULL");
@@ -102,11 +102,11 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, fl
   if (B < 0 || H < 0 || N < 0) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: B, H, N must be >= 0");
   if (!(a > 0.0f) || a == __builtin_inff()) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: a must be finite and > 0");
   if (!shape_supported(d, d_v, n))
-    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: only d=16, d_v=64, n in 1..4 are built");
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: only d=16, d_v=64, n in 1..6 are built");
   const bool in_bf16 = in_dtype == TAYLOR_BF16, out_bf16 = out_dtype == TAYLOR_BF16;
   if (!taylor::prefill_supported(n, chunk, in_bf16))
     return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: unsupported (n, chunk, in_dtype): for n in 1..3 chunk "
-                                     "must be 32/64 (float32) or 32/64/128 (bfloat16); for n = 4 chunk 32/64");
+                                     "must be 32/64 (float32) or 32/64/128 (bfloat16); for n = 4..6 chunk 32/64");
   if ((int64_t)B * H == 0 || N == 0) return TAYLOR_OK;
   if (!q || !k || !v || !o || !state) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: NULL tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state))
@@ -135,7 +135,7 @@ int taylor_attn_decode(const void* q, const void* k, const void* v, void* o, flo
   if (B < 0 || H < 0) return fail(TAYLOR_EINVAL, "taylor_attn_decode: B and H must be >= 0");
   if (!(a > 0.0f) || a == __builtin_inff()) return fail(TAYLOR_EINVAL, "taylor_attn_decode: a must be finite and > 0");
   if (!shape_supported(d, d_v, n))
-    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_decode: only d=16, d_v=64, n in 1..4 are built");
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_decode: only d=16, d_v=64, n in 1..6 are built");
   if ((int64_t)B * H == 0) return TAYLOR_OK;
   if ((int64_t)B * H > (1 << 30)) return fail(TAYLOR_EINVAL, "taylor_attn_decode: B*H out of range");
   if (!q || !k || !v || !o || !state) return fail(TAYLOR_EINVAL, "taylor_attn_decode: NULL tensor pointer");

@@ -21,6 +21,35 @@ namespace taylor {
 
 __constant__ FeatureTable kFeatTab = make_feature_table();
 
+static __device__ WideFeatureTable kWideTab = make_wide_feature_table();
+
+// Sum of the partial reads of the 256 threads (16 row groups: 4 inside a wave,
+// lanes 16 apart, then the 4 waves) and o = y[:d_v] / y[d_v].  acc holds this
+// thread's 4 columns of y, dacc its part of the normaliser.
+template <typename TOUT>
+__device__ __forceinline__ void finish_read(float4 acc, float dacc, TOUT* __restrict__ o, int bh, int tid) {
+  __shared__ __align__(16) float red[4][kDV];
+  __shared__ float red_den[4];
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    acc.x += __shfl_xor(acc.x, off);
+    acc.y += __shfl_xor(acc.y, off);
+    acc.z += __shfl_xor(acc.z, off);
+    acc.w += __shfl_xor(acc.w, off);
+  }
+#pragma unroll
+  for (int off = 1; off <= 32; off <<= 1) dacc += __shfl_xor(dacc, off);
+  if (lane < 16) *reinterpret_cast<float4*>(&red[wave][4 * lane]) = acc;
+  if (lane == 0) red_den[wave] = dacc;
+  __syncthreads();
+  if (tid < kDV) {
+    const float y = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    const float den = red_den[0] + red_den[1] + red_den[2] + red_den[3];
+    Elem<TOUT>::store(o, (size_t)bh * kDV + tid, y / den);
+  }
+}
+
 template <int NT, typename TIN, typename TOUT>
 __global__ __launch_bounds__(256) void decode_step_kernel(const TIN* __restrict__ q, const TIN* __restrict__ k,
                                                           const TIN* __restrict__ v, TOUT* __restrict__ o,
@@ -32,7 +61,6 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIN* __restrict_
   static_assert(!kPrefetch || D <= 256, "one feature row and one T entry per thread");
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
   float* __restrict__ Sh = S + (size_t)bh * D * kDV;
   float* __restrict__ Th = T + (size_t)bh * D;
   const int c4 = tid & 15, rg = tid >> 4;
@@ -67,8 +95,6 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIN* __restrict_
   __shared__ float xq[kD], xk[kD];
   __shared__ __align__(16) float vs[kDV];
   __shared__ float phq[D], phk[D];
-  __shared__ __align__(16) float red[4][kDV];
-  __shared__ float red_den[4];
 
   if (tid < kD) xq[tid] = xin;
   else if (tid < 2 * kD) xk[tid - kD] = xin;
@@ -124,24 +150,53 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIN* __restrict_
     }
   }
 
-  // Reduce the 16 row groups: 4 inside a wave (lanes 16 apart), then 4 waves.
-#pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-    acc.x += __shfl_xor(acc.x, off);
-    acc.y += __shfl_xor(acc.y, off);
-    acc.z += __shfl_xor(acc.z, off);
-    acc.w += __shfl_xor(acc.w, off);
-  }
-#pragma unroll
-  for (int off = 1; off <= 32; off <<= 1) dacc += __shfl_xor(dacc, off);
-  if (lane < 16) *reinterpret_cast<float4*>(&red[wave][4 * lane]) = acc;
-  if (lane == 0) red_den[wave] = dacc;
+  finish_read<TOUT>(acc, dacc, o, bh, tid);
+}
+
+// Orders up to 5 (n = 5, 6: 4,845 or 20,349 rows, more than LDS holds as
+// feature vectors): the same one pass over the state, with each row's
+// features phi(k)_r and phi_hat(q)_r formed from the row table as the row is
+// streamed (the 16 threads of a row form the same two values).
+template <int NT, typename TIN, typename TOUT>
+__global__ __launch_bounds__(256) void decode_step_wide_kernel(const TIN* __restrict__ q, const TIN* __restrict__ k,
+                                                               const TIN* __restrict__ v, TOUT* __restrict__ o,
+                                                               float* __restrict__ S, float* __restrict__ T,
+                                                               float inv_a) {
+  constexpr int D = state_width(NT);
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  float* __restrict__ Sh = S + (size_t)bh * D * kDV;
+  float* __restrict__ Th = T + (size_t)bh * D;
+  const int c4 = tid & 15, rg = tid >> 4;
+
+  __shared__ float xq[kD], xk[kD];
+  __shared__ __align__(16) float vs[kDV];
+  if (tid < kD) xq[tid] = Elem<TIN>::load(q, (size_t)bh * kD + tid);
+  else if (tid < 2 * kD) xk[tid - kD] = Elem<TIN>::load(k, (size_t)bh * kD + tid - kD);
+  else if (tid < 2 * kD + kDV) vs[tid - 2 * kD] = Elem<TIN>::load(v, (size_t)bh * kDV + tid - 2 * kD);
   __syncthreads();
-  if (tid < kDV) {
-    const float y = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-    const float den = red_den[0] + red_den[1] + red_den[2] + red_den[3];
-    Elem<TOUT>::store(o, (size_t)bh * kDV + tid, y / den);
+
+  const Alphas al = query_alphas(inv_a);
+  const float4 vv = *reinterpret_cast<const float4*>(&vs[4 * c4]);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int r = rg; r < D; r += 16) {
+    const uint32_t c = kWideTab.code[r];
+    float4 s = *reinterpret_cast<const float4*>(Sh + (size_t)r * kDV + 4 * c4);
+    const float pk = wide_feature_value(c, xk, 1.0f);
+    const float pq = wide_feature_value(c, xq, alpha_of(al, c));
+    s.x += pk * vv.x; s.y += pk * vv.y; s.z += pk * vv.z; s.w += pk * vv.w;
+    *reinterpret_cast<float4*>(Sh + (size_t)r * kDV + 4 * c4) = s;
+    acc.x += pq * s.x; acc.y += pq * s.y; acc.z += pq * s.z; acc.w += pq * s.w;
   }
+  float dacc = 0.f;
+  for (int r = tid; r < D; r += 256) {
+    const uint32_t c = kWideTab.code[r];
+    const float t = Th[r] + wide_feature_value(c, xk, 1.0f);
+    Th[r] = t;
+    dacc += wide_feature_value(c, xq, alpha_of(al, c)) * t;
+  }
+  finish_read<TOUT>(acc, dacc, o, bh, tid);
 }
 
 template <int NT, typename TIN, typename TOUT>
@@ -149,9 +204,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
   const int D = state_width(NT);
   float* S = a.state;
   float* T = a.state + (size_t)a.BH * D * kDV;
-  hipLaunchKernelGGL((decode_step_kernel<NT, TIN, TOUT>), dim3(a.BH), dim3(256), 0, a.stream,
-                     static_cast<const TIN*>(a.q), static_cast<const TIN*>(a.k), static_cast<const TIN*>(a.v),
-                     static_cast<TOUT*>(a.o), S, T, 1.0f / a.a);
+  if constexpr (NT <= 4)
+    hipLaunchKernelGGL((decode_step_kernel<NT, TIN, TOUT>), dim3(a.BH), dim3(256), 0, a.stream,
+                       static_cast<const TIN*>(a.q), static_cast<const TIN*>(a.k), static_cast<const TIN*>(a.v),
+                       static_cast<TOUT*>(a.o), S, T, 1.0f / a.a);
+  else
+    hipLaunchKernelGGL((decode_step_wide_kernel<NT, TIN, TOUT>), dim3(a.BH), dim3(256), 0, a.stream,
+                       static_cast<const TIN*>(a.q), static_cast<const TIN*>(a.k), static_cast<const TIN*>(a.v),
+                       static_cast<TOUT*>(a.o), S, T, 1.0f / a.a);
   return hipGetLastError();
 }
 
@@ -169,6 +229,8 @@ hipError_t launch_decode(const DecodeArgs& a) {
     case 2: return launch_decode_n<2>(a);
     case 3: return launch_decode_n<3>(a);
     case 4: return launch_decode_n<4>(a);
+    case 5: return launch_decode_n<5>(a);
+    case 6: return launch_decode_n<6>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -81,6 +81,72 @@ __device__ inline float feature_value(const FeatureTable& tab, int f, const floa
   return feature_value(tab.code[f], tab.weight[f], x, alpha);
 }
 
+// Rows of the stacked basis for orders up to 5 (n <= 6, up to 20,349 rows),
+// for kernels that index rows at run time: bits 0-2 hold the order m, the
+// 4-bit fields from bit 3 the coordinates i_1 <= ... <= i_m, and bits 23-29
+// the multinomial m! / prod_i c_i! (at most 120), whose square root is the
+// weight of section 3.4.  Same row order as FeatureTable.
+constexpr int kMaxN = 6;
+struct WideFeatureTable {
+  uint32_t code[state_width(kMaxN)];
+};
+
+constexpr WideFeatureTable make_wide_feature_table() {
+  WideFeatureTable t{};
+  int f = 0;
+  for (int m = 0; m < kMaxN; ++m) {
+    int idx[kMaxN] = {};
+    while (true) {
+      uint32_t mult = 1;  // m! / prod_i c_i!, built up one coordinate at a time
+      for (int p = 0, run = 0; p < m; ++p) {
+        run = (p > 0 && idx[p] == idx[p - 1]) ? run + 1 : 1;
+        mult = mult * (p + 1) / run;
+      }
+      uint32_t c = (uint32_t)m | mult << 23;
+      for (int p = 0; p < m; ++p) c |= (uint32_t)idx[p] << (3 + 4 * p);
+      t.code[f++] = c;
+      int p = m - 1;  // next nondecreasing multi-index in lexicographic order
+      while (p >= 0 && idx[p] == kD - 1) --p;
+      if (p < 0) break;
+      ++idx[p];
+      for (int r = p + 1; r < m; ++r) idx[r] = idx[p];
+    }
+  }
+  return t;
+}
+
+// alpha_m = 1 / (m! a^m) for m = 0..5 (query side), given 1/a.
+struct Alphas {
+  float v[kMaxN];
+};
+__device__ inline Alphas query_alphas(float inv_a) {
+  Alphas al;
+  float am = 1.0f;
+  for (int m = 0; m < kMaxN; ++m) {
+    al.v[m] = am;
+    am = am * inv_a / (float)(m + 1);
+  }
+  return al;
+}
+
+// Value of a WideFeatureTable row at x (kD floats, e.g. in LDS), times `scale`
+// (alpha_m on the query side, 1 on the key side).
+__device__ inline float wide_feature_value(uint32_t c, const float* x, float scale) {
+  const int m = c & 7;
+  float v = scale * __fsqrt_rn((float)(c >> 23));
+#pragma unroll
+  for (int p = 0; p < kMaxN - 1; ++p)
+    if (p < m) v *= x[(c >> (3 + 4 * p)) & 15];
+  return v;
+}
+__device__ inline float alpha_of(const Alphas& al, uint32_t c) {
+  const int m = c & 7;
+  float r = al.v[0];
+#pragma unroll
+  for (int i = 1; i < kMaxN; ++i) r = m == i ? al.v[i] : r;
+  return r;
+}
+
 // Compile-time enumeration of rows [F0, F1) of the stacked basis for n <= 3,
 // calling fn(f, value) with f relative to F0.  Rows >= D give 0 (padding).
 // All indices are compile-time constants after unrolling, so x stays in

@@ -52,10 +52,12 @@ size_t prefill_n3_workspace_floats(int BH, int nseg);
 constexpr int kN3Magic = 0x54617933;
 constexpr int kN3ErrTimeout = 1;
 
-// n = 4, feature-blocked, chunk 32 or 64 (taylor_prefill_fb.hip), and the
-// floats of its per-block output workspace.
-hipError_t launch_prefill_n4(const PrefillArgs& a);
-size_t prefill_fb_output_floats(int BH, int N);
+// n = 4, 5, 6, feature-blocked, chunk 32 or 64 (taylor_prefill_fb.hip): the
+// launch, the number of 176-row feature blocks, and the floats of the
+// per-block output workspace.
+hipError_t launch_prefill_fb(const PrefillArgs& a);
+int prefill_fb_blocks(int n);
+size_t prefill_fb_output_floats(int BH, int N, int n);
 
 // Exclusive scan of the per-segment state sums in place, seeded with the
 // caller's state (taylor_prefill.hip).

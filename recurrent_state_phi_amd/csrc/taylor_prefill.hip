@@ -576,28 +576,29 @@ PrefillPlan plan_prefill(int BH, int N, int n, int chunk) {
   p.nchunks = (N + chunk - 1) / chunk;
   // Aim for at least 512 workgroups in the chunk kernel (two per CU on a
   // 256-CU part) when the heads alone do not provide them; 128-token chunks
-  // fill an LDS on their own, so for them aim at one workgroup per CU.  For n = 4 every
-  // segment is split into 6 feature blocks, one workgroup each.
-  const int blocks = n == 4 ? 6 : 1;
+  // fill an LDS on their own, so for them aim at one workgroup per CU.  For
+  // n >= 4 every segment is split into feature blocks (6, 28 or 116), one
+  // workgroup each.
+  const int blocks = n >= 4 ? prefill_fb_blocks(n) : 1;
   const int target = chunk >= 128 ? 256 : 512;
-  // n = 4: at most one round of workgroups (a second, partial round would
+  // n >= 4: at most one round of workgroups (a second, partial round would
   // cost as much as the first)
-  int nseg = n == 4 ? target / (BH * blocks) : (target + BH * blocks - 1) / (BH * blocks);
+  int nseg = n >= 4 ? target / (BH * blocks) : (target + BH * blocks - 1) / (BH * blocks);
   if (nseg < 1) nseg = 1;
   if (nseg > p.nchunks) nseg = p.nchunks;
   p.chunks_per_seg = (p.nchunks + nseg - 1) / nseg;
   p.nseg = (p.nchunks + p.chunks_per_seg - 1) / p.chunks_per_seg;
-  const int D = n == 1 ? state_width(1) : n == 2 ? state_width(2) : n == 3 ? state_width(3) : state_width(4);
+  const int D = state_width(n);
   p.workspace_floats = p.nseg > 1 ? (size_t)BH * p.nseg * D * (kDV + 1) : 0;
   // n = 3 with bfloat16 inputs takes the look-back kernel, whose workspace is
   // larger; the size does not depend on the input type, so cover both
   if (n == 3) p.workspace_floats = std::max(p.workspace_floats, prefill_n3_workspace_floats(BH, p.nseg));
-  if (n == 4) p.workspace_floats += prefill_fb_output_floats(BH, N);
+  if (n >= 4) p.workspace_floats += prefill_fb_output_floats(BH, N, n);
   return p;
 }
 
 bool prefill_supported(int n, int chunk, bool in_bf16) {
-  if (n == 4) return chunk == 32 || chunk == 64;
+  if (n >= 4 && n <= 6) return chunk == 32 || chunk == 64;
   if (n < 1 || n > 3) return false;
   if (in_bf16) return chunk == 32 || chunk == 64 || chunk == 128;
   return chunk == 32 || chunk == 64;
@@ -666,7 +667,9 @@ hipError_t launch_prefill(const PrefillArgs& a) {
     case 3:
       if (a.in_bf16 && (a.chunk == 64 || a.chunk == 128)) return launch_prefill_n3_bf16(a);
       return launch_prefill_n<3>(a);
-    case 4: return launch_prefill_n4(a);
+    case 4:
+    case 5:
+    case 6: return launch_prefill_fb(a);
   }
   return hipErrorInvalidValue;
 }

@@ -1,10 +1,11 @@
-// Chunked prefill for n = 4 (section 3.5 of "A Taylor-Series Route to
+// Chunked prefill for n = 4, 5, 6 (section 3.5 of "A Taylor-Series Route to
 // Linear-Time Transformers with a Fixed Number of Recurrent States",
-// arXiv 2610.20637), where the stacked state has D = 1 + 16 + 136 + 816 = 969
-// rows of d_v + 1 = 65 floats (252 KB per head): more than one workgroup can
-// hold in registers or LDS.
+// arXiv 2610.20637), where the stacked state has D = 969, 4,845 or 20,349
+// rows of d_v + 1 = 65 floats (252 KB, 1.26 MB, 5.3 MB per head): more than
+// one workgroup can hold in registers or LDS.
 //
-// The feature rows are therefore split into NFB blocks of 11 tiles (176 rows).
+// The feature rows are therefore split into NFB blocks of 11 tiles (176 rows;
+// 6, 28 or 116 blocks).
 // Everything the method does is linear in the state rows, so each block is an
 // independent problem:
 //   * segment sums, scan and replay run per (head, segment, feature block),
@@ -16,7 +17,8 @@
 //     o = sum_fb Y_fb[:d_v] / sum_fb Y_fb[d_v]  (Eq. (5)).
 // Arithmetic is float32 throughout (16x16x4 float32 MFMA); bfloat16 inputs are
 // widened when staged.  Feature rows follow the caller's layout (m ascending,
-// lexicographic multi-indices, sqrt-multinomial weights) and come from a table.
+// lexicographic multi-indices, sqrt-multinomial weights) and come from a table
+// (orders up to 3 for n = 4, up to 5 for n = 5, 6).
 //
 // Work inside one 256-thread workgroup (4 waves): wave w owns value columns
 // 16w..16w+15 of the block's state (11 accumulator tiles); the ones-column T of
@@ -31,15 +33,14 @@
 namespace taylor {
 namespace fb {
 
-constexpr int kN4 = 4;
-constexpr int kD4 = state_width(kN4);        // 969
 constexpr int kFT = 11;                      // feature tiles per block
 constexpr int kBF = 16 * kFT;                // 176 rows per block
-constexpr int kNFB = (kD4 + kBF - 1) / kBF;  // 6 blocks
 constexpr int kPS = kBF + 1;                 // feature row stride in LDS (odd: bank spread)
 constexpr int kNTW = (kFT + 3) / 4;          // T tiles per wave
+constexpr int blocks_of(int n) { return (state_width(n) + kBF - 1) / kBF; }  // 6, 28, 116
 
-__constant__ FeatureTable kTab = make_feature_table();
+__constant__ FeatureTable kTab = make_feature_table();           // n = 4 (orders <= 3)
+static __device__ WideFeatureTable kWideTab = make_wide_feature_table();  // n = 5, 6
 
 template <int C>
 struct Lds {
@@ -56,8 +57,17 @@ template <typename IT> __device__ __forceinline__ float ld(const IT* p, size_t i
 
 // p_4(y) = 1 + y + y^2/2 + y^3/6
 __device__ __forceinline__ float poly4(float y) { return 1.0f + y * (1.0f + y * (0.5f + y * (1.0f / 6.0f))); }
+// p_n(y) = sum_{m<n} y^m / m! by Horner's rule: 1 + y (1 + y/2 (1 + y/3 (...))).
+template <int NT>
+__device__ __forceinline__ float poly(float y) {
+  if constexpr (NT == 4) return poly4(y);
+  float r = 1.0f;
+#pragma unroll
+  for (int m = NT - 1; m >= 1; --m) r = 1.0f + y * r * (1.0f / (float)m);
+  return r;
+}
 
-template <int C, bool FULL, typename IT>
+template <int NT, int C, bool FULL, typename IT>
 __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const IT* __restrict__ q, const IT* __restrict__ k,
                                                          const IT* __restrict__ v, float* __restrict__ Yp,
                                                          const float* __restrict__ pre_S,
@@ -67,6 +77,8 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
                                                          float inv_a) {
   __shared__ __align__(16) Lds<C> L;
   constexpr int NTT = C / 16;
+  constexpr int kD4 = state_width(NT);  // rows of the stacked state
+  constexpr int kNFB = blocks_of(NT);
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: guards MFMAs
   const int fbk = blockIdx.x % kNFB;
@@ -107,6 +119,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
   const float a2 = inv_a * inv_a;
   const float4 alpha_q = make_float4(1.0f, inv_a, 0.5f * a2, a2 * inv_a * (1.0f / 6.0f));
   const float4 alpha_k = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+  const Alphas al = query_alphas(inv_a);
 
   for (int t0 = t_begin; t0 < t_end; t0 += C) {
     const int nv = min(C, t_end - t0);
@@ -139,9 +152,15 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
       const int tok = i / kBF, fl = i % kBF, f = F0 + fl;
       float fk = 0.0f, fq = 0.0f;
       if (f < kD4) {
-        fk = feature_value(kTab, f, &L.Xk[tok][0], alpha_k);
+        if constexpr (NT == 4) {
+          fk = feature_value(kTab, f, &L.Xk[tok][0], alpha_k);
+          if (FULL) fq = feature_value(kTab, f, &L.Xq[tok][0], alpha_q);
+        } else {
+          const uint32_t c = kWideTab.code[f];
+          fk = wide_feature_value(c, &L.Xk[tok][0], 1.0f);
+          if (FULL) fq = wide_feature_value(c, &L.Xq[tok][0], alpha_of(al, c));
+        }
         if (f == 0) fk = tok < nv ? 1.0f : 0.0f;  // the constant feature of a padding token is 0
-        if (FULL) fq = feature_value(kTab, f, &L.Xq[tok][0], alpha_q);
       }
       L.PhK[tok][fl] = fk;
       if (FULL) L.PhQ[tok][fl] = fq;
@@ -152,7 +171,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
         float s = 0.0f;
 #pragma unroll
         for (int j = 0; j < kD; ++j) s += L.Xq[tq][j] * L.Xk[tk][j];
-        L.P[tq][tk] = tk <= tq ? poly4(s * inv_a) : 0.0f;
+        L.P[tq][tk] = tk <= tq ? poly<NT>(s * inv_a) : 0.0f;
       }
     }
     __syncthreads();
@@ -237,7 +256,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
 }
 
 // o = sum over blocks of the numerators / sum of the normalisers (Eq. (5)).
-template <typename TOUT>
+template <int kNFB, typename TOUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Yp, TOUT* __restrict__ o,
                                                       size_t rows) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -254,8 +273,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   Elem<TOUT>::store(o, i, num / den);
 }
 
-template <int C, typename IT, typename TOUT>
+template <int NT, int C, typename IT, typename TOUT>
 hipError_t launch(const PrefillArgs& a) {
+  constexpr int kD4 = state_width(NT);
+  constexpr int kNFB = blocks_of(NT);
   const PrefillPlan& pl = a.plan;
   float* st_S = a.state;
   float* st_T = a.state + (size_t)a.BH * kD4 * kDV;
@@ -271,43 +292,55 @@ hipError_t launch(const PrefillArgs& a) {
   hipEvent_t* ev = a.events;
   if (ev) (void)hipEventRecord(ev[0], a.stream);
   if (pl.nseg > 1) {
-    hipLaunchKernelGGL((prefill_fb_kernel<C, false, IT>), dim3(a.BH * (pl.nseg - 1) * kNFB), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((prefill_fb_kernel<NT, C, false, IT>), dim3(a.BH * (pl.nseg - 1) * kNFB), dim3(256), 0, a.stream,
                        q, k, v, (float*)nullptr, (const float*)nullptr, (const float*)nullptr, 1, W_S, W_T, pl.nseg,
                        a.BH, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
     if (ev) (void)hipEventRecord(ev[1], a.stream);
     if (hipError_t e = launch_segment_scan(st_S, st_T, W_S, W_T, kD4, pl.nseg, a.BH, a.stream)) return e;
     if (ev) (void)hipEventRecord(ev[2], a.stream);
-    hipLaunchKernelGGL((prefill_fb_kernel<C, true, IT>), dim3(a.BH * pl.nseg * kNFB), dim3(256), 0, a.stream, q, k,
+    hipLaunchKernelGGL((prefill_fb_kernel<NT, C, true, IT>), dim3(a.BH * pl.nseg * kNFB), dim3(256), 0, a.stream, q, k,
                        v, Yp, W_S, W_T, pl.nseg, st_S, st_T, 1, a.BH, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
   } else {
     if (ev) {
       (void)hipEventRecord(ev[1], a.stream);
       (void)hipEventRecord(ev[2], a.stream);
     }
-    hipLaunchKernelGGL((prefill_fb_kernel<C, true, IT>), dim3(a.BH * kNFB), dim3(256), 0, a.stream, q, k, v, Yp,
+    hipLaunchKernelGGL((prefill_fb_kernel<NT, C, true, IT>), dim3(a.BH * kNFB), dim3(256), 0, a.stream, q, k, v, Yp,
                        st_S, st_T, 1, st_S, st_T, 1, a.BH, a.N, 1, pl.chunks_per_seg, inv_a);
   }
   const size_t rows = (size_t)a.BH * a.N;
-  hipLaunchKernelGGL((combine_kernel<TOUT>), dim3((unsigned)((rows * kDV + 255) / 256)), dim3(256), 0, a.stream, Yp,
+  hipLaunchKernelGGL((combine_kernel<kNFB, TOUT>), dim3((unsigned)((rows * kDV + 255) / 256)), dim3(256), 0, a.stream, Yp,
                      static_cast<TOUT*>(a.o), rows);
   if (ev) (void)hipEventRecord(ev[3], a.stream);
   return hipGetLastError();
 }
 
-template <int C>
+template <int NT, int C>
 hipError_t launch_c(const PrefillArgs& a) {
-  if (a.in_bf16) return a.out_bf16 ? launch<C, uint16_t, uint16_t>(a) : launch<C, uint16_t, float>(a);
-  return a.out_bf16 ? launch<C, float, uint16_t>(a) : launch<C, float, float>(a);
+  if (a.in_bf16) return a.out_bf16 ? launch<NT, C, uint16_t, uint16_t>(a) : launch<NT, C, uint16_t, float>(a);
+  return a.out_bf16 ? launch<NT, C, float, uint16_t>(a) : launch<NT, C, float, float>(a);
+}
+
+template <int NT>
+hipError_t launch_n(const PrefillArgs& a) {
+  switch (a.chunk) {
+    case 32: return launch_c<NT, 32>(a);
+    case 64: return launch_c<NT, 64>(a);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fb
 
-size_t prefill_fb_output_floats(int BH, int N) { return (size_t)fb::kNFB * BH * N * (kDV + 1); }
+int prefill_fb_blocks(int n) { return fb::blocks_of(n); }
 
-hipError_t launch_prefill_n4(const PrefillArgs& a) {
-  switch (a.chunk) {
-    case 32: return fb::launch_c<32>(a);
-    case 64: return fb::launch_c<64>(a);
+size_t prefill_fb_output_floats(int BH, int N, int n) { return (size_t)fb::blocks_of(n) * BH * N * (kDV + 1); }
+
+hipError_t launch_prefill_fb(const PrefillArgs& a) {
+  switch (a.n) {
+    case 4: return fb::launch_n<4>(a);
+    case 5: return fb::launch_n<5>(a);
+    case 6: return fb::launch_n<6>(a);
   }
   return hipErrorInvalidValue;
 }

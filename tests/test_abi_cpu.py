@@ -70,6 +70,19 @@ def test_workspace_sizing_n4(rsp):
     assert rsp.prefill_workspace_bytes(1, 1, 10, 4, 32) == 6 * 10 * 65 * 4  # one segment: outputs only
 
 
+@pytest.mark.parametrize("n,D,blocks", [(5, 4845, 28), (6, 20349, 116)])
+def test_workspace_sizing_high_orders(rsp, n, D, blocks):
+    """n = 5, 6: D rows split into 176-row feature blocks (28, 116); segment sums of D x 65
+    floats per segment plus one block of 65 floats per head-token per feature block."""
+    BH, N = 2, 333
+    ws = rsp.prefill_workspace_bytes(1, 2, N, n, 32)
+    out = blocks * BH * N * 65 * 4
+    nseg = (ws - out) // (BH * D * 65 * 4)
+    assert ws == out + nseg * BH * D * 65 * 4 and nseg > 1
+    assert BH * nseg * blocks <= 512  # at most one round of workgroups
+    assert rsp.prefill_workspace_bytes(64, 8, 100, n, 64) == blocks * 512 * 100 * 65 * 4  # one segment
+
+
 def test_workspace_sizing(rsp):
     # one segment per head when the heads alone fill the GPU: no workspace
     assert rsp.prefill_workspace_bytes(64, 8, 4096, 3, 64) == 0
@@ -101,8 +114,11 @@ def test_invalid_arguments_are_rejected_before_launch(rsp):
     assert b"NULL" in lib.taylor_last_error()
     assert _prefill_rc(lib, d=32) == -2                 # shape not built
     assert _prefill_rc(lib, d_v=128) == -2
-    assert _prefill_rc(lib, n=5) == -2
-    assert _prefill_rc(lib, n=4, chunk=128, ind=1) == -2   # n = 4: chunk 32 or 64
+    assert _prefill_rc(lib, n=7) == -2                  # orders up to 5 (n <= 6) are built
+    assert _prefill_rc(lib, n=0) == -2
+    assert _prefill_rc(lib, n=4, chunk=128, ind=1) == -2   # n = 4..6: chunk 32 or 64
+    assert _prefill_rc(lib, n=6, chunk=128, ind=1) == -2
+    assert _prefill_rc(lib, n=5) == -1                  # built: fails on the NULL pointers instead
     assert _prefill_rc(lib, chunk=48) == -2
     assert _prefill_rc(lib, chunk=128, ind=0) == -2     # float32 path stops at chunk 64
     assert _prefill_rc(lib, a=0.0) == -1
@@ -120,6 +136,8 @@ def test_invalid_arguments_are_rejected_before_launch(rsp):
     dec = lib.taylor_attn_decode
     assert dec(None, None, None, None, None, 1, 1, 16, 64, 3, 1.0, 0, 0, None) == -1
     assert dec(None, None, None, None, None, 1, 1, 16, 64, 9, 1.0, 0, 0, None) == -2
+    assert dec(None, None, None, None, None, 1, 1, 16, 64, 7, 1.0, 0, 0, None) == -2
+    assert dec(None, None, None, None, None, 1, 1, 16, 64, 6, 1.0, 0, 0, None) == -1
     assert dec(None, None, None, None, None, 0, 4, 16, 64, 3, 1.0, 0, 0, None) == 0
     assert lib.taylor_state_init(None, 1, 1, 16, 64, 3, None) == -1
     assert lib.taylor_state_init(None, 0, 1, 16, 64, 3, None) == 0

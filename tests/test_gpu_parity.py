@@ -130,6 +130,46 @@ def test_prefill_n4_short_and_split(rsp, N):
         assert np.abs(st.cpu().numpy() - st_w.cpu().numpy()).max() <= 1e-5 * np.abs(st_w.cpu().numpy()).max()
 
 
+@pytest.mark.parametrize("n", [5, 6])
+@pytest.mark.parametrize("dtype,chunk", [("f32", 32), ("f32", 64), ("bf16", 64)])
+def test_prefill_high_order_vs_oracle(rsp, n, dtype, chunk):
+    """n = 5, 6: the 4,845- or 20,349-row state in 28 or 116 feature blocks, each head cut
+    into several segments, ragged length, a = 0.8 (so every alpha_m = 1/(m! a^m) up to
+    m = 5 matters); outputs and final state against the oracle."""
+    say("prefill high order", n, dtype, chunk)
+    a = 0.8
+    q, k, v = TI.make_qkv(80 + n, 1, 2, 333, 16, 64, dtype=dtype)
+    ref = oracle.taylor_direct(q, k, v, n, a)
+    got, st = run_prefill(rsp, q, k, v, n, a, chunk, dtype)
+    assert oracle.rel_err_rowwise(got, ref) <= TOL["f32"]  # float32 arithmetic for both input types
+    S, T = (x.cpu().numpy().astype(np.float64) for x in rsp.state_views(st, 1, 2, n))
+    A = oracle_state(k, v, n)
+    scale = np.abs(A).max()
+    assert np.abs(S - A[..., :64]).max() <= 1e-5 * scale
+    assert np.abs(T - A[..., 64]).max() <= 1e-5 * scale
+
+
+@pytest.mark.parametrize("n", [5, 6])
+def test_high_order_split_and_decode(rsp, n):
+    """n = 5, 6: prefill in two calls equals one call, and a decode loop continuing from the
+    prefilled state matches the oracle (the state carries every order across calls)."""
+    say("high order split + decode", n)
+    a, N, t1, steps = 1.1, 150, 61, 12
+    q, k, v = TI.make_qkv(90 + n, 1, 2, N + steps, 16, 64)
+    ref = oracle.taylor_direct(q, k, v, n, a)
+    whole, st_w = run_prefill(rsp, q[:, :, :N], k[:, :, :N], v[:, :, :N], n, a, 32, "f32")
+    assert oracle.rel_err_rowwise(whole, ref[:, :, :N]) <= TOL["f32"]
+    a_out, st = run_prefill(rsp, q[:, :, :t1], k[:, :, :t1], v[:, :, :t1], n, a, 64, "f32")
+    b_out, st = run_prefill(rsp, q[:, :, t1:N], k[:, :, t1:N], v[:, :, t1:N], n, a, 32, "f32", state=st)
+    assert oracle.rel_err_rowwise(np.concatenate([a_out, b_out], axis=2), ref[:, :, :N]) <= TOL["f32"]
+    assert np.abs(st.cpu().numpy() - st_w.cpu().numpy()).max() <= 1e-5 * np.abs(st_w.cpu().numpy()).max()
+    qd, kd, vd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
+    outs = [rsp.decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), st, n, a)
+            for t in range(N, N + steps)]
+    got = torch.stack(outs, dim=2).cpu().numpy().astype(np.float64)
+    assert oracle.rel_err_rowwise(got, ref[:, :, N:]) <= TOL["f32"]
+
+
 @pytest.mark.parametrize("N", [1, 2, 15, 17, 33, 64, 65, 129])
 def test_prefill_short_lengths(rsp, N):
     say("prefill short", N)
@@ -205,7 +245,7 @@ def test_prefill_equals_decode_loop(rsp):
     assert np.abs(st.cpu().numpy() - st_p.cpu().numpy()).max() <= 1e-5 * np.abs(st_p.cpu().numpy()).max()
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_after_prefix(rsp, n, dtype):
     say("decode after prefix", n, dtype)
@@ -214,7 +254,7 @@ def test_decode_after_prefix(rsp, n, dtype):
     ref = oracle.taylor_direct(q, k, v, n, 1.0)
     st = rsp.new_state(B, H, n, device=DEV)
     qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
-    for t in range(N0):  # build the prefix by decode (also covers n = 4)
+    for t in range(N0):  # build the prefix by decode (also covers n >= 4)
         rsp.decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), st, n, 1.0)
     outs = [rsp.decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), st, n, 1.0)
             for t in range(N0, N0 + steps)]
