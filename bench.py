@@ -224,7 +224,7 @@ def order_sweep(torch, rsp, dev, reps=10):
     ref = torch.softmax(s, dim=-1) @ v.double()
     del s
     out = {}
-    for n in (1, 2, 3, 4):
+    for n in (1, 2, 3, 4, 5, 6):  # n = 5, 6 go beyond the configured sweep
         chunk = 64 if n < 4 else 32
         ws = torch.empty(max(rsp.prefill_workspace_bytes(B, H, N, n, chunk) // 4, 1), device=dev)
         o = torch.empty(B, H, N, c["d_v"], device=dev)
@@ -233,13 +233,41 @@ def order_sweep(torch, rsp, dev, reps=10):
             st = rsp.new_state(B, H, n, device=dev)
             rsp.prefill(q, k, v, st, n, c["a"], chunk=chunk, out=o, workspace=ws)
 
-        ms = _time_calls(torch, call, reps)
+        ms = _time_calls(torch, call, reps if n < 5 else 3, warmup=2 if n < 5 else 1)
         err = float((o.double() - ref).norm() / ref.norm())
         out[f"n{n}"] = {"tokens_per_s": B * N / (ms * 1e-3), "ms": ms, "chunk": chunk,
-                        "err_vs_softmax_frobenius": err}
+                        "state_rows": state_width(c["d"], n), "err_vs_softmax_frobenius": err}
         del ws, o
-    return {"workload": "order sweep B=2 H=8 N=4096 d=16 d_v=64 a=1, float32 q/k/v/out, normalised Gaussian q,k",
+    return {"workload": "order sweep B=2 H=8 N=4096 d=16 d_v=64 a=1, float32 q/k/v/out, normalised Gaussian q,k "
+                        "(n = 1..4 configured; n = 5, 6 added)",
             "per_n": out}
+
+
+def decode_high_order(torch, rsp, dev, n=5, steps=20):
+    """Decode at n = 5 (4,845 x 65 floats per head) for B=64, H=8: a 645 MB state,
+    larger than the Infinity Cache, streamed once per step.  The state starts empty
+    (its values do not change the cost of a step)."""
+    B, H, d, dv = DECODE["B"], DECODE["H"], DECODE["d"], DECODE["d_v"]
+    g = torch.Generator(device=dev).manual_seed(1007)
+    st = rsp.new_state(B, H, n, device=dev)
+    qs = torch.randn(steps, B, H, d, device=dev, generator=g)
+    ks = torch.randn(steps, B, H, d, device=dev, generator=g)
+    vs = torch.randn(steps, B, H, dv, device=dev, generator=g)
+    qs, ks = qs / qs.norm(dim=-1, keepdim=True), ks / ks.norm(dim=-1, keepdim=True)
+    out = torch.empty(B, H, dv, device=dev)
+    it = iter(range(10 ** 9))
+
+    def step():
+        s = next(it) % steps
+        rsp.decode(qs[s], ks[s], vs[s], st, n, DECODE["a"], out=out)
+
+    ms = _time_calls(torch, step, steps)
+    D = state_width(d, n)
+    bytes_step = B * H * (2 * 4.0 * D * (dv + 1) + 4.0 * (2 * d + 2 * dv))
+    return {"workload": f"decode B={B} H={H} n={n} fp32 state ({B * H * D * (dv + 1) * 4 / 1e6:.0f} MB), {steps} steps",
+            "us_per_step": ms * 1e3,
+            "roofline": {"bound": "hbm", "achieved": bytes_step / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
 def long_prefill(torch, rsp, dev, reps=5):
@@ -386,9 +414,10 @@ def main():
                          "algorithmic_bytes_per_step": dbytes},
         }
     if args.only == "all" and not args.no_secondary:
-        print("[bench] order sweep n=1..4 and long prefill", file=sys.stderr, flush=True)
+        print("[bench] order sweep n=1..6, long prefill, decode n=5", file=sys.stderr, flush=True)
         result["order_sweep"] = order_sweep(torch, rsp, dev)
         result["long_prefill"] = long_prefill(torch, rsp, dev)
+        result["decode_n5"] = decode_high_order(torch, rsp, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (float64 oracle, sampled rows)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(host)

@@ -14,8 +14,9 @@
  *
  * Conventions shared by every call
  * --------------------------------
- * - Supported shapes: d = 16, d_v = 64, n in {1, 2, 3, 4}.  Anything else
- *   returns TAYLOR_EUNSUPPORTED without launching.
+ * - Supported shapes: d = 16, d_v = 64, n in {1, ..., 6} (state widths
+ *   D = 1, 17, 153, 969, 4845, 20349; section 5.8 discusses orders up to 6).
+ *   Anything else returns TAYLOR_EUNSUPPORTED without launching.
  * - Tensors are dense, row-major, on the current HIP device:
  *     q, k : [B, H, N, d]       v, o : [B, H, N, d_v]      (decode: N = 1)
  *   element type given by `in_dtype` (q, k, v) and `out_dtype` (o).
@@ -82,7 +83,9 @@ int64_t taylor_state_numel(int d, int d_v, int n);
 int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStream_t stream);
 
 /* Bytes of device workspace taylor_attn_prefill needs for these sizes (0 when
- * the sequence fits one segment).  Host only; -1 cast to size_t on error. */
+ * the sequence fits one segment and n <= 3).  Host only; -1 cast to size_t on
+ * error.  For n >= 4 it includes one block of (d_v + 1) floats per head-token
+ * per 176-row feature block (6, 28, 116 blocks for n = 4, 5, 6). */
 size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n, int chunk);
 
 /* Chunked prefill (section 3.5): for every head and every t in [0, N)
@@ -95,13 +98,14 @@ size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n
  *   N >= 0 (N = 0 is a no-op), any N (the last chunk may be partial).
  *   a > 0 : temperature.
  *   chunk : n = 1..3: 32 or 64 for TAYLOR_F32 inputs; 32, 64 or 128 for
- *           TAYLOR_BF16.  n = 4: 32 or 64 for either input type.
+ *           TAYLOR_BF16.  n = 4..6: 32 or 64 for either input type.
  *   in_dtype selects the matrix-core arithmetic for n = 1..3: float32 inputs
  *   use float32 MFMA throughout; bfloat16 inputs use bfloat16 MFMA with
- *   float32 accumulation and a float32 state.  n = 4 computes in float32 for
- *   both input types (bfloat16 inputs are widened); its 969-row state is
- *   split into 6 blocks of 176 rows handled by separate workgroups, and the
- *   workspace then also holds each block's share of the outputs.
+ *   float32 accumulation and a float32 state.  n = 4..6 compute in float32
+ *   for both input types (bfloat16 inputs are widened); their 969-, 4845- or
+ *   20349-row states are split into 6, 28 or 116 blocks of 176 rows handled
+ *   by separate workgroups, and the workspace then also holds each block's
+ *   share of the outputs.
  *   workspace : device, at least taylor_prefill_workspace_bytes(...) bytes
  *   (may be NULL when that is 0); it is scratch, its contents are undefined
  *   afterwards (any contents are fine on entry).  o must not alias q, k, v or

@@ -179,17 +179,46 @@ __global__ __launch_bounds__(256) void decode_step_wide_kernel(const TIN* __rest
   const Alphas al = query_alphas(inv_a);
   const float4 vv = *reinterpret_cast<const float4*>(&vs[4 * c4]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
-  for (int r = rg; r < D; r += 16) {
-    const uint32_t c = kWideTab.code[r];
-    float4 s = *reinterpret_cast<const float4*>(Sh + (size_t)r * kDV + 4 * c4);
-    const float pk = wide_feature_value(c, xk, 1.0f);
-    const float pq = wide_feature_value(c, xq, alpha_of(al, c));
-    s.x += pk * vv.x; s.y += pk * vv.y; s.z += pk * vv.z; s.w += pk * vv.w;
-    *reinterpret_cast<float4*>(Sh + (size_t)r * kDV + 4 * c4) = s;
-    acc.x += pq * s.x; acc.y += pq * s.y; acc.z += pq * s.z; acc.w += pq * s.w;
+  // Rows in batches of kB per thread, two batches in flight: the loads of
+  // batch b + 1 are issued before batch b is used.  Every load is issued
+  // (row indices past the state clamped to its last row, values unused).
+  constexpr int kB = 8;
+  constexpr int kBatches = (D + 16 * kB - 1) / (16 * kB);
+  float4 cur[kB], nxt[kB];
+  uint32_t ccur[kB], cnxt[kB];
+  auto load_batch = [&](int b, float4 (&sv)[kB], uint32_t (&cv)[kB]) {
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const int r0 = rg + 16 * (b * kB + i);
+      const int r = r0 < D ? r0 : D - 1;
+      cv[i] = kWideTab.code[r];
+      sv[i] = *reinterpret_cast<const float4*>(Sh + (size_t)r * kDV + 4 * c4);
+    }
+  };
+  load_batch(0, cur, ccur);
+  for (int b = 0; b < kBatches; ++b) {
+    if (b + 1 < kBatches) load_batch(b + 1, nxt, cnxt);
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      const int r = rg + 16 * (b * kB + i);
+      if (r < D) {
+        float4 s = cur[i];
+        const uint32_t c = ccur[i];
+        const float pk = wide_feature_value(c, xk, 1.0f);
+        const float pq = wide_feature_value(c, xq, alpha_of(al, c));
+        s.x += pk * vv.x; s.y += pk * vv.y; s.z += pk * vv.z; s.w += pk * vv.w;
+        *reinterpret_cast<float4*>(Sh + (size_t)r * kDV + 4 * c4) = s;
+        acc.x += pq * s.x; acc.y += pq * s.y; acc.z += pq * s.z; acc.w += pq * s.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kB; ++i) {
+      cur[i] = nxt[i];
+      ccur[i] = cnxt[i];
+    }
   }
   float dacc = 0.f;
+#pragma unroll 4
   for (int r = tid; r < D; r += 256) {
     const uint32_t c = kWideTab.code[r];
     const float t = Th[r] + wide_feature_value(c, xk, 1.0f);
