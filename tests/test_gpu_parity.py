@@ -310,9 +310,10 @@ def test_one_head_many_segments(rsp, chunk):
     assert np.abs(S - A[..., :64]).max() <= 2e-2 * np.abs(A[..., :64]).max()
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 4])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6])
 def test_order_sweep_workload(rsp, n):
-    """B=2, H=8, N=4096, float32, a=1: all rows against the oracle."""
+    """B=2, H=8, N=4096, float32, a=1 (n = 5, 6 beyond the configured sweep, as timed):
+    sampled rows against the oracle."""
     say("order sweep", n)
     B, H, N = 2, 8, 4096
     q, k, v = TI.make_qkv(TI.SEEDS["order_sweep"], B, H, N, 16, 64)
@@ -337,6 +338,21 @@ def test_long_prefill_workload(rsp, variant):
     assert oracle.rel_err_rowwise(got.reshape(-1, 64)[rows], ref) <= TOL["bf16"]
     rep = oracle.convergence_report(q[:, :1, :256], k[:, :1, :256], v[:, :1, :256], 1.0, 6)
     assert rep["non_converged"] == (not norm)
+
+
+def test_decode_n5_workload(rsp):
+    """B=64 streams, H=8, n=5 (a 645 MB state, as timed): 20 steps from the empty state,
+    every output against the oracle."""
+    say("decode n=5 workload 64x8, 20 steps")
+    B, H, steps, n = 64, 8, 20, 5
+    q, k, v = TI.make_qkv(1007, B, H, steps, 16, 64)
+    ref = oracle.taylor_direct(q, k, v, n, 1.0)
+    st = rsp.new_state(B, H, n, device=DEV)
+    qd, kd, vd = to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32")
+    outs = [rsp.decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), st, n, 1.0)
+            for t in range(steps)]
+    got = torch.stack(outs, dim=2).cpu().numpy().astype(np.float64)
+    assert oracle.rel_err_rowwise(got, ref) <= TOL["f32"]
 
 
 def test_decode_workload_sampled(rsp):
