@@ -21,10 +21,14 @@
 // (orders up to 3 for n = 4, up to 5 for n = 5, 6).
 //
 // Work inside one 256-thread workgroup (4 waves): wave w owns value columns
-// 16w..16w+15 of the block's state (11 accumulator tiles); the ones-column T of
-// tile ft sits in column 0 of an extra accumulator tile owned by wave ft % 4.
-// Per chunk: stage q, k, v | features of the block and (fb = 0) the masked
-// polynomial block P into LDS | state read and update on MFMA.
+// 16w..16w+15 of the block's state (11 accumulator tiles), read and updated on
+// MFMA.  The ones-column T of the block (176 floats) is spread over the
+// threads, one row each, and its read (a dot product of the query features
+// with T, plus the row sums of P for block 0) and update (column sums of the
+// key features) are plain sums over all 256 threads, so every wave does the
+// same matrix work.
+// Per chunk: stage q, k, v and T | features of the block and (fb = 0) the
+// masked polynomial block P into LDS | state read and update.
 #include <type_traits>
 
 #include "taylor_device.h"
@@ -36,7 +40,6 @@ namespace fb {
 constexpr int kFT = 11;                      // feature tiles per block
 constexpr int kBF = 16 * kFT;                // 176 rows per block
 constexpr int kPS = kBF + 1;                 // feature row stride in LDS (odd: bank spread)
-constexpr int kNTW = (kFT + 3) / 4;          // T tiles per wave
 constexpr int blocks_of(int n) { return (state_width(n) + kBF - 1) / kBF; }  // 6, 28, 116
 
 __constant__ FeatureTable kTab = make_feature_table();           // n = 4 (orders <= 3)
@@ -90,9 +93,10 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
   const int t_end = min(N, t_begin + cps * C);
   const int col = 16 * w + li;
 
-  // ---- the segment's starting state (rows F0 .. F0 + 175 of the block)
+  // ---- the segment's starting state (rows F0 .. F0 + 175 of the block);
+  //      thread tid < 176 holds T of row F0 + tid
   f32x4 Sacc[kFT];
-  f32x4 Tacc[kNTW];
+  float treg = 0.0f;
   {
     const size_t slot = (size_t)bh * pre_slots + (pre_slots == 1 ? 0 : seg);
     const float* ps = (FULL && pre_S) ? pre_S + slot * kD4 * kDV : nullptr;
@@ -105,15 +109,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
         Sacc[ft][r] = ps ? ps[(size_t)min(row, kD4 - 1) * kDV + col] : 0.0f;
         if (row >= kD4) Sacc[ft][r] = 0.0f;
       }
-#pragma unroll
-    for (int j = 0; j < kNTW; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int ft = w + 4 * j;
-        const int row = F0 + 16 * ft + 4 * g + r;
-        const float t = pt ? pt[min(row, kD4 - 1)] : 0.0f;
-        Tacc[j][r] = (li == 0 && ft < kFT && row < kD4) ? t : 0.0f;
-      }
+    if (pt && tid < kBF && F0 + tid < kD4) treg = pt[F0 + tid];
   }
 
   const float a2 = inv_a * inv_a;
@@ -135,16 +131,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
       const int tok = i / kDV, j = i % kDV;
       L.V[tok][j] = tok < nv ? ld(v, (base + tok) * kDV + j) : 0.0f;
     }
-    if (FULL && li == 0) {
-#pragma unroll
-      for (int j = 0; j < kNTW; ++j) {
-        const int ft = w + 4 * j;
-        if (ft < kFT) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) L.Ts[16 * ft + 4 * g + r] = Tacc[j][r];
-        }
-      }
-    }
+    if (FULL && tid < kBF) L.Ts[tid] = treg;
     __syncthreads();
 
     // ---- features of the block (query side scaled by alpha_m), and P for block 0
@@ -178,53 +165,51 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
 
     // ---- this block's share of the outputs: Y = phi_hat(Q)_fb S_fb (+ P [V, 1])
     if constexpr (FULL) {
-      const float one = li == 0 ? 1.0f : 0.0f;
+      float* yrow = Yp + ((size_t)fbk * BH * N + base) * (kDV + 1);
 #pragma unroll
       for (int mt = 0; mt < NTT; ++mt) {
         const int tok = 16 * mt + li;
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
-        f32x4 yd = {0.f, 0.f, 0.f, 0.f};
-        const bool mine = (mt & 3) == w;  // wave-uniform
 #pragma unroll
         for (int ft = 0; ft < kFT; ++ft)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float a = L.PhQ[tok][16 * ft + 4 * g + r];
-            y = mfma_f32_k4(a, Sacc[ft][r], y);
-            if (mine) yd = mfma_f32_k4(a, li == 0 ? L.Ts[16 * ft + 4 * g + r] : 0.0f, yd);
-          }
+          for (int r = 0; r < 4; ++r) y = mfma_f32_k4(L.PhQ[tok][16 * ft + 4 * g + r], Sacc[ft][r], y);
         if (fbk == 0) {  // uniform
-          for (int st = 0; st < C / 4; ++st) {
-            const float a = L.P[tok][4 * st + g];
-            y = mfma_f32_k4(a, L.V[4 * st + g][col], y);
-            if (mine) yd = mfma_f32_k4(a, one, yd);
-          }
+          for (int st = 0; st < C / 4; ++st) y = mfma_f32_k4(L.P[tok][4 * st + g], L.V[4 * st + g][col], y);
         }
         // lane holds Y[token 16mt + 4g + r][col]
-        float* yrow = Yp + ((size_t)fbk * BH * N + base) * (kDV + 1);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * mt + 4 * g + r;
-          if (t < nv) {
-            yrow[(size_t)t * (kDV + 1) + col] = y[r];
-            if (mine && li == 0) yrow[(size_t)t * (kDV + 1) + kDV] = yd[r];
-          }
+          if (t < nv) yrow[(size_t)t * (kDV + 1) + col] = y[r];
         }
       }
+      // the block's share of the normaliser: phi_hat(q)_fb . T_fb, plus the row
+      // sum of P for block 0; 256 / C consecutive threads per token
+      constexpr int TPT = 256 / C;
+      const int tok = tid / TPT, part = tid % TPT;
+      float yd = 0.0f;
+      for (int fl = part; fl < kBF; fl += TPT) yd += L.PhQ[tok][fl] * L.Ts[fl];
+      if (fbk == 0) {  // uniform
+        for (int tk = part; tk < C; tk += TPT) yd += L.P[tok][tk];
+      }
+#pragma unroll
+      for (int off = 1; off < TPT; off <<= 1) yd += __shfl_xor(yd, off);
+      if (part == 0 && tok < nv) yrow[(size_t)tok * (kDV + 1) + kDV] = yd;
     }
 
-    // ---- state update: S_fb += phi(K)_fb^T V, T_fb += phi(K)_fb^T 1
-    {
-      const float one = li == 0 ? 1.0f : 0.0f;
-      for (int st = 0; st < C / 4; ++st) {
-        const float b = L.V[4 * st + g][col];
+    // ---- state update: S_fb += phi(K)_fb^T V (MFMA), T_fb += phi(K)_fb^T 1
+    //      (padding tokens have zero features, the constant one included)
+    for (int st = 0; st < C / 4; ++st) {
+      const float b = L.V[4 * st + g][col];
 #pragma unroll
-        for (int ft = 0; ft < kFT; ++ft) {
-          const float a = L.PhK[4 * st + g][16 * ft + li];
-          Sacc[ft] = mfma_f32_k4(a, b, Sacc[ft]);
-          if ((ft & 3) == w) Tacc[ft >> 2] = mfma_f32_k4(a, one, Tacc[ft >> 2]);
-        }
-      }
+      for (int ft = 0; ft < kFT; ++ft) Sacc[ft] = mfma_f32_k4(L.PhK[4 * st + g][16 * ft + li], b, Sacc[ft]);
+    }
+    if (tid < kBF) {
+      float ts = 0.0f;
+#pragma unroll 8
+      for (int tok = 0; tok < C; ++tok) ts += L.PhK[tok][tid];
+      treg += ts;
     }
     __syncthreads();
   }
@@ -242,16 +227,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
         const int row = F0 + 16 * ft + 4 * g + r;
         if (row < kD4) ds[(size_t)row * kDV + col] = Sacc[ft][r];
       }
-    if (li == 0) {
-#pragma unroll
-      for (int j = 0; j < kNTW; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int ft = w + 4 * j;
-          const int row = F0 + 16 * ft + 4 * g + r;
-          if (ft < kFT && row < kD4) dt[row] = Tacc[j][r];
-        }
-    }
+    if (tid < kBF && F0 + tid < kD4) dt[F0 + tid] = treg;
   }
 }
 
