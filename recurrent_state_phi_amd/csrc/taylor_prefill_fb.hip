@@ -28,7 +28,13 @@
 // key features) are plain sums over all 256 threads, so every wave does the
 // same matrix work.
 // Per chunk: stage q, k, v and T | features of the block and (fb = 0) the
-// masked polynomial block P into LDS | state read and update.
+// masked polynomial block P into LDS | state read and update.  Thread
+// fl < 176 owns row F0 + fl of the block for the whole kernel: it decodes the
+// row's table entry once (coordinates, weight, alpha_m) and forms that row's
+// feature for every token of every chunk as weight * x_i1 * ... * x_i(n-1),
+// unused coordinate slots pointing at a column that holds 1.  The next
+// chunk's q, k, v are loaded into registers while the current one is
+// computed.
 #include <type_traits>
 
 #include "taylor_device.h"
@@ -47,9 +53,9 @@ static __device__ WideFeatureTable kWideTab = make_wide_feature_table();  // n =
 
 template <int C>
 struct Lds {
-  float Xq[C][kD];
-  float Xk[C][kD];
-  float V[C][kDV + 4];
+  float Xq[C][kD + 1];  // column kD: 1 (the factor of unused coordinate slots)
+  float Xk[C][kD + 1];  // column kD: 1, or 0 for a padding token
+  float V[C][kDV + 16];  // row stride 80 floats: the 4 lane groups of an MFMA operand read hit different banks
   float PhQ[C][kPS];
   float PhK[C][kPS];
   float P[C][C + 1];
@@ -112,45 +118,94 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
     if (pt && tid < kBF && F0 + tid < kD4) treg = pt[F0 + tid];
   }
 
-  const float a2 = inv_a * inv_a;
-  const float4 alpha_q = make_float4(1.0f, inv_a, 0.5f * a2, a2 * inv_a * (1.0f / 6.0f));
-  const float4 alpha_k = make_float4(1.0f, 1.0f, 1.0f, 1.0f);
-  const Alphas al = query_alphas(inv_a);
+  // ---- this thread's feature row (tid < 176): coordinates (kD = the column
+  //      of ones for unused slots), key-side weight and query-side weight
+  constexpr int NF = NT - 1;  // coordinate slots: orders up to n - 1
+  int fidx[NF];
+  float wk = 0.0f, wq = 0.0f;  // 0 for rows past the state and threads >= 176
+  {
+    const int f = F0 + tid;
+    const bool valid = tid < kBF && f < kD4;
+    const int fr = valid ? f : 0;
+    if constexpr (NT == 4) {
+      const uint32_t c = kTab.code[fr];
+      const int m = c & 3;
+      const float a2 = inv_a * inv_a;
+      const float am = m == 0 ? 1.0f : m == 1 ? inv_a : m == 2 ? 0.5f * a2 : a2 * inv_a * (1.0f / 6.0f);
+#pragma unroll
+      for (int p = 0; p < NF; ++p) fidx[p] = p < m ? (int)((c >> (2 + 4 * p)) & 15) : kD;
+      const float wt = kTab.weight[fr];
+      wk = valid ? wt : 0.0f;
+      wq = valid ? wt * am : 0.0f;
+    } else {
+      const uint32_t c = kWideTab.code[fr];
+      const int m = c & 7;
+#pragma unroll
+      for (int p = 0; p < NF; ++p) fidx[p] = p < m ? (int)((c >> (3 + 4 * p)) & 15) : kD;
+      const float wt = __fsqrt_rn((float)(c >> 23));
+      wk = valid ? wt : 0.0f;
+      wq = valid ? alpha_of(query_alphas(inv_a), c) * wt : 0.0f;
+    }
+  }
+
+  // ---- loads of one chunk into registers (token indices clamped into the
+  //      chunk; values of padding tokens are replaced when staged)
+  constexpr int NLK = C * kD / 256, NLV = C * kDV / 256;
+  float rk[NLK], rq[NLK], rv[NLV];
+  auto fetch = [&](int t0n) {
+    const int last = min(C, t_end - t0n) - 1;
+    const size_t basen = (size_t)bh * N + t0n;
+#pragma unroll
+    for (int e = 0; e < NLK; ++e) {
+      const int i = tid + 256 * e, tok = min(i / kD, last), j = i % kD;
+      rk[e] = ld(k, (basen + tok) * kD + j);
+      if (FULL) rq[e] = ld(q, (basen + tok) * kD + j);
+    }
+#pragma unroll
+    for (int e = 0; e < NLV; ++e) {
+      const int i = tid + 256 * e, tok = min(i / kDV, last), j = i % kDV;
+      rv[e] = ld(v, (basen + tok) * kDV + j);
+    }
+  };
+  if (t_begin < t_end) fetch(t_begin);  // uniform
 
   for (int t0 = t_begin; t0 < t_end; t0 += C) {
     const int nv = min(C, t_end - t0);
     const size_t base = (size_t)bh * N + t0;
 
     // ---- stage q, k, v (float), zero for padding tokens; publish T of the block
-    for (int i = tid; i < C * kD; i += 256) {
-      const int tok = i / kD, j = i % kD;
-      L.Xk[tok][j] = tok < nv ? ld(k, (base + tok) * kD + j) : 0.0f;
-      if (FULL) L.Xq[tok][j] = tok < nv ? ld(q, (base + tok) * kD + j) : 0.0f;
+#pragma unroll
+    for (int e = 0; e < NLK; ++e) {
+      const int i = tid + 256 * e, tok = i / kD, j = i % kD;
+      L.Xk[tok][j] = tok < nv ? rk[e] : 0.0f;
+      if (FULL) L.Xq[tok][j] = tok < nv ? rq[e] : 0.0f;
     }
-    for (int i = tid; i < C * kDV; i += 256) {
-      const int tok = i / kDV, j = i % kDV;
-      L.V[tok][j] = tok < nv ? ld(v, (base + tok) * kDV + j) : 0.0f;
+#pragma unroll
+    for (int e = 0; e < NLV; ++e) {
+      const int i = tid + 256 * e, tok = i / kDV, j = i % kDV;
+      L.V[tok][j] = tok < nv ? rv[e] : 0.0f;
+    }
+    if (tid < C) {
+      L.Xk[tid][kD] = tid < nv ? 1.0f : 0.0f;  // the constant feature of a padding token is 0
+      if (FULL) L.Xq[tid][kD] = 1.0f;
     }
     if (FULL && tid < kBF) L.Ts[tid] = treg;
+    if (t0 + C < t_end) fetch(t0 + C);  // uniform
     __syncthreads();
 
     // ---- features of the block (query side scaled by alpha_m), and P for block 0
-    for (int i = tid; i < C * kBF; i += 256) {
-      const int tok = i / kBF, fl = i % kBF, f = F0 + fl;
-      float fk = 0.0f, fq = 0.0f;
-      if (f < kD4) {
-        if constexpr (NT == 4) {
-          fk = feature_value(kTab, f, &L.Xk[tok][0], alpha_k);
-          if (FULL) fq = feature_value(kTab, f, &L.Xq[tok][0], alpha_q);
-        } else {
-          const uint32_t c = kWideTab.code[f];
-          fk = wide_feature_value(c, &L.Xk[tok][0], 1.0f);
-          if (FULL) fq = wide_feature_value(c, &L.Xq[tok][0], alpha_of(al, c));
+    if (tid < kBF) {
+#pragma unroll 4
+      for (int tok = 0; tok < C; ++tok) {
+        float fk = wk, fq = wq;
+#pragma unroll
+        for (int p = 0; p < NF; ++p) {
+          fk *= L.Xk[tok][fidx[p]];
+          if (FULL) fq *= L.Xq[tok][fidx[p]];
         }
-        if (f == 0) fk = tok < nv ? 1.0f : 0.0f;  // the constant feature of a padding token is 0
+        L.PhK[tok][tid] = fk;
+        if (FULL) L.PhQ[tok][tid] = fq;
       }
-      L.PhK[tok][fl] = fk;
-      if (FULL) L.PhQ[tok][fl] = fq;
     }
     if (FULL && fbk == 0) {
       for (int i = tid; i < C * C; i += 256) {
