@@ -45,7 +45,7 @@ namespace fb {
 
 constexpr int kFT = 11;                      // feature tiles per block
 constexpr int kBF = 16 * kFT;                // 176 rows per block
-constexpr int kPS = kBF + 1;                 // feature row stride in LDS (odd: bank spread)
+constexpr int kPS = kBF + 4;                 // feature row stride in LDS (16-byte aligned rows)
 constexpr int blocks_of(int n) { return (state_width(n) + kBF - 1) / kBF; }  // 6, 28, 116
 
 __constant__ FeatureTable kTab = make_feature_table();           // n = 4 (orders <= 3)
@@ -207,13 +207,20 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
         if (FULL) L.PhQ[tok][tid] = fq;
       }
     }
-    if (FULL && fbk == 0) {
-      for (int i = tid; i < C * C; i += 256) {
-        const int tq = i / C, tk = i % C;
-        float s = 0.0f;
+    if (FULL && fbk == 0) {  // uniform
+      // scores Q K^T on the matrix cores, one 16x16 tile per wave at a time;
+      // the lane holds S[16a + 4g + r][16b + li]
+      for (int tile = w; tile < NTT * NTT; tile += 4) {
+        const int ta = tile / NTT, tb = tile % NTT;
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < kD; ++j) s += L.Xq[tq][j] * L.Xk[tk][j];
-        L.P[tq][tk] = tk <= tq ? poly<NT>(s * inv_a) : 0.0f;
+        for (int s4 = 0; s4 < kD / 4; ++s4)
+          sc = mfma_f32_k4(L.Xq[16 * ta + li][4 * s4 + g], L.Xk[16 * tb + li][4 * s4 + g], sc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tq = 16 * ta + 4 * g + r, tk = 16 * tb + li;
+          L.P[tq][tk] = tk <= tq ? poly<NT>(sc[r] * inv_a) : 0.0f;
+        }
       }
     }
     __syncthreads();
@@ -226,9 +233,11 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
         const int tok = 16 * mt + li;
         f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ft = 0; ft < kFT; ++ft)
+        for (int ft = 0; ft < kFT; ++ft) {
+          const f32x4 a4 = *reinterpret_cast<const f32x4*>(&L.PhQ[tok][16 * ft + 4 * g]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) y = mfma_f32_k4(L.PhQ[tok][16 * ft + 4 * g + r], Sacc[ft][r], y);
+          for (int r = 0; r < 4; ++r) y = mfma_f32_k4(a4[r], Sacc[ft][r], y);
+        }
         if (fbk == 0) {  // uniform
           for (int st = 0; st < C / 4; ++st) y = mfma_f32_k4(L.P[tok][4 * st + g], L.V[4 * st + g][col], y);
         }
