@@ -170,6 +170,46 @@ def test_high_order_split_and_decode(rsp, n):
     assert oracle.rel_err_rowwise(got, ref[:, :, N:]) <= TOL["f32"]
 
 
+# ---------------------------------------------------------------------------
+# closed forms of Eq. (1)-(2) that fix the outputs without the oracle
+# ---------------------------------------------------------------------------
+def running_mean(v):
+    v = v.astype(np.float64)
+    return np.cumsum(v, axis=-2) / np.arange(1, v.shape[-2] + 1)[:, None]
+
+
+@pytest.mark.parametrize("dtype,chunk", [("f32", 32), ("f32", 64), ("bf16", 64), ("bf16", 128)])
+def test_n1_is_running_mean(rsp, dtype, chunk):
+    """n = 1: the truncated kernel is the constant 1, so o_t is the mean of v_0..v_t for any
+    q, k and a; several segments per head, ragged length."""
+    say("n=1 running mean", dtype, chunk)
+    q, k, v = TI.make_qkv(120, 1, 2, 1500, 16, 64, dtype=dtype)
+    got, _ = run_prefill(rsp, q, k, v, 1, 0.7, chunk, dtype)
+    assert oracle.rel_err_rowwise(got, running_mean(v)) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("n,dtype,chunk", [(2, "f32", 64), (3, "f32", 32), (3, "bf16", 64), (3, "bf16", 128),
+                                           (4, "f32", 32), (5, "bf16", 64), (6, "f32", 32)])
+def test_equal_keys_is_running_mean(rsp, n, dtype, chunk):
+    """All keys equal: every weight p_n(q_t.k / a) of row t is the same (and positive at
+    a = 2 for unit vectors), so o_t is the mean of v_0..v_t for any n and q; decode steps
+    with the same key continue it.  Covers the timed n = 3 bfloat16 kernel across 47
+    segments per head."""
+    say("equal keys running mean", n, dtype, chunk)
+    N, steps = 3000, 4
+    q, k, v = TI.make_qkv(121, 1, 2, N + steps, 16, 64, dtype=dtype)
+    k = np.ascontiguousarray(np.broadcast_to(k[:, :, :1], k.shape))
+    ref = running_mean(v)
+    tol = TOL["f32"] if (n >= 4 or dtype == "f32") else TOL["bf16"]
+    got, st = run_prefill(rsp, q[:, :, :N], k[:, :, :N], v[:, :, :N], n, 2.0, chunk, dtype)
+    assert oracle.rel_err_rowwise(got, ref[:, :, :N]) <= tol
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    outs = [rsp.decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), st, n, 2.0)
+            for t in range(N, N + steps)]
+    dec = torch.stack(outs, dim=2).cpu().numpy().astype(np.float64)
+    assert oracle.rel_err_rowwise(dec, ref[:, :, N:]) <= tol
+
+
 @pytest.mark.parametrize("N", [1, 2, 15, 17, 33, 64, 65, 129])
 def test_prefill_short_lengths(rsp, N):
     say("prefill short", N)
