@@ -78,7 +78,8 @@ int64_t taylor_state_width(int d, int n);
  * Returns -1 for invalid arguments. */
 int64_t taylor_state_numel(int d, int d_v, int n);
 
-/* Zero B*H heads of state (the empty history, Eq. (4) at t < 0).
+/* Zero B*H heads of state (the empty history, Eq. (4) at t < 0), with a
+ * kernel (no memset node, so the call may be captured in a HIP graph).
  * state: device, B*H*taylor_state_numel(d, d_v, n) floats. */
 int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStream_t stream);
 

@@ -81,11 +81,11 @@ int taylor_set_phase_events(hipEvent_t* events, int count) {
 int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStream_t stream) {
   if (B < 0 || H < 0) return fail(TAYLOR_EINVAL, "taylor_state_init: B and H must be >= 0");
   if (!shape_supported(d, d_v, n)) return fail(TAYLOR_EUNSUPPORTED, "taylor_state_init: only d=16, d_v=64, n in 1..6");
-  const size_t bytes = (size_t)B * H * taylor_state_numel(d, d_v, n) * sizeof(float);
-  if (bytes == 0) return TAYLOR_OK;
+  const size_t floats = (size_t)B * H * taylor_state_numel(d, d_v, n);
+  if (floats == 0) return TAYLOR_OK;
   if (state == nullptr) return fail(TAYLOR_EINVAL, "taylor_state_init: state is NULL");
-  const hipError_t e = hipMemsetAsync(state, 0, bytes, stream);
-  if (e != hipSuccess) return hip_fail(e, "taylor_state_init: hipMemsetAsync");
+  const hipError_t e = taylor::launch_fill_zero(state, floats, stream);
+  if (e != hipSuccess) return hip_fail(e, "taylor_state_init: kernel launch");
   return TAYLOR_OK;
 }
 

@@ -252,6 +252,18 @@ static hipError_t launch_decode_n(const DecodeArgs& a) {
   return launch_decode_t<NT, uint16_t, uint16_t>(a);
 }
 
+__global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, size_t n) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
+}
+
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a) {
   switch (a.n) {
     case 1: return launch_decode_n<1>(a);

@@ -41,6 +41,9 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a);
+// Zero n floats with a kernel (not a memset node, so that a caller may capture
+// it in a HIP graph).
+hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a);
 
 // n = 3, bfloat16 inputs, chunk 64 or 128 (taylor_prefill_n3.hip): one

@@ -302,6 +302,49 @@ def test_decode_after_prefix(rsp, n, dtype):
     assert oracle.rel_err_rowwise(got, ref[:, :, N0:]) <= TOL[dtype]
 
 
+def test_graph_replay_matches_eager(rsp):
+    """The calls the bench replays from a HIP graph (state init, n = 3 bfloat16 prefill with
+    its workspace, decode steps) captured once and replayed three times, with eager work
+    and synchronisations in between: every replay gives the eager outputs and state."""
+    say("graph replay vs eager")
+    B, H, N, steps, n = 2, 4, 1000, 6, 3
+    q, k, v = TI.make_qkv(130, B, H, N + steps, 16, 64, dtype="bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    qp, kp, vp = qd[:, :, :N].contiguous(), kd[:, :, :N].contiguous(), vd[:, :, :N].contiguous()
+    qs = [qd[:, :, t].contiguous() for t in range(N, N + steps)]
+    ks = [kd[:, :, t].contiguous() for t in range(N, N + steps)]
+    vs = [vd[:, :, t].contiguous() for t in range(N, N + steps)]
+    st = torch.empty(B * H * rsp.state_numel(16, 64, n), device=DEV)
+    ws = torch.empty(rsp.prefill_workspace_bytes(B, H, N, n, 64) // 4 + 4, device=DEV)
+    o = torch.empty(B, H, N, 64, device=DEV)
+    od = torch.empty(steps, B, H, 64, device=DEV)
+
+    def run():
+        rsp.state_init(st, B, H, n)
+        rsp.prefill(qp, kp, vp, st, n, 1.0, chunk=64, out=o, workspace=ws)
+        for s in range(steps):
+            rsp.decode(qs[s], ks[s], vs[s], st, n, 1.0, out=od[s])
+
+    run()
+    torch.cuda.synchronize()
+    ref_o, ref_od, ref_st = o.clone(), od.clone(), st.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        run()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.fill_(float("nan")), od.fill_(float("nan")), st.fill_(7.0)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref_o) and torch.equal(od, ref_od) and torch.equal(st, ref_st), rep
+    exp = oracle.taylor_direct(q, k, v, n, 1.0)
+    got = np.concatenate([o.cpu().numpy(), od.permute(1, 2, 0, 3).cpu().numpy()], axis=2).astype(np.float64)
+    assert oracle.rel_err_rowwise(got, exp) <= TOL["bf16"]
+
+
 # ---------------------------------------------------------------------------
 # the workloads at full size, on sampled rows
 # ---------------------------------------------------------------------------
