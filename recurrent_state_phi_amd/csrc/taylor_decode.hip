@@ -153,16 +153,25 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIN* __restrict_
   finish_read<TOUT>(acc, dacc, o, bh, tid);
 }
 
-// Orders up to 5 (n = 5, 6: 4,845 or 20,349 rows, more than LDS holds as
-// feature vectors): the same one pass over the state, with each row's
-// features phi(k)_r and phi_hat(q)_r formed from the row table as the row is
-// streamed (the 16 threads of a row form the same two values).
+// Orders up to 5 (n = 5, 6: 4,845 or 20,349 rows; the two feature vectors of
+// n = 6 alone would take 163 KB of LDS): the same one pass over the state,
+// with the features phi(k)_r and phi_hat(q)_r formed from the row table into
+// LDS one piece of kPiece rows at a time, one row per thread.  The state rows
+// are streamed in double-buffered batches of 8 per thread; the loads of the
+// next batch are issued before a piece's features are formed, so they stay in
+// flight across it.  The ones-column T of a piece is updated and read by the
+// thread that forms the piece's row.
 template <int NT, typename TIN, typename TOUT>
 __global__ __launch_bounds__(256) void decode_step_wide_kernel(const TIN* __restrict__ q, const TIN* __restrict__ k,
                                                                const TIN* __restrict__ v, TOUT* __restrict__ o,
                                                                float* __restrict__ S, float* __restrict__ T,
                                                                float inv_a) {
   constexpr int D = state_width(NT);
+  constexpr int kB = 8;                              // rows per thread per batch
+  constexpr int kBatchRows = 16 * kB;                // rows per batch (all threads)
+  constexpr int kPiece = 2048;                       // rows per feature piece
+  static_assert(kPiece % kBatchRows == 0, "pieces hold whole batches");
+  constexpr int kBatches = (D + kBatchRows - 1) / kBatchRows;
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
   float* __restrict__ Sh = S + (size_t)bh * D * kDV;
@@ -171,59 +180,60 @@ __global__ __launch_bounds__(256) void decode_step_wide_kernel(const TIN* __rest
 
   __shared__ float xq[kD], xk[kD];
   __shared__ __align__(16) float vs[kDV];
+  __shared__ float phq[kPiece], phk[kPiece];
   if (tid < kD) xq[tid] = Elem<TIN>::load(q, (size_t)bh * kD + tid);
   else if (tid < 2 * kD) xk[tid - kD] = Elem<TIN>::load(k, (size_t)bh * kD + tid - kD);
   else if (tid < 2 * kD + kDV) vs[tid - 2 * kD] = Elem<TIN>::load(v, (size_t)bh * kDV + tid - 2 * kD);
-  __syncthreads();
 
-  const Alphas al = query_alphas(inv_a);
-  const float4 vv = *reinterpret_cast<const float4*>(&vs[4 * c4]);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  // Rows in batches of kB per thread, two batches in flight: the loads of
-  // batch b + 1 are issued before batch b is used.  Every load is issued
-  // (row indices past the state clamped to its last row, values unused).
-  constexpr int kB = 8;
-  constexpr int kBatches = (D + 16 * kB - 1) / (16 * kB);
+  float dacc = 0.f;
+  // Every load is issued (row indices past the state clamped to its last row,
+  // values unused).
   float4 cur[kB], nxt[kB];
-  uint32_t ccur[kB], cnxt[kB];
-  auto load_batch = [&](int b, float4 (&sv)[kB], uint32_t (&cv)[kB]) {
+  auto load_batch = [&](int b, float4 (&sv)[kB]) {
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
-      const int r0 = rg + 16 * (b * kB + i);
+      const int r0 = b * kBatchRows + rg + 16 * i;
       const int r = r0 < D ? r0 : D - 1;
-      cv[i] = kWideTab.code[r];
       sv[i] = *reinterpret_cast<const float4*>(Sh + (size_t)r * kDV + 4 * c4);
     }
   };
-  load_batch(0, cur, ccur);
+  load_batch(0, cur);
+  __syncthreads();  // q, k, v in LDS
+  const float4 vv = *reinterpret_cast<const float4*>(&vs[4 * c4]);
+  int p0 = 0;  // first row of the piece whose features are in LDS
   for (int b = 0; b < kBatches; ++b) {
-    if (b + 1 < kBatches) load_batch(b + 1, nxt, cnxt);
+    if (b + 1 < kBatches) load_batch(b + 1, nxt);
+    if ((b * kBatchRows) % kPiece == 0) {  // uniform: a new piece starts
+      p0 = b * kBatchRows;
+      __syncthreads();  // the previous piece's features are no longer read
+      for (int f = tid; f < kPiece && p0 + f < D; f += 256) {
+        const int r = p0 + f;
+        const float tr = Th[r];
+        const uint32_t c = kWideTab.code[r];
+        const float pk = wide_feature_value(c, xk, 1.0f);
+        const float pq = wide_feature_value(c, xq, alpha_of(inv_a, c));
+        phk[f] = pk;
+        phq[f] = pq;
+        const float t = tr + pk;  // T block (the ones-column): update, then read
+        Th[r] = t;
+        dacc += pq * t;
+      }
+      __syncthreads();
+    }
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
-      const int r = rg + 16 * (b * kB + i);
+      const int r = b * kBatchRows + rg + 16 * i;
       if (r < D) {
         float4 s = cur[i];
-        const uint32_t c = ccur[i];
-        const float pk = wide_feature_value(c, xk, 1.0f);
-        const float pq = wide_feature_value(c, xq, alpha_of(al, c));
+        const float pk = phk[r - p0], pq = phq[r - p0];
         s.x += pk * vv.x; s.y += pk * vv.y; s.z += pk * vv.z; s.w += pk * vv.w;
         *reinterpret_cast<float4*>(Sh + (size_t)r * kDV + 4 * c4) = s;
         acc.x += pq * s.x; acc.y += pq * s.y; acc.z += pq * s.z; acc.w += pq * s.w;
       }
     }
 #pragma unroll
-    for (int i = 0; i < kB; ++i) {
-      cur[i] = nxt[i];
-      ccur[i] = cnxt[i];
-    }
-  }
-  float dacc = 0.f;
-#pragma unroll 4
-  for (int r = tid; r < D; r += 256) {
-    const uint32_t c = kWideTab.code[r];
-    const float t = Th[r] + wide_feature_value(c, xk, 1.0f);
-    Th[r] = t;
-    dacc += wide_feature_value(c, xq, alpha_of(al, c)) * t;
+    for (int i = 0; i < kB; ++i) cur[i] = nxt[i];
   }
   finish_read<TOUT>(acc, dacc, o, bh, tid);
 }

@@ -115,20 +115,6 @@ constexpr WideFeatureTable make_wide_feature_table() {
   return t;
 }
 
-// alpha_m = 1 / (m! a^m) for m = 0..5 (query side), given 1/a.
-struct Alphas {
-  float v[kMaxN];
-};
-__device__ inline Alphas query_alphas(float inv_a) {
-  Alphas al;
-  float am = 1.0f;
-  for (int m = 0; m < kMaxN; ++m) {
-    al.v[m] = am;
-    am = am * inv_a / (float)(m + 1);
-  }
-  return al;
-}
-
 // Value of a WideFeatureTable row at x (kD floats, e.g. in LDS), times `scale`
 // (alpha_m on the query side, 1 on the key side).
 __device__ inline float wide_feature_value(uint32_t c, const float* x, float scale) {
@@ -139,11 +125,20 @@ __device__ inline float wide_feature_value(uint32_t c, const float* x, float sca
     if (p < m) v *= x[(c >> (3 + 4 * p)) & 15];
   return v;
 }
-__device__ inline float alpha_of(const Alphas& al, uint32_t c) {
+// alpha_m = 1 / (m! a^m) (query side) for the order m of a WideFeatureTable
+// row, given 1/a.  The six factors are plain values and the choice a chain of
+// selects between them (a table in memory indexed per lane would go to
+// scratch); in a loop they are computed once.
+__device__ inline float alpha_of(float inv_a, uint32_t c) {
   const int m = c & 7;
-  float r = al.v[0];
-#pragma unroll
-  for (int i = 1; i < kMaxN; ++i) r = m == i ? al.v[i] : r;
+  const float a1 = inv_a, a2 = a1 * inv_a / 2.0f, a3 = a2 * inv_a / 3.0f;
+  const float a4 = a3 * inv_a / 4.0f, a5 = a4 * inv_a / 5.0f;
+  float r = 1.0f;
+  r = m == 1 ? a1 : r;
+  r = m == 2 ? a2 : r;
+  r = m == 3 ? a3 : r;
+  r = m == 4 ? a4 : r;
+  r = m == 5 ? a5 : r;
   return r;
 }
 

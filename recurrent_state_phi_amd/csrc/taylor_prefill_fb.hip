@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
       for (int p = 0; p < NF; ++p) fidx[p] = p < m ? (int)((c >> (3 + 4 * p)) & 15) : kD;
       const float wt = __fsqrt_rn((float)(c >> 23));
       wk = valid ? wt : 0.0f;
-      wq = valid ? alpha_of(query_alphas(inv_a), c) * wt : 0.0f;
+      wq = valid ? alpha_of(inv_a, c) * wt : 0.0f;
     }
   }
 
