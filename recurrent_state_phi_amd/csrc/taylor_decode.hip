@@ -23,13 +23,13 @@ __constant__ FeatureTable kFeatTab = make_feature_table();
 
 static __device__ WideFeatureTable kWideTab = make_wide_feature_table();
 
-// Sum of the partial reads of the 256 threads (16 row groups: 4 inside a wave,
-// lanes 16 apart, then the 4 waves) and o = y[:d_v] / y[d_v].  acc holds this
-// thread's 4 columns of y, dacc its part of the normaliser.
-template <typename TOUT>
+// Sum of the partial reads of the NWV * 64 threads (row groups of 16 threads:
+// 4 inside a wave, lanes 16 apart, then the NWV waves) and o = y[:d_v] / y[d_v].
+// acc holds this thread's 4 columns of y, dacc its part of the normaliser.
+template <typename TOUT, int NWV = 4>
 __device__ __forceinline__ void finish_read(float4 acc, float dacc, TOUT* __restrict__ o, int bh, int tid) {
-  __shared__ __align__(16) float red[4][kDV];
-  __shared__ float red_den[4];
+  __shared__ __align__(16) float red[NWV][kDV];
+  __shared__ float red_den[NWV];
   const int lane = tid & 63, wave = tid >> 6;
 #pragma unroll
   for (int off = 16; off <= 32; off <<= 1) {
@@ -44,8 +44,12 @@ __device__ __forceinline__ void finish_read(float4 acc, float dacc, TOUT* __rest
   if (lane == 0) red_den[wave] = dacc;
   __syncthreads();
   if (tid < kDV) {
-    const float y = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-    const float den = red_den[0] + red_den[1] + red_den[2] + red_den[3];
+    float y = red[0][tid], den = red_den[0];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) {
+      y += red[i][tid];
+      den += red_den[i];
+    }
     Elem<TOUT>::store(o, (size_t)bh * kDV + tid, y / den);
   }
 }
@@ -154,21 +158,26 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIN* __restrict_
 }
 
 // Orders up to 5 (n = 5, 6: 4,845 or 20,349 rows; the two feature vectors of
-// n = 6 alone would take 163 KB of LDS): the same one pass over the state,
+// n = 6 alone would take 163 KB of LDS): 512 threads per head (32 row groups,
+// so 16 waves per CU keep the long stream of state rows in flight), the same
+// one pass over the state,
 // with the features phi(k)_r and phi_hat(q)_r formed from the row table into
 // LDS one piece of kPiece rows at a time, one row per thread.  The state rows
 // are streamed in double-buffered batches of 8 per thread; the loads of the
 // next batch are issued before a piece's features are formed, so they stay in
 // flight across it.  The ones-column T of a piece is updated and read by the
 // thread that forms the piece's row.
+constexpr int kWideThreads = 512;
+
 template <int NT, typename TIN, typename TOUT>
-__global__ __launch_bounds__(256) void decode_step_wide_kernel(const TIN* __restrict__ q, const TIN* __restrict__ k,
+__global__ __launch_bounds__(kWideThreads) void decode_step_wide_kernel(const TIN* __restrict__ q, const TIN* __restrict__ k,
                                                                const TIN* __restrict__ v, TOUT* __restrict__ o,
                                                                float* __restrict__ S, float* __restrict__ T,
                                                                float inv_a) {
   constexpr int D = state_width(NT);
   constexpr int kB = 8;                              // rows per thread per batch
-  constexpr int kBatchRows = 16 * kB;                // rows per batch (all threads)
+  constexpr int kGroups = kWideThreads / 16;        // row groups of 16 threads
+  constexpr int kBatchRows = kGroups * kB;           // rows per batch (all threads)
   constexpr int kPiece = 2048;                       // rows per feature piece
   static_assert(kPiece % kBatchRows == 0, "pieces hold whole batches");
   constexpr int kBatches = (D + kBatchRows - 1) / kBatchRows;
@@ -193,7 +202,7 @@ __global__ __launch_bounds__(256) void decode_step_wide_kernel(const TIN* __rest
   auto load_batch = [&](int b, float4 (&sv)[kB]) {
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
-      const int r0 = b * kBatchRows + rg + 16 * i;
+      const int r0 = b * kBatchRows + rg + kGroups * i;
       const int r = r0 < D ? r0 : D - 1;
       sv[i] = *reinterpret_cast<const float4*>(Sh + (size_t)r * kDV + 4 * c4);
     }
@@ -207,7 +216,7 @@ __global__ __launch_bounds__(256) void decode_step_wide_kernel(const TIN* __rest
     if ((b * kBatchRows) % kPiece == 0) {  // uniform: a new piece starts
       p0 = b * kBatchRows;
       __syncthreads();  // the previous piece's features are no longer read
-      for (int f = tid; f < kPiece && p0 + f < D; f += 256) {
+      for (int f = tid; f < kPiece && p0 + f < D; f += kWideThreads) {
         const int r = p0 + f;
         const float tr = Th[r];
         const uint32_t c = kWideTab.code[r];
@@ -223,7 +232,7 @@ __global__ __launch_bounds__(256) void decode_step_wide_kernel(const TIN* __rest
     }
 #pragma unroll
     for (int i = 0; i < kB; ++i) {
-      const int r = b * kBatchRows + rg + 16 * i;
+      const int r = b * kBatchRows + rg + kGroups * i;
       if (r < D) {
         float4 s = cur[i];
         const float pk = phk[r - p0], pq = phq[r - p0];
@@ -235,7 +244,7 @@ __global__ __launch_bounds__(256) void decode_step_wide_kernel(const TIN* __rest
 #pragma unroll
     for (int i = 0; i < kB; ++i) cur[i] = nxt[i];
   }
-  finish_read<TOUT>(acc, dacc, o, bh, tid);
+  finish_read<TOUT, kWideThreads / 64>(acc, dacc, o, bh, tid);
 }
 
 template <int NT, typename TIN, typename TOUT>
@@ -248,7 +257,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a) {
                        static_cast<const TIN*>(a.q), static_cast<const TIN*>(a.k), static_cast<const TIN*>(a.v),
                        static_cast<TOUT*>(a.o), S, T, 1.0f / a.a);
   else
-    hipLaunchKernelGGL((decode_step_wide_kernel<NT, TIN, TOUT>), dim3(a.BH), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((decode_step_wide_kernel<NT, TIN, TOUT>), dim3(a.BH), dim3(kWideThreads), 0, a.stream,
                        static_cast<const TIN*>(a.q), static_cast<const TIN*>(a.k), static_cast<const TIN*>(a.v),
                        static_cast<TOUT*>(a.o), S, T, 1.0f / a.a);
   return hipGetLastError();
