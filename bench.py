@@ -308,14 +308,30 @@ def cpu_baseline(qkv_host, sample_every=4):
     oracle.taylor_direct(q, k, v, c["n"], c["a"], rows=rows)
     dt = time.perf_counter() - t0
     full_s = dt * full_pairs / sample_pairs
+    cores = oracle.num_threads()
+    # one thread, as the paper's own measurements (every 64th query row)
+    pos1 = np.arange(63, N, 64)
+    rows1 = (np.arange(BH)[:, None] * N + pos1[None, :]).ravel()
+    pairs1 = float(BH * (pos1 + 1).sum())
+    oracle.set_num_threads(1)
+    try:
+        t1 = time.perf_counter()
+        oracle.taylor_direct(q, k, v, c["n"], c["a"], rows=rows1)
+        dt1 = time.perf_counter() - t1
+    finally:
+        oracle.set_num_threads(cores)
+    full1_s = dt1 * full_pairs / pairs1
     return {
         "value": c["B"] * N / full_s,
         "unit": "tokens/s",
-        "cores": oracle.num_threads(),
+        "cores": cores,
         "kind": "oracle",
         "sample": f"float64 direct O(N^2) sum on every {sample_every}th query row of all {BH} heads "
                   f"({rows.size} rows, {sample_pairs:.3g} of {full_pairs:.3g} query-key pairs, {dt:.1f} s); "
                   f"time extrapolated by pair count to the full job ({full_s:.1f} s)",
+        "single_thread": {"value": c["B"] * N / full1_s, "unit": "tokens/s", "cores": 1,
+                          "sample": f"every 64th query row of all {BH} heads ({rows1.size} rows, {dt1:.1f} s), "
+                                    f"extrapolated by pair count ({full1_s:.0f} s)"},
     }
 
 

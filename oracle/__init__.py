@@ -53,6 +53,8 @@ def _lib():
                                          _i64, _dp, _dp, _lp]
         lib.oracle_arg_stats.restype = None
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         lib.oracle_taylor_weights.argtypes = [_dp, _i64, ctypes.c_int, ctypes.c_double, _dp]
         lib.oracle_taylor_weights.restype = None
         _LIB = lib
@@ -62,6 +64,11 @@ def _lib():
 def num_threads() -> int:
     """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all cores)."""
     return int(_lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for the following oracle calls (timing only: each row is summed by one thread)."""
+    _lib().oracle_set_num_threads(int(n))
 
 
 def taylor_weights(x, n: int, a: float):

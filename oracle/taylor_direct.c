@@ -57,6 +57,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the following calls (timing only; results do not depend on it:
+ * every row is summed sequentially by one thread). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 void oracle_taylor_direct(const float* q, const float* k, const float* v,
                           int64_t BH, int64_t N, int d, int dv, int n, double a,
                           const int64_t* rows, int64_t nrows,
