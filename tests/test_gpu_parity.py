@@ -232,12 +232,41 @@ def test_bf16_prefill_temperatures(rsp, a, chunk):
     assert oracle.rel_err_rowwise(np.concatenate([a_out, b_out], axis=2), ref) <= TOL["bf16"]
 
 
-def test_bf16_output(rsp):
-    say("prefill bf16 out")
-    q, k, v = TI.make_qkv(6, 1, 4, 700, 16, 64, dtype="bf16")
-    ref = oracle.taylor_direct(q, k, v, 3, 1.0)
-    got, _ = run_prefill(rsp, q, k, v, 3, 1.0, 64, "bf16", out_dtype=torch.bfloat16)
+@pytest.mark.parametrize("n,in_dtype,chunk", [(3, "bf16", 64), (3, "f32", 32), (4, "bf16", 32), (5, "f32", 64),
+                                              (6, "bf16", 32)])
+def test_bf16_output(rsp, n, in_dtype, chunk):
+    """bfloat16 outputs (rounded once from the float32 result) for every prefill kernel."""
+    say("prefill bf16 out", n, in_dtype, chunk)
+    q, k, v = TI.make_qkv(6, 1, 4, 700 if n < 6 else 200, 16, 64, dtype=in_dtype)
+    ref = oracle.taylor_direct(q, k, v, n, 1.0)
+    got, _ = run_prefill(rsp, q, k, v, n, 1.0, chunk, in_dtype, out_dtype=torch.bfloat16)
     assert oracle.rel_err_rowwise(got, ref) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("n", [3, 5, 6])
+def test_decode_bf16_io(rsp, n):
+    """Decode with bfloat16 q, k, v and bfloat16 outputs (float32 state), after a prefix."""
+    say("decode bf16 in/out", n)
+    B, H, N0, steps = 1, 3, 40, 5
+    q, k, v = TI.make_qkv(7, B, H, N0 + steps, 16, 64, dtype="bf16")
+    ref = oracle.taylor_direct(q, k, v, n, 1.0)
+    _, st = run_prefill(rsp, q[:, :, :N0], k[:, :, :N0], v[:, :, :N0], n, 1.0, 32, "bf16")
+    qd, kd, vd = to_dev(q, "bf16"), to_dev(k, "bf16"), to_dev(v, "bf16")
+    outs = [rsp.decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), st, n, 1.0,
+                       out_dtype=torch.bfloat16) for t in range(N0, N0 + steps)]
+    got = torch.stack(outs, dim=2).float().cpu().numpy().astype(np.float64)
+    assert oracle.rel_err_rowwise(got, ref[:, :, N0:]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("n", [5, 6])
+@pytest.mark.parametrize("N", [1, 2, 33])
+def test_high_order_short_lengths(rsp, n, N):
+    """n = 5, 6 with one, two and 33 tokens (a partial chunk, padding in every feature block)."""
+    say("high order short", n, N)
+    q, k, v = TI.make_qkv(8, 2, 1, N, 16, 64)
+    ref = oracle.taylor_direct(q, k, v, n, 1.0)
+    got, _ = run_prefill(rsp, q, k, v, n, 1.0, 32, "f32")
+    assert oracle.rel_err_rowwise(got, ref) <= TOL["f32"]
 
 
 def test_many_heads_single_segment(rsp):
