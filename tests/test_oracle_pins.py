@@ -173,12 +173,12 @@ def test_exact_rational_tiny_case():
 # --------------------------------------------------------------------------
 # The softmax limit (Eq. (1)) and the signs of the truncated kernel
 # --------------------------------------------------------------------------
+@pytest.mark.parametrize("a", [1.0, 2.5])
 @pytest.mark.parametrize("n", [2, 3, 4, 6, 10, 16])
-def test_taylor_tends_to_softmax_within_remainder_bound(n):
+def test_taylor_tends_to_softmax_within_remainder_bound(n, a):
     """|o^(n) - o^soft| <= delta/(1-delta) * max_i |v_i - o^soft| per coordinate, where delta
     bounds |p_n(y) e^-y - 1| over the row's scores; the bound follows from Eq. (1)-(2)."""
     q, k, v = TI.make_qkv(31, 1, 2, 96, 8, 5)
-    a = 1.0
     ref = oracle.softmax(q, k, v, a)
     got = oracle.taylor_direct(q, k, v, n, a)
     for h in range(2):
@@ -193,6 +193,40 @@ def test_taylor_tends_to_softmax_within_remainder_bound(n):
             assert np.all(np.abs(got[0, h, t] - ref[0, h, t]) <= bound * (1 + 1e-9) + 1e-15)
     if n == 16:
         assert np.abs(got - ref).max() <= 1e-12
+
+
+@pytest.mark.parametrize("a", [0.7, 3.0])
+def test_softmax_two_tokens_closed_form(a):
+    """Exact softmax (Eq. (1)) with two keys: o_1 = s(d) v_1 + s(-d) v_0 with the logistic
+    function s and d = q_1.(k_1 - k_0) / a; o_0 = v_0."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 2, 6)).astype(np.float32)
+    k = (2.0 * rng.standard_normal((1, 1, 2, 6))).astype(np.float32)
+    v = rng.standard_normal((1, 1, 2, 3)).astype(np.float32)
+    got = oracle.softmax(q, k, v, a)[0, 0]
+    qq, kk, vv = (x[0, 0].astype(np.float64) for x in (q, k, v))
+    d = float(qq[1] @ (kk[1] - kk[0])) / a
+    w1 = 1.0 / (1.0 + math.exp(-d))
+    assert np.allclose(got[0], vv[0], rtol=0, atol=1e-15)
+    assert np.allclose(got[1], w1 * vv[1] + (1.0 - w1) * vv[0], rtol=0, atol=1e-14)
+
+
+def test_softmax_equal_keys_and_dominant_key():
+    """Exact softmax with all keys equal is the running mean of v for any q; a key whose
+    score exceeds every other by 60 (e^-60 < 1e-26) takes all the weight."""
+    q, k, v = TI.make_qkv(32, 1, 1, 40, 4, 3)
+    keq = np.ascontiguousarray(np.broadcast_to(k[:, :, :1], k.shape))
+    got = oracle.softmax(q, keq, v, 1.7)[0, 0]
+    mean = np.cumsum(v[0, 0].astype(np.float64), axis=0) / np.arange(1, 41)[:, None]
+    assert np.abs(got - mean).max() <= 1e-14
+    qd = np.zeros((1, 1, 40, 4), np.float32)
+    qd[..., 0] = 1.0
+    kd = np.zeros((1, 1, 40, 4), np.float32)
+    kd[0, 0, 7, 0] = 60.0  # only key 7 scores above 0
+    got = oracle.softmax(qd, kd, v, 1.0)[0, 0]
+    assert np.abs(got[7:] - v[0, 0, 7].astype(np.float64)).max() <= 1e-20 + 1e-24
+    mean7 = np.cumsum(v[0, 0, :7].astype(np.float64), axis=0) / np.arange(1, 8)[:, None]
+    assert np.abs(got[:7] - mean7).max() <= 1e-15
 
 
 def test_negative_kernel_fraction_matches_printed():
