@@ -32,8 +32,12 @@ int64_t binom(int64_t n, int64_t k) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Shapes compiled into this build.
-bool shape_supported(int d, int d_v, int n) { return d == taylor::kD && d_v == taylor::kDV && n >= 1 && n <= 6; }
+// Shapes compiled into this build: d_v = 64 with d = 16 and n = 1..6, or
+// d = 32, 64 and n = 1..3.
+bool shape_supported(int d, int d_v, int n) {
+  if (d_v != taylor::kDV || n < 1) return false;
+  return (d == taylor::kD && n <= 6) || ((d == 32 || d == 64) && n <= 3);
+}
 
 int check_dtypes(taylor_dtype in, taylor_dtype out) {
   if ((in != TAYLOR_F32 && in != TAYLOR_BF16) || (out != TAYLOR_F32 && out != TAYLOR_BF16))
@@ -80,7 +84,7 @@ int taylor_set_phase_events(hipEvent_t* events, int count) {
 
 int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStream_t stream) {
   if (B < 0 || H < 0) return fail(TAYLOR_EINVAL, "taylor_state_init: B and H must be >= 0");
-  if (!shape_supported(d, d_v, n)) return fail(TAYLOR_EUNSUPPORTED, "taylor_state_init: only d=16, d_v=64, n in 1..6");
+  if (!shape_supported(d, d_v, n)) return fail(TAYLOR_EUNSUPPORTED, "taylor_state_init: only d_v=64 with d=16, n in 1..6 or d=32/64, n in 1..3");
   const size_t floats = (size_t)B * H * taylor_state_numel(d, d_v, n);
   if (floats == 0) return TAYLOR_OK;
   if (state == nullptr) return fail(TAYLOR_EINVAL, "taylor_state_init: state is NULL");
@@ -91,7 +95,7 @@ int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStre
 
 size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n, int chunk) {
   if (B < 0 || H < 0 || N < 0 || !shape_supported(d, d_v, n) || chunk <= 0) return (size_t)-1;
-  const taylor::PrefillPlan p = taylor::plan_prefill(B * H, N, n, chunk);
+  const taylor::PrefillPlan p = taylor::plan_prefill(B * H, N, d, n, chunk);
   return p.workspace_floats * sizeof(float);
 }
 
@@ -102,18 +106,18 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, fl
   if (B < 0 || H < 0 || N < 0) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: B, H, N must be >= 0");
   if (!(a > 0.0f) || a == __builtin_inff()) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: a must be finite and > 0");
   if (!shape_supported(d, d_v, n))
-    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: only d=16, d_v=64, n in 1..6 are built");
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: only d_v=64 with d=16, n in 1..6 or d=32/64, n in 1..3 are built");
   const bool in_bf16 = in_dtype == TAYLOR_BF16, out_bf16 = out_dtype == TAYLOR_BF16;
-  if (!taylor::prefill_supported(n, chunk, in_bf16))
-    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: unsupported (n, chunk, in_dtype): for n in 1..3 chunk "
-                                     "must be 32/64 (float32) or 32/64/128 (bfloat16); for n = 4..6 chunk 32/64");
+  if (!taylor::prefill_supported(d, n, chunk, in_bf16))
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill: unsupported (d, n, chunk, in_dtype): at d = 16, n in 1..3, "
+                                     "chunk must be 32/64 (float32) or 32/64/128 (bfloat16); otherwise 32/64");
   if ((int64_t)B * H == 0 || N == 0) return TAYLOR_OK;
   if (!q || !k || !v || !o || !state) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: NULL tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state))
     return fail(TAYLOR_EINVAL, "taylor_attn_prefill: q, k, v, o and state must be 16-byte aligned");
   if ((int64_t)B * H > (1 << 24) || (int64_t)N * chunk > ((int64_t)1 << 40))
     return fail(TAYLOR_EINVAL, "taylor_attn_prefill: sizes out of range");
-  const taylor::PrefillPlan plan = taylor::plan_prefill(B * H, N, n, chunk);
+  const taylor::PrefillPlan plan = taylor::plan_prefill(B * H, N, d, n, chunk);
   const size_t need = plan.workspace_floats * sizeof(float);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need)
@@ -121,7 +125,7 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, fl
                                      " bytes, see taylor_prefill_workspace_bytes)");
     if (!aligned16(workspace)) return fail(TAYLOR_EINVAL, "taylor_attn_prefill: workspace must be 16-byte aligned");
   }
-  taylor::PrefillArgs args{q, k, v, o, state, static_cast<float*>(workspace), B * H, N, n, chunk, a,
+  taylor::PrefillArgs args{q, k, v, o, state, static_cast<float*>(workspace), B * H, N, d, n, chunk, a,
                            in_bf16, out_bf16, plan, stream, g_phase_events_on ? g_phase_events : nullptr,
                            g_wait_limit.load(std::memory_order_relaxed)};
   const hipError_t e = taylor::launch_prefill(args);
@@ -135,13 +139,14 @@ int taylor_attn_decode(const void* q, const void* k, const void* v, void* o, flo
   if (B < 0 || H < 0) return fail(TAYLOR_EINVAL, "taylor_attn_decode: B and H must be >= 0");
   if (!(a > 0.0f) || a == __builtin_inff()) return fail(TAYLOR_EINVAL, "taylor_attn_decode: a must be finite and > 0");
   if (!shape_supported(d, d_v, n))
-    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_decode: only d=16, d_v=64, n in 1..6 are built");
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_decode: only d_v=64 with d=16, n in 1..6 or d=32/64, n in 1..3 are built");
   if ((int64_t)B * H == 0) return TAYLOR_OK;
   if ((int64_t)B * H > (1 << 30)) return fail(TAYLOR_EINVAL, "taylor_attn_decode: B*H out of range");
   if (!q || !k || !v || !o || !state) return fail(TAYLOR_EINVAL, "taylor_attn_decode: NULL tensor pointer");
   if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(TAYLOR_EINVAL, "taylor_attn_decode: q, k, v, o and state must be 16-byte aligned");
-  taylor::DecodeArgs args{q, k, v, o, state, B * H, n, a, in_dtype == TAYLOR_BF16, out_dtype == TAYLOR_BF16, stream};
+  taylor::DecodeArgs args{q, k, v, o, state, B * H, d, n, a, in_dtype == TAYLOR_BF16, out_dtype == TAYLOR_BF16,
+                          stream};
   const hipError_t e = taylor::launch_decode(args);
   if (e != hipSuccess) return hip_fail(e, "taylor_attn_decode: kernel launch");
   return TAYLOR_OK;

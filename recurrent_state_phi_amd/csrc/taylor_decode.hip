@@ -21,7 +21,17 @@ namespace taylor {
 
 __constant__ FeatureTable kFeatTab = make_feature_table();
 
-static __device__ WideFeatureTable kWideTab = make_wide_feature_table();
+static __device__ RowTable<16, 5> kRows16 = make_row_table<16, 5>();  // d = 16, n = 5, 6
+static __device__ RowTable<32, 2> kRows32 = make_row_table<32, 2>();  // d = 32, n <= 3
+static __device__ RowTable<64, 2> kRows64 = make_row_table<64, 2>();  // d = 64, n <= 3
+
+template <int KD>
+__device__ __forceinline__ uint32_t row_code(int f) {
+  if constexpr (KD == 16) return kRows16.code[f];
+  else if constexpr (KD == 32) return kRows32.code[f];
+  else return kRows64.code[f];
+}
+template <int KD> constexpr int table_orders() { return KD == 16 ? 5 : 2; }
 
 // Sum of the partial reads of the NWV * 64 threads (row groups of 16 threads:
 // 4 inside a wave, lanes 16 apart, then the NWV waves) and o = y[:d_v] / y[d_v].
@@ -169,12 +179,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const TIN* __restrict_
 // thread that forms the piece's row.
 constexpr int kWideThreads = 512;
 
-template <int NT, typename TIN, typename TOUT>
+template <int NT, int KD, typename TIN, typename TOUT>
 __global__ __launch_bounds__(kWideThreads) void decode_step_wide_kernel(const TIN* __restrict__ q, const TIN* __restrict__ k,
                                                                const TIN* __restrict__ v, TOUT* __restrict__ o,
                                                                float* __restrict__ S, float* __restrict__ T,
                                                                float inv_a) {
-  constexpr int D = state_width(NT);
+  constexpr int D = state_width_d(KD, NT);
+  constexpr int MAXM = table_orders<KD>();
+  static_assert(2 * KD + kDV <= kWideThreads, "one thread per element of q, k and v");
   constexpr int kB = 8;                              // rows per thread per batch
   constexpr int kGroups = kWideThreads / 16;        // row groups of 16 threads
   constexpr int kBatchRows = kGroups * kB;           // rows per batch (all threads)
@@ -187,12 +199,12 @@ __global__ __launch_bounds__(kWideThreads) void decode_step_wide_kernel(const TI
   float* __restrict__ Th = T + (size_t)bh * D;
   const int c4 = tid & 15, rg = tid >> 4;
 
-  __shared__ float xq[kD], xk[kD];
+  __shared__ float xq[KD], xk[KD];
   __shared__ __align__(16) float vs[kDV];
   __shared__ float phq[kPiece], phk[kPiece];
-  if (tid < kD) xq[tid] = Elem<TIN>::load(q, (size_t)bh * kD + tid);
-  else if (tid < 2 * kD) xk[tid - kD] = Elem<TIN>::load(k, (size_t)bh * kD + tid - kD);
-  else if (tid < 2 * kD + kDV) vs[tid - 2 * kD] = Elem<TIN>::load(v, (size_t)bh * kDV + tid - 2 * kD);
+  if (tid < KD) xq[tid] = Elem<TIN>::load(q, (size_t)bh * KD + tid);
+  else if (tid < 2 * KD) xk[tid - KD] = Elem<TIN>::load(k, (size_t)bh * KD + tid - KD);
+  else if (tid < 2 * KD + kDV) vs[tid - 2 * KD] = Elem<TIN>::load(v, (size_t)bh * kDV + tid - 2 * KD);
 
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float dacc = 0.f;
@@ -219,9 +231,9 @@ __global__ __launch_bounds__(kWideThreads) void decode_step_wide_kernel(const TI
       for (int f = tid; f < kPiece && p0 + f < D; f += kWideThreads) {
         const int r = p0 + f;
         const float tr = Th[r];
-        const uint32_t c = kWideTab.code[r];
-        const float pk = wide_feature_value(c, xk, 1.0f);
-        const float pq = wide_feature_value(c, xq, alpha_of(inv_a, c));
+        const uint32_t c = row_code<KD>(r);
+        const float pk = row_feature_value<KD, MAXM>(c, xk, 1.0f);
+        const float pq = row_feature_value<KD, MAXM>(c, xq, alpha_of(inv_a, c));
         phk[f] = pk;
         phq[f] = pq;
         const float t = tr + pk;  // T block (the ones-column): update, then read
@@ -247,28 +259,30 @@ __global__ __launch_bounds__(kWideThreads) void decode_step_wide_kernel(const TI
   finish_read<TOUT, kWideThreads / 64>(acc, dacc, o, bh, tid);
 }
 
-template <int NT, typename TIN, typename TOUT>
+// d = 16, n <= 4: decode_step_kernel; d = 16, n = 5, 6 and d = 32, 64:
+// decode_step_wide_kernel.
+template <int NT, int KD, typename TIN, typename TOUT>
 static hipError_t launch_decode_t(const DecodeArgs& a) {
-  const int D = state_width(NT);
+  const int D = state_width_d(KD, NT);
   float* S = a.state;
   float* T = a.state + (size_t)a.BH * D * kDV;
-  if constexpr (NT <= 4)
+  if constexpr (KD == kD && NT <= 4)
     hipLaunchKernelGGL((decode_step_kernel<NT, TIN, TOUT>), dim3(a.BH), dim3(256), 0, a.stream,
                        static_cast<const TIN*>(a.q), static_cast<const TIN*>(a.k), static_cast<const TIN*>(a.v),
                        static_cast<TOUT*>(a.o), S, T, 1.0f / a.a);
   else
-    hipLaunchKernelGGL((decode_step_wide_kernel<NT, TIN, TOUT>), dim3(a.BH), dim3(kWideThreads), 0, a.stream,
+    hipLaunchKernelGGL((decode_step_wide_kernel<NT, KD, TIN, TOUT>), dim3(a.BH), dim3(kWideThreads), 0, a.stream,
                        static_cast<const TIN*>(a.q), static_cast<const TIN*>(a.k), static_cast<const TIN*>(a.v),
                        static_cast<TOUT*>(a.o), S, T, 1.0f / a.a);
   return hipGetLastError();
 }
 
-template <int NT>
+template <int NT, int KD>
 static hipError_t launch_decode_n(const DecodeArgs& a) {
-  if (!a.in_bf16 && !a.out_bf16) return launch_decode_t<NT, float, float>(a);
-  if (!a.in_bf16 && a.out_bf16) return launch_decode_t<NT, float, uint16_t>(a);
-  if (a.in_bf16 && !a.out_bf16) return launch_decode_t<NT, uint16_t, float>(a);
-  return launch_decode_t<NT, uint16_t, uint16_t>(a);
+  if (!a.in_bf16 && !a.out_bf16) return launch_decode_t<NT, KD, float, float>(a);
+  if (!a.in_bf16 && a.out_bf16) return launch_decode_t<NT, KD, float, uint16_t>(a);
+  if (a.in_bf16 && !a.out_bf16) return launch_decode_t<NT, KD, uint16_t, float>(a);
+  return launch_decode_t<NT, KD, uint16_t, uint16_t>(a);
 }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ p, size_t n) {
@@ -284,13 +298,21 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a) {
+  if (a.d == 32 || a.d == 64) {
+    switch (a.n) {
+      case 1: return a.d == 32 ? launch_decode_n<1, 32>(a) : launch_decode_n<1, 64>(a);
+      case 2: return a.d == 32 ? launch_decode_n<2, 32>(a) : launch_decode_n<2, 64>(a);
+      case 3: return a.d == 32 ? launch_decode_n<3, 32>(a) : launch_decode_n<3, 64>(a);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (a.n) {
-    case 1: return launch_decode_n<1>(a);
-    case 2: return launch_decode_n<2>(a);
-    case 3: return launch_decode_n<3>(a);
-    case 4: return launch_decode_n<4>(a);
-    case 5: return launch_decode_n<5>(a);
-    case 6: return launch_decode_n<6>(a);
+    case 1: return launch_decode_n<1, kD>(a);
+    case 2: return launch_decode_n<2, kD>(a);
+    case 3: return launch_decode_n<3, kD>(a);
+    case 4: return launch_decode_n<4, kD>(a);
+    case 5: return launch_decode_n<5, kD>(a);
+    case 6: return launch_decode_n<6, kD>(a);
     default: return hipErrorInvalidValue;
   }
 }

@@ -81,32 +81,52 @@ __device__ inline float feature_value(const FeatureTable& tab, int f, const floa
   return feature_value(tab.code[f], tab.weight[f], x, alpha);
 }
 
-// Rows of the stacked basis for orders up to 5 (n <= 6, up to 20,349 rows),
-// for kernels that index rows at run time: bits 0-2 hold the order m, the
-// 4-bit fields from bit 3 the coordinates i_1 <= ... <= i_m, and bits 23-29
-// the multinomial m! / prod_i c_i! (at most 120), whose square root is the
-// weight of section 3.4.  Same row order as FeatureTable.
-constexpr int kMaxN = 6;
-struct WideFeatureTable {
-  uint32_t code[state_width(kMaxN)];
+// D for head dimension d: sum_{m<n} C(d + m - 1, m).
+constexpr int state_width_d(int d, int n) {
+  int s = 0;
+  for (int m = 0; m < n; ++m) {
+    long r = 1;
+    for (int i = 1; i <= m; ++i) r = r * (d - 1 + i) / i;
+    s += (int)r;
+  }
+  return s;
+}
+
+// Rows of the stacked basis (section 3.4) for head dimension KD and orders up
+// to MAXM, for kernels that index rows at run time.  Row order as in the
+// caller's layout: m ascending, nondecreasing multi-indices i_1 <= ... <= i_m
+// in lexicographic order.  Code of a row: bits 0-2 the order m, then MAXM
+// fields of kCB bits holding the coordinates, then the multinomial
+// m! / prod_i c_i! (at most 120), whose square root is the row's weight.
+//   RowTable<16, 5>: n <= 6 at d = 16 (20,349 rows, 4-bit coordinates)
+//   RowTable<32, 2>, RowTable<64, 2>: n <= 3 at d = 32, 64 (561, 2,145 rows)
+template <int KD, int MAXM>
+struct RowTable {
+  static constexpr int kCB = KD <= 16 ? 4 : 6;  // bits per coordinate
+  static constexpr int kMultShift = 3 + kCB * MAXM;
+  static constexpr int kRows = state_width_d(KD, MAXM + 1);
+  static_assert(kMultShift + 7 <= 32, "row code fits 32 bits");
+  uint32_t code[kRows];
 };
 
-constexpr WideFeatureTable make_wide_feature_table() {
-  WideFeatureTable t{};
+template <int KD, int MAXM>
+constexpr RowTable<KD, MAXM> make_row_table() {
+  using T = RowTable<KD, MAXM>;
+  T t{};
   int f = 0;
-  for (int m = 0; m < kMaxN; ++m) {
-    int idx[kMaxN] = {};
+  for (int m = 0; m <= MAXM; ++m) {
+    int idx[MAXM + 1] = {};
     while (true) {
       uint32_t mult = 1;  // m! / prod_i c_i!, built up one coordinate at a time
       for (int p = 0, run = 0; p < m; ++p) {
         run = (p > 0 && idx[p] == idx[p - 1]) ? run + 1 : 1;
         mult = mult * (p + 1) / run;
       }
-      uint32_t c = (uint32_t)m | mult << 23;
-      for (int p = 0; p < m; ++p) c |= (uint32_t)idx[p] << (3 + 4 * p);
+      uint32_t c = (uint32_t)m | mult << T::kMultShift;
+      for (int p = 0; p < m; ++p) c |= (uint32_t)idx[p] << (3 + T::kCB * p);
       t.code[f++] = c;
       int p = m - 1;  // next nondecreasing multi-index in lexicographic order
-      while (p >= 0 && idx[p] == kD - 1) --p;
+      while (p >= 0 && idx[p] == KD - 1) --p;
       if (p < 0) break;
       ++idx[p];
       for (int r = p + 1; r < m; ++r) idx[r] = idx[p];
@@ -115,17 +135,30 @@ constexpr WideFeatureTable make_wide_feature_table() {
   return t;
 }
 
-// Value of a WideFeatureTable row at x (kD floats, e.g. in LDS), times `scale`
-// (alpha_m on the query side, 1 on the key side).
-__device__ inline float wide_feature_value(uint32_t c, const float* x, float scale) {
+// Coordinate p of a row code (meaningful for p < m).
+template <int KD, int MAXM>
+__device__ inline int row_coord(uint32_t c, int p) {
+  using T = RowTable<KD, MAXM>;
+  return (int)((c >> (3 + T::kCB * p)) & ((1u << T::kCB) - 1));
+}
+// The row's sqrt-multinomial weight.
+template <int KD, int MAXM>
+__device__ inline float row_weight(uint32_t c) {
+  return __fsqrt_rn((float)(c >> RowTable<KD, MAXM>::kMultShift));
+}
+// Value of a row at x (KD floats, e.g. in LDS), times `scale` (alpha_m on the
+// query side, 1 on the key side).
+template <int KD, int MAXM>
+__device__ inline float row_feature_value(uint32_t c, const float* x, float scale) {
   const int m = c & 7;
-  float v = scale * __fsqrt_rn((float)(c >> 23));
+  float v = scale * row_weight<KD, MAXM>(c);
 #pragma unroll
-  for (int p = 0; p < kMaxN - 1; ++p)
-    if (p < m) v *= x[(c >> (3 + 4 * p)) & 15];
+  for (int p = 0; p < MAXM; ++p)
+    if (p < m) v *= x[row_coord<KD, MAXM>(c, p)];
   return v;
 }
-// alpha_m = 1 / (m! a^m) (query side) for the order m of a WideFeatureTable
+
+// alpha_m = 1 / (m! a^m) (query side) for the order m of a RowTable
 // row, given 1/a.  The six factors are plain values and the choice a chain of
 // selects between them (a table in memory indexed per lane would go to
 // scratch); in a loop they are computed once.

@@ -10,7 +10,7 @@ namespace taylor {
 struct DecodeArgs {
   const void* q; const void* k; const void* v; void* o;
   float* state;
-  int BH, n;
+  int BH, d, n;
   float a;
   bool in_bf16, out_bf16;
   hipStream_t stream;
@@ -25,13 +25,13 @@ struct PrefillPlan {
   size_t workspace_floats = 0;  // 0 when nseg == 1
 };
 
-PrefillPlan plan_prefill(int BH, int N, int n, int chunk);
+PrefillPlan plan_prefill(int BH, int N, int d, int n, int chunk);
 
 struct PrefillArgs {
   const void* q; const void* k; const void* v; void* o;
   float* state;
   float* workspace;
-  int BH, N, n, chunk;
+  int BH, N, d, n, chunk;
   float a;
   bool in_bf16, out_bf16;
   PrefillPlan plan;
@@ -55,19 +55,21 @@ size_t prefill_n3_workspace_floats(int BH, int nseg);
 constexpr int kN3Magic = 0x54617933;
 constexpr int kN3ErrTimeout = 1;
 
-// n = 4, 5, 6, feature-blocked, chunk 32 or 64 (taylor_prefill_fb.hip): the
-// launch, the number of 176-row feature blocks, and the floats of the
-// per-block output workspace.
+// Feature-blocked prefill, chunk 32 or 64 (taylor_prefill_fb.hip): d = 16
+// with n = 4, 5, 6, and d = 32, 64 with n = 1, 2, 3.  The launch, the number
+// of 176-row feature blocks, and the floats of the per-block output workspace.
 hipError_t launch_prefill_fb(const PrefillArgs& a);
-int prefill_fb_blocks(int n);
-size_t prefill_fb_output_floats(int BH, int N, int n);
+int prefill_fb_blocks(int d, int n);
+size_t prefill_fb_output_floats(int BH, int N, int d, int n);
+// Whether prefill of head dimension d and order n runs feature-blocked.
+inline bool prefill_uses_fb(int d, int n) { return d != 16 || n >= 4; }
 
 // Exclusive scan of the per-segment state sums in place, seeded with the
 // caller's state (taylor_prefill.hip).
 hipError_t launch_segment_scan(const float* st_S, const float* st_T, float* W_S, float* W_T, int D, int nseg, int BH,
                                hipStream_t stream);
 
-// Whether a (n, chunk, input dtype) combination is compiled.
-bool prefill_supported(int n, int chunk, bool in_bf16);
+// Whether a (d, n, chunk, input dtype) combination is compiled.
+bool prefill_supported(int d, int n, int chunk, bool in_bf16);
 
 }  // namespace taylor

@@ -570,34 +570,38 @@ hipError_t launch_segment_scan(const float* st_S, const float* st_T, float* W_S,
   return hipGetLastError();
 }
 
-PrefillPlan plan_prefill(int BH, int N, int n, int chunk) {
+PrefillPlan plan_prefill(int BH, int N, int d, int n, int chunk) {
   PrefillPlan p;
   if (BH <= 0 || N <= 0 || chunk <= 0) return p;
   p.nchunks = (N + chunk - 1) / chunk;
   // Aim for at least 512 workgroups in the chunk kernel (two per CU on a
   // 256-CU part) when the heads alone do not provide them; 128-token chunks
-  // fill an LDS on their own, so for them aim at one workgroup per CU.  For
-  // n >= 4 every segment is split into feature blocks (6, 28 or 116), one
-  // workgroup each.
-  const int blocks = n >= 4 ? prefill_fb_blocks(n) : 1;
+  // fill an LDS on their own, so for them aim at one workgroup per CU.  In
+  // the feature-blocked kernel (d = 16 with n >= 4, and d = 32, 64) every
+  // segment is split into feature blocks, one workgroup each.
+  const bool fbk = prefill_uses_fb(d, n);
+  const int blocks = fbk ? prefill_fb_blocks(d, n) : 1;
   const int target = chunk >= 128 ? 256 : 512;
-  // n >= 4: at most one round of workgroups (a second, partial round would
-  // cost as much as the first)
-  int nseg = n >= 4 ? target / (BH * blocks) : (target + BH * blocks - 1) / (BH * blocks);
+  // feature-blocked: at most one round of workgroups (a second, partial round
+  // would cost as much as the first)
+  int nseg = fbk ? target / (BH * blocks) : (target + BH * blocks - 1) / (BH * blocks);
   if (nseg < 1) nseg = 1;
   if (nseg > p.nchunks) nseg = p.nchunks;
   p.chunks_per_seg = (p.nchunks + nseg - 1) / nseg;
   p.nseg = (p.nchunks + p.chunks_per_seg - 1) / p.chunks_per_seg;
-  const int D = state_width(n);
+  const int D = state_width_d(d, n);
   p.workspace_floats = p.nseg > 1 ? (size_t)BH * p.nseg * D * (kDV + 1) : 0;
-  // n = 3 with bfloat16 inputs takes the look-back kernel, whose workspace is
-  // larger; the size does not depend on the input type, so cover both
-  if (n == 3) p.workspace_floats = std::max(p.workspace_floats, prefill_n3_workspace_floats(BH, p.nseg));
-  if (n >= 4) p.workspace_floats += prefill_fb_output_floats(BH, N, n);
+  // d = 16, n = 3 with bfloat16 inputs takes the look-back kernel, whose
+  // workspace is larger; the size does not depend on the input type, so
+  // cover both
+  if (d == 16 && n == 3) p.workspace_floats = std::max(p.workspace_floats, prefill_n3_workspace_floats(BH, p.nseg));
+  if (fbk) p.workspace_floats += prefill_fb_output_floats(BH, N, d, n);
   return p;
 }
 
-bool prefill_supported(int n, int chunk, bool in_bf16) {
+bool prefill_supported(int d, int n, int chunk, bool in_bf16) {
+  if (d == 32 || d == 64) return n >= 1 && n <= 3 && (chunk == 32 || chunk == 64);
+  if (d != 16) return false;
   if (n >= 4 && n <= 6) return chunk == 32 || chunk == 64;
   if (n < 1 || n > 3) return false;
   if (in_bf16) return chunk == 32 || chunk == 64 || chunk == 128;
@@ -661,15 +665,13 @@ static hipError_t launch_prefill_n(const PrefillArgs& a) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {
+  if (prefill_uses_fb(a.d, a.n)) return launch_prefill_fb(a);
   switch (a.n) {
     case 1: return launch_prefill_n<1>(a);
     case 2: return launch_prefill_n<2>(a);
     case 3:
       if (a.in_bf16 && (a.chunk == 64 || a.chunk == 128)) return launch_prefill_n3_bf16(a);
       return launch_prefill_n<3>(a);
-    case 4:
-    case 5:
-    case 6: return launch_prefill_fb(a);
   }
   return hipErrorInvalidValue;
 }

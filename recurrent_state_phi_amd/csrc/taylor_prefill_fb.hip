@@ -1,4 +1,5 @@
-// Chunked prefill for n = 4, 5, 6 (section 3.5 of "A Taylor-Series Route to
+// Chunked prefill for n = 4, 5, 6 at d = 16 and n = 1, 2, 3 at d = 32, 64
+// (section 3.5 of "A Taylor-Series Route to
 // Linear-Time Transformers with a Fixed Number of Recurrent States",
 // arXiv 2610.20637), where the stacked state has D = 969, 4,845 or 20,349
 // rows of d_v + 1 = 65 floats (252 KB, 1.26 MB, 5.3 MB per head): more than
@@ -46,15 +47,28 @@ namespace fb {
 constexpr int kFT = 11;                      // feature tiles per block
 constexpr int kBF = 16 * kFT;                // 176 rows per block
 constexpr int kPS = kBF + 4;                 // feature row stride in LDS (16-byte aligned rows)
-constexpr int blocks_of(int n) { return (state_width(n) + kBF - 1) / kBF; }  // 6, 28, 116
+// Feature blocks of the state: d = 16: 6, 28, 116 for n = 4, 5, 6;
+// d = 32: 1, 1, 4 and d = 64: 1, 1, 13 for n = 1, 2, 3.
+constexpr int blocks_of(int d, int n) { return (state_width_d(d, n) + kBF - 1) / kBF; }
 
-__constant__ FeatureTable kTab = make_feature_table();           // n = 4 (orders <= 3)
-static __device__ WideFeatureTable kWideTab = make_wide_feature_table();  // n = 5, 6
+__constant__ FeatureTable kTab = make_feature_table();                 // d = 16, n = 4 (orders <= 3)
+static __device__ RowTable<16, 5> kTab16 = make_row_table<16, 5>();   // d = 16, n = 5, 6
+static __device__ RowTable<32, 2> kTab32 = make_row_table<32, 2>();   // d = 32, n <= 3
+static __device__ RowTable<64, 2> kTab64 = make_row_table<64, 2>();   // d = 64, n <= 3
 
-template <int C>
+// The row table a (KD, NT) kernel reads (all but d = 16, n = 4).
+template <int KD>
+__device__ __forceinline__ uint32_t row_code(int f) {
+  if constexpr (KD == 16) return kTab16.code[f];
+  else if constexpr (KD == 32) return kTab32.code[f];
+  else return kTab64.code[f];
+}
+template <int KD> constexpr int table_orders() { return KD == 16 ? 5 : 2; }
+
+template <int C, int KD>
 struct Lds {
-  float Xq[C][kD + 1];  // column kD: 1 (the factor of unused coordinate slots)
-  float Xk[C][kD + 1];  // column kD: 1, or 0 for a padding token
+  float Xq[C][KD + 1];  // column KD: 1 (the factor of unused coordinate slots)
+  float Xk[C][KD + 1];  // column KD: 1, or 0 for a padding token
   float V[C][kDV + 16];  // row stride 80 floats: the 4 lane groups of an MFMA operand read hit different banks
   float PhQ[C][kPS];
   float PhK[C][kPS];
@@ -76,7 +90,7 @@ __device__ __forceinline__ float poly(float y) {
   return r;
 }
 
-template <int NT, int C, bool FULL, typename IT>
+template <int NT, int KD, int C, bool FULL, typename IT>
 __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const IT* __restrict__ q, const IT* __restrict__ k,
                                                          const IT* __restrict__ v, float* __restrict__ Yp,
                                                          const float* __restrict__ pre_S,
@@ -84,10 +98,10 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
                                                          float* __restrict__ dst_S, float* __restrict__ dst_T,
                                                          int dst_slots, int BH, int N, int nseg, int cps,
                                                          float inv_a) {
-  __shared__ __align__(16) Lds<C> L;
+  __shared__ __align__(16) Lds<C, KD> L;
   constexpr int NTT = C / 16;
-  constexpr int kD4 = state_width(NT);  // rows of the stacked state
-  constexpr int kNFB = blocks_of(NT);
+  constexpr int kD4 = state_width_d(KD, NT);  // rows of the stacked state
+  constexpr int kNFB = blocks_of(KD, NT);
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: guards MFMAs
   const int fbk = blockIdx.x % kNFB;
@@ -118,31 +132,32 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
     if (pt && tid < kBF && F0 + tid < kD4) treg = pt[F0 + tid];
   }
 
-  // ---- this thread's feature row (tid < 176): coordinates (kD = the column
+  // ---- this thread's feature row (tid < 176): coordinates (KD = the column
   //      of ones for unused slots), key-side weight and query-side weight
-  constexpr int NF = NT - 1;  // coordinate slots: orders up to n - 1
+  constexpr int NF = NT > 1 ? NT - 1 : 1;  // coordinate slots: orders up to n - 1
   int fidx[NF];
   float wk = 0.0f, wq = 0.0f;  // 0 for rows past the state and threads >= 176
   {
     const int f = F0 + tid;
     const bool valid = tid < kBF && f < kD4;
     const int fr = valid ? f : 0;
-    if constexpr (NT == 4) {
+    if constexpr (KD == 16 && NT == 4) {
       const uint32_t c = kTab.code[fr];
       const int m = c & 3;
       const float a2 = inv_a * inv_a;
       const float am = m == 0 ? 1.0f : m == 1 ? inv_a : m == 2 ? 0.5f * a2 : a2 * inv_a * (1.0f / 6.0f);
 #pragma unroll
-      for (int p = 0; p < NF; ++p) fidx[p] = p < m ? (int)((c >> (2 + 4 * p)) & 15) : kD;
+      for (int p = 0; p < NF; ++p) fidx[p] = p < m ? (int)((c >> (2 + 4 * p)) & 15) : KD;
       const float wt = kTab.weight[fr];
       wk = valid ? wt : 0.0f;
       wq = valid ? wt * am : 0.0f;
     } else {
-      const uint32_t c = kWideTab.code[fr];
+      constexpr int MAXM = table_orders<KD>();
+      const uint32_t c = row_code<KD>(fr);
       const int m = c & 7;
 #pragma unroll
-      for (int p = 0; p < NF; ++p) fidx[p] = p < m ? (int)((c >> (3 + 4 * p)) & 15) : kD;
-      const float wt = __fsqrt_rn((float)(c >> 23));
+      for (int p = 0; p < NF; ++p) fidx[p] = p < m ? row_coord<KD, MAXM>(c, p) : KD;
+      const float wt = row_weight<KD, MAXM>(c);
       wk = valid ? wt : 0.0f;
       wq = valid ? alpha_of(inv_a, c) * wt : 0.0f;
     }
@@ -150,16 +165,16 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
 
   // ---- loads of one chunk into registers (token indices clamped into the
   //      chunk; values of padding tokens are replaced when staged)
-  constexpr int NLK = C * kD / 256, NLV = C * kDV / 256;
+  constexpr int NLK = C * KD / 256, NLV = C * kDV / 256;
   float rk[NLK], rq[NLK], rv[NLV];
   auto fetch = [&](int t0n) {
     const int last = min(C, t_end - t0n) - 1;
     const size_t basen = (size_t)bh * N + t0n;
 #pragma unroll
     for (int e = 0; e < NLK; ++e) {
-      const int i = tid + 256 * e, tok = min(i / kD, last), j = i % kD;
-      rk[e] = ld(k, (basen + tok) * kD + j);
-      if (FULL) rq[e] = ld(q, (basen + tok) * kD + j);
+      const int i = tid + 256 * e, tok = min(i / KD, last), j = i % KD;
+      rk[e] = ld(k, (basen + tok) * KD + j);
+      if (FULL) rq[e] = ld(q, (basen + tok) * KD + j);
     }
 #pragma unroll
     for (int e = 0; e < NLV; ++e) {
@@ -176,7 +191,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
     // ---- stage q, k, v (float), zero for padding tokens; publish T of the block
 #pragma unroll
     for (int e = 0; e < NLK; ++e) {
-      const int i = tid + 256 * e, tok = i / kD, j = i % kD;
+      const int i = tid + 256 * e, tok = i / KD, j = i % KD;
       L.Xk[tok][j] = tok < nv ? rk[e] : 0.0f;
       if (FULL) L.Xq[tok][j] = tok < nv ? rq[e] : 0.0f;
     }
@@ -186,8 +201,8 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
       L.V[tok][j] = tok < nv ? rv[e] : 0.0f;
     }
     if (tid < C) {
-      L.Xk[tid][kD] = tid < nv ? 1.0f : 0.0f;  // the constant feature of a padding token is 0
-      if (FULL) L.Xq[tid][kD] = 1.0f;
+      L.Xk[tid][KD] = tid < nv ? 1.0f : 0.0f;  // the constant feature of a padding token is 0
+      if (FULL) L.Xq[tid][KD] = 1.0f;
     }
     if (FULL && tid < kBF) L.Ts[tid] = treg;
     if (t0 + C < t_end) fetch(t0 + C);  // uniform
@@ -214,7 +229,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
         const int ta = tile / NTT, tb = tile % NTT;
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s4 = 0; s4 < kD / 4; ++s4)
+        for (int s4 = 0; s4 < KD / 4; ++s4)
           sc = mfma_f32_k4(L.Xq[16 * ta + li][4 * s4 + g], L.Xk[16 * tb + li][4 * s4 + g], sc);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -313,10 +328,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   Elem<TOUT>::store(o, i, num / den);
 }
 
-template <int NT, int C, typename IT, typename TOUT>
+template <int NT, int KD, int C, typename IT, typename TOUT>
 hipError_t launch(const PrefillArgs& a) {
-  constexpr int kD4 = state_width(NT);
-  constexpr int kNFB = blocks_of(NT);
+  constexpr int kD4 = state_width_d(KD, NT);
+  constexpr int kNFB = blocks_of(KD, NT);
   const PrefillPlan& pl = a.plan;
   float* st_S = a.state;
   float* st_T = a.state + (size_t)a.BH * kD4 * kDV;
@@ -332,20 +347,20 @@ hipError_t launch(const PrefillArgs& a) {
   hipEvent_t* ev = a.events;
   if (ev) (void)hipEventRecord(ev[0], a.stream);
   if (pl.nseg > 1) {
-    hipLaunchKernelGGL((prefill_fb_kernel<NT, C, false, IT>), dim3(a.BH * (pl.nseg - 1) * kNFB), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((prefill_fb_kernel<NT, KD, C, false, IT>), dim3(a.BH * (pl.nseg - 1) * kNFB), dim3(256), 0, a.stream,
                        q, k, v, (float*)nullptr, (const float*)nullptr, (const float*)nullptr, 1, W_S, W_T, pl.nseg,
                        a.BH, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
     if (ev) (void)hipEventRecord(ev[1], a.stream);
     if (hipError_t e = launch_segment_scan(st_S, st_T, W_S, W_T, kD4, pl.nseg, a.BH, a.stream)) return e;
     if (ev) (void)hipEventRecord(ev[2], a.stream);
-    hipLaunchKernelGGL((prefill_fb_kernel<NT, C, true, IT>), dim3(a.BH * pl.nseg * kNFB), dim3(256), 0, a.stream, q, k,
+    hipLaunchKernelGGL((prefill_fb_kernel<NT, KD, C, true, IT>), dim3(a.BH * pl.nseg * kNFB), dim3(256), 0, a.stream, q, k,
                        v, Yp, W_S, W_T, pl.nseg, st_S, st_T, 1, a.BH, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
   } else {
     if (ev) {
       (void)hipEventRecord(ev[1], a.stream);
       (void)hipEventRecord(ev[2], a.stream);
     }
-    hipLaunchKernelGGL((prefill_fb_kernel<NT, C, true, IT>), dim3(a.BH * kNFB), dim3(256), 0, a.stream, q, k, v, Yp,
+    hipLaunchKernelGGL((prefill_fb_kernel<NT, KD, C, true, IT>), dim3(a.BH * kNFB), dim3(256), 0, a.stream, q, k, v, Yp,
                        st_S, st_T, 1, st_S, st_T, 1, a.BH, a.N, 1, pl.chunks_per_seg, inv_a);
   }
   const size_t rows = (size_t)a.BH * a.N;
@@ -355,32 +370,42 @@ hipError_t launch(const PrefillArgs& a) {
   return hipGetLastError();
 }
 
-template <int NT, int C>
+template <int NT, int KD, int C>
 hipError_t launch_c(const PrefillArgs& a) {
-  if (a.in_bf16) return a.out_bf16 ? launch<NT, C, uint16_t, uint16_t>(a) : launch<NT, C, uint16_t, float>(a);
-  return a.out_bf16 ? launch<NT, C, float, uint16_t>(a) : launch<NT, C, float, float>(a);
+  if (a.in_bf16) return a.out_bf16 ? launch<NT, KD, C, uint16_t, uint16_t>(a) : launch<NT, KD, C, uint16_t, float>(a);
+  return a.out_bf16 ? launch<NT, KD, C, float, uint16_t>(a) : launch<NT, KD, C, float, float>(a);
 }
 
-template <int NT>
+template <int NT, int KD>
 hipError_t launch_n(const PrefillArgs& a) {
   switch (a.chunk) {
-    case 32: return launch_c<NT, 32>(a);
-    case 64: return launch_c<NT, 64>(a);
+    case 32: return launch_c<NT, KD, 32>(a);
+    case 64: return launch_c<NT, KD, 64>(a);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace fb
 
-int prefill_fb_blocks(int n) { return fb::blocks_of(n); }
+int prefill_fb_blocks(int d, int n) { return fb::blocks_of(d, n); }
 
-size_t prefill_fb_output_floats(int BH, int N, int n) { return (size_t)fb::blocks_of(n) * BH * N * (kDV + 1); }
+size_t prefill_fb_output_floats(int BH, int N, int d, int n) {
+  return (size_t)fb::blocks_of(d, n) * BH * N * (kDV + 1);
+}
 
 hipError_t launch_prefill_fb(const PrefillArgs& a) {
-  switch (a.n) {
-    case 4: return fb::launch_n<4>(a);
-    case 5: return fb::launch_n<5>(a);
-    case 6: return fb::launch_n<6>(a);
+  if (a.d == 16) {
+    switch (a.n) {
+      case 4: return fb::launch_n<4, 16>(a);
+      case 5: return fb::launch_n<5, 16>(a);
+      case 6: return fb::launch_n<6, 16>(a);
+    }
+  } else if (a.d == 32 || a.d == 64) {
+    switch (a.n) {
+      case 1: return a.d == 32 ? fb::launch_n<1, 32>(a) : fb::launch_n<1, 64>(a);
+      case 2: return a.d == 32 ? fb::launch_n<2, 32>(a) : fb::launch_n<2, 64>(a);
+      case 3: return a.d == 32 ? fb::launch_n<3, 32>(a) : fb::launch_n<3, 64>(a);
+    }
   }
   return hipErrorInvalidValue;
 }

@@ -83,6 +83,19 @@ def test_workspace_sizing_high_orders(rsp, n, D, blocks):
     assert rsp.prefill_workspace_bytes(64, 8, 100, n, 64) == blocks * 512 * 100 * 65 * 4  # one segment
 
 
+@pytest.mark.parametrize("d,n,D,blocks", [(32, 3, 561, 4), (64, 3, 2145, 13), (64, 2, 65, 1), (32, 1, 1, 1)])
+def test_workspace_sizing_wide_heads(rsp, d, n, D, blocks):
+    """d = 32, 64 (n <= 3) run feature-blocked: segment sums of D x 65 floats per segment plus
+    one block of 65 floats per head-token per 176-row feature block."""
+    assert rsp.state_width(d, n) == D
+    BH, N = 2, 333
+    ws = rsp.prefill_workspace_bytes(1, 2, N, n, 32, d=d)
+    out = blocks * BH * N * 65 * 4
+    nseg = (ws - out) // (BH * D * 65 * 4)
+    assert ws == out + nseg * BH * D * 65 * 4 and nseg >= 1
+    assert BH * max(nseg, 1) * blocks <= 512
+
+
 def test_workspace_sizing(rsp):
     # one segment per head when the heads alone fill the GPU: no workspace
     assert rsp.prefill_workspace_bytes(64, 8, 4096, 3, 64) == 0
@@ -112,9 +125,13 @@ def test_invalid_arguments_are_rejected_before_launch(rsp):
     lib = rsp.raw_library()
     assert _prefill_rc(lib) == -1                       # NULL pointers
     assert b"NULL" in lib.taylor_last_error()
-    assert _prefill_rc(lib, d=32) == -2                 # shape not built
+    assert _prefill_rc(lib, d=24) == -2                 # shape not built
     assert _prefill_rc(lib, d_v=128) == -2
     assert _prefill_rc(lib, n=7) == -2                  # orders up to 5 (n <= 6) are built
+    assert _prefill_rc(lib, d=32, n=4) == -2            # d = 32, 64: n <= 3
+    assert _prefill_rc(lib, d=64, chunk=128, ind=1) == -2
+    assert _prefill_rc(lib, d=48) == -2
+    assert _prefill_rc(lib, d=64, n=3) == -1            # built: fails on the NULL pointers instead
     assert _prefill_rc(lib, n=0) == -2
     assert _prefill_rc(lib, n=4, chunk=128, ind=1) == -2   # n = 4..6: chunk 32 or 64
     assert _prefill_rc(lib, n=6, chunk=128, ind=1) == -2

@@ -41,7 +41,7 @@ def to_dev(x, dtype):
 def run_prefill(rsp, q, k, v, n, a, chunk, dtype, out_dtype=torch.float32, state=None):
     B, H = q.shape[:2]
     if state is None:
-        state = rsp.new_state(B, H, n, device=DEV)
+        state = rsp.new_state(B, H, n, d=q.shape[-1], device=DEV)
     o = rsp.prefill(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), state, n, a, chunk=chunk,
                     out_dtype=out_dtype)
     torch.cuda.synchronize()
@@ -147,6 +147,31 @@ def test_prefill_high_order_vs_oracle(rsp, n, dtype, chunk):
     scale = np.abs(A).max()
     assert np.abs(S - A[..., :64]).max() <= 1e-5 * scale
     assert np.abs(T - A[..., 64]).max() <= 1e-5 * scale
+
+
+@pytest.mark.parametrize("d", [32, 64])
+@pytest.mark.parametrize("n", [1, 2, 3])
+@pytest.mark.parametrize("dtype,chunk", [("f32", 32), ("bf16", 64)])
+def test_wide_heads_vs_oracle(rsp, d, n, dtype, chunk):
+    """Head dimensions 32 and 64 (state widths 1/33/561 and 1/65/2,145 rows, in 176-row
+    feature blocks): ragged prefill cut into segments, final state, then decode steps
+    continuing from it, all against the oracle; a = 1.3."""
+    say("wide heads", d, n, dtype, chunk)
+    a, N, steps = 1.3, 333, 5
+    q, k, v = TI.make_qkv(140 + d + n, 1, 2, N + steps, d, 64, dtype=dtype)
+    ref = oracle.taylor_direct(q, k, v, n, a)
+    got, st = run_prefill(rsp, q[:, :, :N], k[:, :, :N], v[:, :, :N], n, a, chunk, dtype)
+    assert oracle.rel_err_rowwise(got, ref[:, :, :N]) <= TOL["f32"]  # float32 arithmetic for both input types
+    S, T = (x.cpu().numpy().astype(np.float64) for x in rsp.state_views(st, 1, 2, n, d=d))
+    A = oracle_state(k[:, :, :N], v[:, :, :N], n)
+    scale = np.abs(A).max()
+    assert np.abs(S - A[..., :64]).max() <= 1e-5 * scale
+    assert np.abs(T - A[..., 64]).max() <= 1e-5 * scale
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    outs = [rsp.decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(), st, n, a)
+            for t in range(N, N + steps)]
+    dec = torch.stack(outs, dim=2).cpu().numpy().astype(np.float64)
+    assert oracle.rel_err_rowwise(dec, ref[:, :, N:]) <= TOL["f32"]
 
 
 @pytest.mark.parametrize("n", [5, 6])
