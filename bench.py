@@ -243,6 +243,45 @@ def order_sweep(torch, rsp, dev, reps=10):
             "per_n": out}
 
 
+def wide_head(torch, rsp, dev):
+    """d = 64, n = 3 (2,145 x 65 floats per head): decode for B=64, H=8 (a 286 MB state,
+    about the size of the Infinity Cache) and a float32 prefill of B=2, H=8, N=4096."""
+    d, n, dv, a = 64, 3, DECODE["d_v"], DECODE["a"]
+    B, H, steps = DECODE["B"], DECODE["H"], 20
+    g = torch.Generator(device=dev).manual_seed(1008)
+    st = rsp.new_state(B, H, n, d=d, device=dev)
+    qs = torch.randn(steps, B, H, d, device=dev, generator=g)
+    ks = torch.randn(steps, B, H, d, device=dev, generator=g)
+    vs = torch.randn(steps, B, H, dv, device=dev, generator=g)
+    qs, ks = qs / qs.norm(dim=-1, keepdim=True), ks / ks.norm(dim=-1, keepdim=True)
+    out = torch.empty(B, H, dv, device=dev)
+    it = iter(range(10 ** 9))
+
+    def step():
+        s = next(it) % steps
+        rsp.decode(qs[s], ks[s], vs[s], st, n, a, out=out)
+
+    ms_d = _time_calls(torch, step, steps)
+    D = state_width(d, n)
+    bytes_step = B * H * (2 * 4.0 * D * (dv + 1) + 4.0 * (2 * d + 2 * dv))
+    c = ORDER_SWEEP
+    q, k, v = _gpu_inputs(torch, dev, c["B"], c["H"], c["N"], d, dv, 1009, torch.float32)
+    ws = torch.empty(max(rsp.prefill_workspace_bytes(c["B"], c["H"], c["N"], n, 32, d=d) // 4, 1), device=dev)
+    o = torch.empty(c["B"], c["H"], c["N"], dv, device=dev)
+
+    def call():
+        s2 = rsp.new_state(c["B"], c["H"], n, d=d, device=dev)
+        rsp.prefill(q, k, v, s2, n, a, chunk=32, out=o, workspace=ws)
+
+    ms_p = _time_calls(torch, call, 3, warmup=1)
+    return {"workload": f"d=64 n=3 ({D} state rows): decode B={B} H={H} ({B * H * D * (dv + 1) * 4 / 1e6:.0f} MB "
+                        f"state), prefill B={c['B']} H={c['H']} N={c['N']} float32, chunk 32",
+            "decode_us_per_step": ms_d * 1e3,
+            "decode_roofline": {"bound": "hbm", "achieved": bytes_step / (ms_d * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s", "frac": bytes_step / (ms_d * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "prefill_ms": ms_p, "prefill_tokens_per_s": c["B"] * c["N"] / (ms_p * 1e-3)}
+
+
 def decode_high_order(torch, rsp, dev, n=5, steps=20):
     """Decode at n = 5 (4,845 x 65 floats per head) for B=64, H=8: a 645 MB state,
     larger than the Infinity Cache, streamed once per step.  The state starts empty
@@ -433,10 +472,11 @@ def main():
                          "algorithmic_bytes_per_step": dbytes},
         }
     if args.only == "all" and not args.no_secondary:
-        print("[bench] order sweep n=1..6, long prefill, decode n=5", file=sys.stderr, flush=True)
+        print("[bench] order sweep n=1..6, long prefill, decode n=5, d=64 lines", file=sys.stderr, flush=True)
         result["order_sweep"] = order_sweep(torch, rsp, dev)
         result["long_prefill"] = long_prefill(torch, rsp, dev)
         result["decode_n5"] = decode_high_order(torch, rsp, dev)
+        result["wide_head_d64"] = wide_head(torch, rsp, dev)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (float64 oracle, sampled rows)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(host)

@@ -14,8 +14,9 @@
  *
  * Conventions shared by every call
  * --------------------------------
- * - Supported shapes: d = 16, d_v = 64, n in {1, ..., 6} (state widths
- *   D = 1, 17, 153, 969, 4845, 20349; section 5.8 discusses orders up to 6).
+ * - Supported shapes: d_v = 64 with d = 16 and n in {1, ..., 6} (state widths
+ *   D = 1, 17, 153, 969, 4845, 20349), or d = 32, 64 and n in {1, 2, 3}
+ *   (D = 1, 33, 561 and 1, 65, 2145); section 5.8 discusses both directions.
  *   Anything else returns TAYLOR_EUNSUPPORTED without launching.
  * - Tensors are dense, row-major, on the current HIP device:
  *     q, k : [B, H, N, d]       v, o : [B, H, N, d_v]      (decode: N = 1)
@@ -85,8 +86,9 @@ int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStre
 
 /* Bytes of device workspace taylor_attn_prefill needs for these sizes (0 when
  * the sequence fits one segment and n <= 3).  Host only; -1 cast to size_t on
- * error.  For n >= 4 it includes one block of (d_v + 1) floats per head-token
- * per 176-row feature block (6, 28, 116 blocks for n = 4, 5, 6). */
+ * error.  For the feature-blocked shapes (d = 16 with n >= 4, and d = 32, 64)
+ * it includes one block of (d_v + 1) floats per head-token per 176-row
+ * feature block. */
 size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n, int chunk);
 
 /* Chunked prefill (section 3.5): for every head and every t in [0, N)
@@ -98,14 +100,16 @@ size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n
  *   q, k, v : device, in_dtype (TAYLOR_F32 or TAYLOR_BF16); o : device, out_dtype.
  *   N >= 0 (N = 0 is a no-op), any N (the last chunk may be partial).
  *   a > 0 : temperature.
- *   chunk : n = 1..3: 32 or 64 for TAYLOR_F32 inputs; 32, 64 or 128 for
- *           TAYLOR_BF16.  n = 4..6: 32 or 64 for either input type.
- *   in_dtype selects the matrix-core arithmetic for n = 1..3: float32 inputs
- *   use float32 MFMA throughout; bfloat16 inputs use bfloat16 MFMA with
- *   float32 accumulation and a float32 state.  n = 4..6 compute in float32
- *   for both input types (bfloat16 inputs are widened); their 969-, 4845- or
- *   20349-row states are split into 6, 28 or 116 blocks of 176 rows handled
- *   by separate workgroups, and the workspace then also holds each block's
+ *   chunk : d = 16, n = 1..3: 32 or 64 for TAYLOR_F32 inputs; 32, 64 or 128
+ *           for TAYLOR_BF16.  d = 16 with n = 4..6, and d = 32, 64: 32 or 64
+ *           for either input type.
+ *   in_dtype selects the matrix-core arithmetic at d = 16, n = 1..3: float32
+ *   inputs use float32 MFMA throughout; bfloat16 inputs use bfloat16 MFMA
+ *   with float32 accumulation and a float32 state.  d = 16 with n = 4..6, and
+ *   d = 32, 64, compute in float32 for both input types (bfloat16 inputs are
+ *   widened); their states are split into blocks of 176 rows handled by
+ *   separate workgroups (6, 28, 116 blocks for d = 16, n = 4, 5, 6; 4 and 13
+ *   for n = 3 at d = 32, 64), and the workspace then also holds each block's
  *   share of the outputs.
  *   workspace : device, at least taylor_prefill_workspace_bytes(...) bytes
  *   (may be NULL when that is 0); it is scratch, its contents are undefined
