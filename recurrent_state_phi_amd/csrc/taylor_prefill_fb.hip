@@ -69,10 +69,10 @@ template <int C, int KD>
 struct Lds {
   float Xq[C][KD + 1];  // column KD: 1 (the factor of unused coordinate slots)
   float Xk[C][KD + 1];  // column KD: 1, or 0 for a padding token
-  float V[C][kDV + 16];  // row stride 80 floats: the 4 lane groups of an MFMA operand read hit different banks
+  float VT[kDV][C + 4];  // V transposed (token index fastest; 16-byte aligned rows)
   float PhQ[C][kPS];
-  float PhK[C][kPS];
-  float P[C][C + 1];
+  float PhKT[kBF][C + 4];  // key features, feature-major (token index fastest)
+  float P[C][C + 4];
   float Ts[kBF];
 };
 
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
 #pragma unroll
     for (int e = 0; e < NLV; ++e) {
       const int i = tid + 256 * e, tok = i / kDV, j = i % kDV;
-      L.V[tok][j] = tok < nv ? rv[e] : 0.0f;
+      L.VT[j][tok] = tok < nv ? rv[e] : 0.0f;
     }
     if (tid < C) {
       L.Xk[tid][KD] = tid < nv ? 1.0f : 0.0f;  // the constant feature of a padding token is 0
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
           fk *= L.Xk[tok][fidx[p]];
           if (FULL) fq *= L.Xq[tok][fidx[p]];
         }
-        L.PhK[tok][tid] = fk;
+        L.PhKT[tid][tok] = fk;
         if (FULL) L.PhQ[tok][tid] = fq;
       }
     }
@@ -254,7 +254,15 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
           for (int r = 0; r < 4; ++r) y = mfma_f32_k4(a4[r], Sacc[ft][r], y);
         }
         if (fbk == 0) {  // uniform
-          for (int st = 0; st < C / 4; ++st) y = mfma_f32_k4(L.P[tok][4 * st + g], L.V[4 * st + g][col], y);
+          // k-slot order: lane group g takes tokens g C/4 .. g C/4 + C/4 - 1, so
+          // its operands for four k-steps are 16 contiguous bytes
+          for (int s4 = 0; s4 < C / 16; ++s4) {
+            const int k0 = g * (C / 4) + 4 * s4;
+            const f32x4 a4 = *reinterpret_cast<const f32x4*>(&L.P[tok][k0]);
+            const f32x4 b4 = *reinterpret_cast<const f32x4*>(&L.VT[col][k0]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y = mfma_f32_k4(a4[r], b4[r], y);
+          }
         }
         // lane holds Y[token 16mt + 4g + r][col]
 #pragma unroll
@@ -279,15 +287,25 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
 
     // ---- state update: S_fb += phi(K)_fb^T V (MFMA), T_fb += phi(K)_fb^T 1
     //      (padding tokens have zero features, the constant one included)
-    for (int st = 0; st < C / 4; ++st) {
-      const float b = L.V[4 * st + g][col];
+    //      k-slot order as in the diagonal block: lane group g takes tokens
+    //      g C/4 .. g C/4 + C/4 - 1, four k-steps per 16-byte read
+    for (int s4 = 0; s4 < C / 16; ++s4) {
+      const int k0 = g * (C / 4) + 4 * s4;
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(&L.VT[col][k0]);
 #pragma unroll
-      for (int ft = 0; ft < kFT; ++ft) Sacc[ft] = mfma_f32_k4(L.PhK[4 * st + g][16 * ft + li], b, Sacc[ft]);
+      for (int ft = 0; ft < kFT; ++ft) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&L.PhKT[16 * ft + li][k0]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Sacc[ft] = mfma_f32_k4(a4[r], b4[r], Sacc[ft]);
+      }
     }
     if (tid < kBF) {
       float ts = 0.0f;
-#pragma unroll 8
-      for (int tok = 0; tok < C; ++tok) ts += L.PhK[tok][tid];
+#pragma unroll
+      for (int t4 = 0; t4 < C; t4 += 4) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(&L.PhKT[tid][t4]);
+        ts += x4[0] + x4[1] + x4[2] + x4[3];
+      }
       treg += ts;
     }
     __syncthreads();
