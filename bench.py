@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
 
 PREFILL = dict(B=4, H=8, N=8192, d=16, d_v=64, n=3, a=1.0, chunk=64)
 DECODE = dict(B=64, H=8, N0=65536, steps=256, d=16, d_v=64, n=3, a=1.0)
@@ -235,8 +236,17 @@ def order_sweep(torch, rsp, dev, reps=10):
 
         ms = _time_calls(torch, call, reps if n < 5 else 3, warmup=2 if n < 5 else 1)
         err = float((o.double() - ref).norm() / ref.norm())
+        # algorithmic work of the whole call (float32 in and out) and its binding roofline
+        D = state_width(c["d"], n)
+        ht = B * H * N
+        flops = ht * (4.0 * D * (c["d_v"] + 1) + (chunk + 1) * (c["d"] + c["d_v"] + 1) + 2.0 * D)
+        nbytes = ht * 4.0 * (2 * c["d"] + 2 * c["d_v"]) + B * H * 4.0 * D * (c["d_v"] + 1)
+        t_mfma, t_hbm = flops / (FP32_MFMA_PEAK_TFLOPS * 1e12), nbytes / (HBM_PEAK_GBS * 1e9)
+        bound = "fp32 mfma" if t_mfma > t_hbm else "hbm"
         out[f"n{n}"] = {"tokens_per_s": B * N / (ms * 1e-3), "ms": ms, "chunk": chunk,
-                        "state_rows": state_width(c["d"], n), "err_vs_softmax_frobenius": err}
+                        "state_rows": D, "err_vs_softmax_frobenius": err,
+                        "roofline": {"bound": bound, "frac": max(t_mfma, t_hbm) / (ms * 1e-3),
+                                     "algorithmic_flops": flops, "algorithmic_bytes": nbytes}}
         del ws, o
     return {"workload": "order sweep B=2 H=8 N=4096 d=16 d_v=64 a=1, float32 q/k/v/out, normalised Gaussian q,k "
                         "(n = 1..4 configured; n = 5, 6 added)",
