@@ -226,7 +226,7 @@ def order_sweep(torch, rsp, dev, reps=10):
     del s
     out = {}
     for n in (1, 2, 3, 4, 5, 6):  # n = 5, 6 go beyond the configured sweep
-        chunk = 64 if n < 4 else 32
+        chunk = 64 if n < 3 else 32
         ws = torch.empty(max(rsp.prefill_workspace_bytes(B, H, N, n, chunk) // 4, 1), device=dev)
         o = torch.empty(B, H, N, c["d_v"], device=dev)
 

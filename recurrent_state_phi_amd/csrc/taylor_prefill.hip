@@ -665,13 +665,11 @@ static hipError_t launch_prefill_n(const PrefillArgs& a) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {
+  if (a.d == kD && a.n == 3 && a.in_bf16 && (a.chunk == 64 || a.chunk == 128)) return launch_prefill_n3_bf16(a);
   if (prefill_uses_fb(a.d, a.n)) return launch_prefill_fb(a);
   switch (a.n) {
     case 1: return launch_prefill_n<1>(a);
     case 2: return launch_prefill_n<2>(a);
-    case 3:
-      if (a.in_bf16 && (a.chunk == 64 || a.chunk == 128)) return launch_prefill_n3_bf16(a);
-      return launch_prefill_n<3>(a);
   }
   return hipErrorInvalidValue;
 }

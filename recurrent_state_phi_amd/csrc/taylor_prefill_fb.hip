@@ -74,6 +74,7 @@ struct Lds {
   float PhKT[kBF][C + 4];  // key features, feature-major (token index fastest)
   float P[C][C + 4];
   float Ts[kBF];
+  float Yd[C];  // normaliser of each token (single-block states only)
 };
 
 template <typename IT> __device__ __forceinline__ float ld(const IT* p, size_t i) { return Elem<IT>::load(p, i); }
@@ -90,9 +91,10 @@ __device__ __forceinline__ float poly(float y) {
   return r;
 }
 
-template <int NT, int KD, int C, bool FULL, typename IT>
+template <int NT, int KD, int C, bool FULL, typename IT, typename TOUT>
 __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const IT* __restrict__ q, const IT* __restrict__ k,
                                                          const IT* __restrict__ v, float* __restrict__ Yp,
+                                                         TOUT* __restrict__ o,
                                                          const float* __restrict__ pre_S,
                                                          const float* __restrict__ pre_T, int pre_slots,
                                                          float* __restrict__ dst_S, float* __restrict__ dst_T,
@@ -240,9 +242,29 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
     }
     __syncthreads();
 
-    // ---- this block's share of the outputs: Y = phi_hat(Q)_fb S_fb (+ P [V, 1])
+    // ---- this block's share of the outputs: Y = phi_hat(Q)_fb S_fb (+ P [V, 1]).
+    //      A state that fits one block (n = 3 at d = 16, n <= 2 at d = 32, 64)
+    //      writes o = Y[:d_v] / Y[d_v] directly; otherwise the block's share of
+    //      the unnormalised outputs goes to the workspace for the combine pass.
     if constexpr (FULL) {
-      float* yrow = Yp + ((size_t)fbk * BH * N + base) * (kDV + 1);
+      // the block's share of the normaliser first: phi_hat(q)_fb . T_fb, plus
+      // the row sum of P for block 0; 256 / C consecutive threads per token
+      constexpr int TPT = 256 / C;
+      {
+        const int tok = tid / TPT, part = tid % TPT;
+        float yd = 0.0f;
+        for (int fl = part; fl < kBF; fl += TPT) yd += L.PhQ[tok][fl] * L.Ts[fl];
+        if (fbk == 0) {  // uniform
+          for (int tk = part; tk < C; tk += TPT) yd += L.P[tok][tk];
+        }
+#pragma unroll
+        for (int off = 1; off < TPT; off <<= 1) yd += __shfl_xor(yd, off);
+        if (part == 0) {
+          if constexpr (kNFB == 1) L.Yd[tok] = yd;
+          else if (tok < nv) Yp[((size_t)fbk * BH * N + base + tok) * (kDV + 1) + kDV] = yd;
+        }
+      }
+      if constexpr (kNFB == 1) __syncthreads();
 #pragma unroll
       for (int mt = 0; mt < NTT; ++mt) {
         const int tok = 16 * mt + li;
@@ -268,21 +290,12 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * mt + 4 * g + r;
-          if (t < nv) yrow[(size_t)t * (kDV + 1) + col] = y[r];
+          if (t < nv) {
+            if constexpr (kNFB == 1) Elem<TOUT>::store(o, (base + t) * kDV + col, y[r] / L.Yd[t]);
+            else Yp[((size_t)fbk * BH * N + base + t) * (kDV + 1) + col] = y[r];
+          }
         }
       }
-      // the block's share of the normaliser: phi_hat(q)_fb . T_fb, plus the row
-      // sum of P for block 0; 256 / C consecutive threads per token
-      constexpr int TPT = 256 / C;
-      const int tok = tid / TPT, part = tid % TPT;
-      float yd = 0.0f;
-      for (int fl = part; fl < kBF; fl += TPT) yd += L.PhQ[tok][fl] * L.Ts[fl];
-      if (fbk == 0) {  // uniform
-        for (int tk = part; tk < C; tk += TPT) yd += L.P[tok][tk];
-      }
-#pragma unroll
-      for (int off = 1; off < TPT; off <<= 1) yd += __shfl_xor(yd, off);
-      if (part == 0 && tok < nv) yrow[(size_t)tok * (kDV + 1) + kDV] = yd;
     }
 
     // ---- state update: S_fb += phi(K)_fb^T V (MFMA), T_fb += phi(K)_fb^T 1
@@ -365,25 +378,29 @@ hipError_t launch(const PrefillArgs& a) {
   hipEvent_t* ev = a.events;
   if (ev) (void)hipEventRecord(ev[0], a.stream);
   if (pl.nseg > 1) {
-    hipLaunchKernelGGL((prefill_fb_kernel<NT, KD, C, false, IT>), dim3(a.BH * (pl.nseg - 1) * kNFB), dim3(256), 0, a.stream,
-                       q, k, v, (float*)nullptr, (const float*)nullptr, (const float*)nullptr, 1, W_S, W_T, pl.nseg,
-                       a.BH, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
+    hipLaunchKernelGGL((prefill_fb_kernel<NT, KD, C, false, IT, TOUT>), dim3(a.BH * (pl.nseg - 1) * kNFB), dim3(256), 0,
+                       a.stream, q, k, v, (float*)nullptr, (TOUT*)nullptr, (const float*)nullptr,
+                       (const float*)nullptr, 1, W_S, W_T, pl.nseg, a.BH, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
     if (ev) (void)hipEventRecord(ev[1], a.stream);
     if (hipError_t e = launch_segment_scan(st_S, st_T, W_S, W_T, kD4, pl.nseg, a.BH, a.stream)) return e;
     if (ev) (void)hipEventRecord(ev[2], a.stream);
-    hipLaunchKernelGGL((prefill_fb_kernel<NT, KD, C, true, IT>), dim3(a.BH * pl.nseg * kNFB), dim3(256), 0, a.stream, q, k,
-                       v, Yp, W_S, W_T, pl.nseg, st_S, st_T, 1, a.BH, a.N, pl.nseg, pl.chunks_per_seg, inv_a);
+    hipLaunchKernelGGL((prefill_fb_kernel<NT, KD, C, true, IT, TOUT>), dim3(a.BH * pl.nseg * kNFB), dim3(256), 0,
+                       a.stream, q, k, v, Yp, static_cast<TOUT*>(a.o), W_S, W_T, pl.nseg, st_S, st_T, 1, a.BH, a.N,
+                       pl.nseg, pl.chunks_per_seg, inv_a);
   } else {
     if (ev) {
       (void)hipEventRecord(ev[1], a.stream);
       (void)hipEventRecord(ev[2], a.stream);
     }
-    hipLaunchKernelGGL((prefill_fb_kernel<NT, KD, C, true, IT>), dim3(a.BH * kNFB), dim3(256), 0, a.stream, q, k, v, Yp,
-                       st_S, st_T, 1, st_S, st_T, 1, a.BH, a.N, 1, pl.chunks_per_seg, inv_a);
+    hipLaunchKernelGGL((prefill_fb_kernel<NT, KD, C, true, IT, TOUT>), dim3(a.BH * kNFB), dim3(256), 0, a.stream, q, k,
+                       v, Yp, static_cast<TOUT*>(a.o), st_S, st_T, 1, st_S, st_T, 1, a.BH, a.N, 1, pl.chunks_per_seg,
+                       inv_a);
   }
-  const size_t rows = (size_t)a.BH * a.N;
-  hipLaunchKernelGGL((combine_kernel<kNFB, TOUT>), dim3((unsigned)((rows * kDV + 255) / 256)), dim3(256), 0, a.stream, Yp,
-                     static_cast<TOUT*>(a.o), rows);
+  if constexpr (kNFB > 1) {
+    const size_t rows = (size_t)a.BH * a.N;
+    hipLaunchKernelGGL((combine_kernel<kNFB, TOUT>), dim3((unsigned)((rows * kDV + 255) / 256)), dim3(256), 0, a.stream,
+                       Yp, static_cast<TOUT*>(a.o), rows);
+  }
   if (ev) (void)hipEventRecord(ev[3], a.stream);
   return hipGetLastError();
 }
@@ -408,12 +425,14 @@ hipError_t launch_n(const PrefillArgs& a) {
 int prefill_fb_blocks(int d, int n) { return fb::blocks_of(d, n); }
 
 size_t prefill_fb_output_floats(int BH, int N, int d, int n) {
-  return (size_t)fb::blocks_of(d, n) * BH * N * (kDV + 1);
+  const int nb = fb::blocks_of(d, n);
+  return nb > 1 ? (size_t)nb * BH * N * (kDV + 1) : 0;  // one block writes o directly
 }
 
 hipError_t launch_prefill_fb(const PrefillArgs& a) {
   if (a.d == 16) {
     switch (a.n) {
+      case 3: return fb::launch_n<3, 16>(a);
       case 4: return fb::launch_n<4, 16>(a);
       case 5: return fb::launch_n<5, 16>(a);
       case 6: return fb::launch_n<6, 16>(a);

@@ -454,7 +454,7 @@ def test_order_sweep_workload(rsp, n):
     say("order sweep", n)
     B, H, N = 2, 8, 4096
     q, k, v = TI.make_qkv(TI.SEEDS["order_sweep"], B, H, N, 16, 64)
-    got, _ = run_prefill(rsp, q, k, v, n, 1.0, 64 if n < 4 else 32, "f32")
+    got, _ = run_prefill(rsp, q, k, v, n, 1.0, 64 if n < 3 else 32, "f32")
     rows = sample_rows(B, H, N, 256, 64)
     ref = oracle.taylor_direct(q, k, v, n, 1.0, rows=rows)
     assert oracle.rel_err_rowwise(got.reshape(-1, 64)[rows], ref) <= TOL["f32"]
