@@ -921,26 +921,32 @@ __device__ __forceinline__ void segment_sum_regs(unsigned char* lds_raw, const O
   // (column 8 = tile 8, row 8: lane 40, element 0)
   Tp[0] -= (lane == 40) ? (float)pad : 0.0f;
 
-  // ---- add up the waves' partial states in LDS, one wave at a time, then
-  //      hand every wave the tiles it owns
+  // ---- add up the waves' partial states in LDS, then hand every wave the
+  //      tiles it owns.  The 41 tiles form NW parts (part of tile t:
+  //      t * NW / 41); in round r wave w adds its partial of part
+  //      (w + r) mod NW (round 0 stores it), so every round keeps all waves
+  //      busy on different parts and each part is summed in a fixed order
+  //      (waves p, p - 1, ..., p - NW + 1 mod NW).
+  static_assert((NW & (NW - 1)) == 0, "NW is a power of two");
   f32x4* R = reinterpret_cast<f32x4*>(lds_raw);  // [41 tiles][64 lanes]
   auto at = [&](int t) { return R + t * 64 + lane; };
+  auto part = [](int t) { return t * NW / 41; };
   __syncthreads();  // the LDS area may still be in use by earlier code
-  if (w == 0) {  // uniform
+#pragma unroll
+  for (int r = 0; r < NW; ++r) {
+    const int pr = (w + r) & (NW - 1);  // uniform
+    if (r > 0) __syncthreads();
 #pragma unroll
     for (int f = 0; f < 10; ++f)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) *at(4 * f + ct) = F[f][ct];
-    *at(40) = Tp;
-  }
-  for (int src = 1; src < NW; ++src) {
-    __syncthreads();
-    if (w == src) {  // uniform
-#pragma unroll
-      for (int f = 0; f < 10; ++f)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) *at(4 * f + ct) += F[f][ct];
-      *at(40) += Tp;
+      for (int ct = 0; ct < 4; ++ct)
+        if (part(4 * f + ct) == pr) {
+          if (r == 0) *at(4 * f + ct) = F[f][ct];
+          else *at(4 * f + ct) += F[f][ct];
+        }
+    if (part(40) == pr) {
+      if (r == 0) *at(40) = Tp;
+      else *at(40) += Tp;
     }
   }
   __syncthreads();
