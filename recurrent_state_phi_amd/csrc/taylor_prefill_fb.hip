@@ -134,14 +134,24 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
     if (pt && tid < kBF && F0 + tid < kD4) treg = pt[F0 + tid];
   }
 
-  // ---- this thread's feature row (tid < 176): coordinates (KD = the column
-  //      of ones for unused slots), key-side weight and query-side weight
+  // ---- this thread's feature items: (row fl of the block, quarter qt of the
+  //      chunk's tokens), items t, t + 256, t + 512 of the 4 * 176, so all
+  //      256 threads share the feature work; for each, the row's coordinates
+  //      (KD = the column of ones for unused slots) and its key- and
+  //      query-side weights, decoded once
   constexpr int NF = NT > 1 ? NT - 1 : 1;  // coordinate slots: orders up to n - 1
-  int fidx[NF];
-  float wk = 0.0f, wq = 0.0f;  // 0 for rows past the state and threads >= 176
-  {
-    const int f = F0 + tid;
-    const bool valid = tid < kBF && f < kD4;
+  constexpr int kItems = 4 * kBF;
+  constexpr int NIT = (kItems + 255) / 256;
+  int fidx[NIT][NF];
+  float wk[NIT], wq[NIT];  // 0 for rows past the state
+  int ifl[NIT], iqt[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int item = tid + 256 * it;
+    ifl[it] = item % kBF;
+    iqt[it] = item < kItems ? item / kBF : 4;  // 4: no item
+    const int f = F0 + ifl[it];
+    const bool valid = f < kD4;
     const int fr = valid ? f : 0;
     if constexpr (KD == 16 && NT == 4) {
       const uint32_t c = kTab.code[fr];
@@ -149,19 +159,19 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
       const float a2 = inv_a * inv_a;
       const float am = m == 0 ? 1.0f : m == 1 ? inv_a : m == 2 ? 0.5f * a2 : a2 * inv_a * (1.0f / 6.0f);
 #pragma unroll
-      for (int p = 0; p < NF; ++p) fidx[p] = p < m ? (int)((c >> (2 + 4 * p)) & 15) : KD;
+      for (int p = 0; p < NF; ++p) fidx[it][p] = p < m ? (int)((c >> (2 + 4 * p)) & 15) : KD;
       const float wt = kTab.weight[fr];
-      wk = valid ? wt : 0.0f;
-      wq = valid ? wt * am : 0.0f;
+      wk[it] = valid ? wt : 0.0f;
+      wq[it] = valid ? wt * am : 0.0f;
     } else {
       constexpr int MAXM = table_orders<KD>();
       const uint32_t c = row_code<KD>(fr);
       const int m = c & 7;
 #pragma unroll
-      for (int p = 0; p < NF; ++p) fidx[p] = p < m ? row_coord<KD, MAXM>(c, p) : KD;
+      for (int p = 0; p < NF; ++p) fidx[it][p] = p < m ? row_coord<KD, MAXM>(c, p) : KD;
       const float wt = row_weight<KD, MAXM>(c);
-      wk = valid ? wt : 0.0f;
-      wq = valid ? alpha_of(inv_a, c) * wt : 0.0f;
+      wk[it] = valid ? wt : 0.0f;
+      wq[it] = valid ? alpha_of(inv_a, c) * wt : 0.0f;
     }
   }
 
@@ -211,17 +221,22 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
     __syncthreads();
 
     // ---- features of the block (query side scaled by alpha_m), and P for block 0
-    if (tid < kBF) {
-#pragma unroll 4
-      for (int tok = 0; tok < C; ++tok) {
-        float fk = wk, fq = wq;
 #pragma unroll
-        for (int p = 0; p < NF; ++p) {
-          fk *= L.Xk[tok][fidx[p]];
-          if (FULL) fq *= L.Xq[tok][fidx[p]];
+    for (int it = 0; it < NIT; ++it) {
+      if (iqt[it] < 4) {
+        const int fl = ifl[it];
+#pragma unroll
+        for (int i = 0; i < C / 4; ++i) {
+          const int tok = iqt[it] * (C / 4) + i;
+          float fk = wk[it], fq = wq[it];
+#pragma unroll
+          for (int p = 0; p < NF; ++p) {
+            fk *= L.Xk[tok][fidx[it][p]];
+            if (FULL) fq *= L.Xq[tok][fidx[it][p]];
+          }
+          L.PhKT[fl][tok] = fk;
+          if (FULL) L.PhQ[tok][fl] = fq;
         }
-        L.PhKT[tid][tok] = fk;
-        if (FULL) L.PhQ[tok][tid] = fq;
       }
     }
     if (FULL && fbk == 0) {  // uniform
