@@ -595,7 +595,10 @@ PrefillPlan plan_prefill(int BH, int N, int d, int n, int chunk) {
   // workspace is larger; the size does not depend on the input type, so
   // cover both
   if (d == 16 && n == 3) p.workspace_floats = std::max(p.workspace_floats, prefill_n3_workspace_floats(BH, p.nseg));
-  if (fbk) p.workspace_floats += prefill_fb_output_floats(BH, N, d, n);
+  if (fbk) {
+    const size_t out = prefill_fb_output_floats(BH, N, d, n);
+    if (out > 0) p.workspace_floats = (p.workspace_floats + 3) / 4 * 4 + out;  // 16-byte aligned partial outputs
+  }
   return p;
 }
 

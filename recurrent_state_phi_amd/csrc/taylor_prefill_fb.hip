@@ -47,6 +47,7 @@ namespace fb {
 constexpr int kFT = 11;                      // feature tiles per block
 constexpr int kBF = 16 * kFT;                // 176 rows per block
 constexpr int kPS = kBF + 4;                 // feature row stride in LDS (16-byte aligned rows)
+constexpr int kYS = kDV + 4;                 // partial-output row: 64 values, the normaliser, padding
 // Feature blocks of the state: d = 16: 6, 28, 116 for n = 4, 5, 6;
 // d = 32: 1, 1, 4 and d = 64: 1, 1, 13 for n = 1, 2, 3.
 constexpr int blocks_of(int d, int n) { return (state_width_d(d, n) + kBF - 1) / kBF; }
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
         for (int off = 1; off < TPT; off <<= 1) yd += __shfl_xor(yd, off);
         if (part == 0) {
           if constexpr (kNFB == 1) L.Yd[tok] = yd;
-          else if (tok < nv) Yp[((size_t)fbk * BH * N + base + tok) * (kDV + 1) + kDV] = yd;
+          else if (tok < nv) Yp[((size_t)fbk * BH * N + base + tok) * kYS + kDV] = yd;
         }
       }
       if constexpr (kNFB == 1) __syncthreads();
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
           const int t = 16 * mt + 4 * g + r;
           if (t < nv) {
             if constexpr (kNFB == 1) Elem<TOUT>::store(o, (base + t) * kDV + col, y[r] / L.Yd[t]);
-            else Yp[((size_t)fbk * BH * N + base + t) * (kDV + 1) + col] = y[r];
+            else Yp[((size_t)fbk * BH * N + base + t) * kYS + col] = y[r];
           }
         }
       }
@@ -357,21 +358,25 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
 }
 
 // o = sum over blocks of the numerators / sum of the normalisers (Eq. (5)).
+// 16 threads per output row, 4 columns each (16-byte reads of the 68-float
+// partial rows); the blocks are added in order.
 template <int kNFB, typename TOUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ Yp, TOUT* __restrict__ o,
                                                       size_t rows) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows * kDV) return;
-  const size_t row = i / kDV;
-  const int c = (int)(i % kDV);
-  float num = 0.0f, den = 0.0f;
-#pragma unroll
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // (row, column quad)
+  if (i >= rows * (kDV / 4)) return;
+  const size_t row = i / (kDV / 4);
+  const int c4 = (int)(i % (kDV / 4));
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.0f;
+#pragma unroll 4
   for (int b = 0; b < kNFB; ++b) {
-    const float* y = Yp + ((size_t)b * rows + row) * (kDV + 1);
-    num += y[c];
+    const float* y = Yp + ((size_t)b * rows + row) * kYS;
+    num += *reinterpret_cast<const f32x4*>(y + 4 * c4);
     den += y[kDV];
   }
-  Elem<TOUT>::store(o, i, num / den);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) Elem<TOUT>::store(o, row * kDV + 4 * c4 + e, num[e] / den);
 }
 
 template <int NT, int KD, int C, typename IT, typename TOUT>
@@ -386,7 +391,8 @@ hipError_t launch(const PrefillArgs& a) {
   const IT* k = static_cast<const IT*>(a.k);
   const IT* v = static_cast<const IT*>(a.v);
   // workspace: [segment sums / prefixes when nseg > 1][block outputs]
-  const size_t agg = pl.nseg > 1 ? (size_t)a.BH * pl.nseg * kD4 * (kDV + 1) : 0;
+  // (rounded up to 4 floats, so the partial-output rows stay 16-byte aligned)
+  const size_t agg = pl.nseg > 1 ? ((size_t)a.BH * pl.nseg * kD4 * (kDV + 1) + 3) / 4 * 4 : 0;
   float* W_S = a.workspace;
   float* W_T = a.workspace + (size_t)a.BH * pl.nseg * kD4 * kDV;
   float* Yp = a.workspace + agg;
@@ -413,7 +419,8 @@ hipError_t launch(const PrefillArgs& a) {
   }
   if constexpr (kNFB > 1) {
     const size_t rows = (size_t)a.BH * a.N;
-    hipLaunchKernelGGL((combine_kernel<kNFB, TOUT>), dim3((unsigned)((rows * kDV + 255) / 256)), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL((combine_kernel<kNFB, TOUT>), dim3((unsigned)((rows * (kDV / 4) + 255) / 256)), dim3(256), 0,
+                       a.stream,
                        Yp, static_cast<TOUT*>(a.o), rows);
   }
   if (ev) (void)hipEventRecord(ev[3], a.stream);
@@ -441,7 +448,7 @@ int prefill_fb_blocks(int d, int n) { return fb::blocks_of(d, n); }
 
 size_t prefill_fb_output_floats(int BH, int N, int d, int n) {
   const int nb = fb::blocks_of(d, n);
-  return nb > 1 ? (size_t)nb * BH * N * (kDV + 1) : 0;  // one block writes o directly
+  return nb > 1 ? (size_t)nb * BH * N * fb::kYS : 0;  // one block writes o directly
 }
 
 hipError_t launch_prefill_fb(const PrefillArgs& a) {
