@@ -86,9 +86,9 @@ int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStre
 
 /* Bytes of device workspace taylor_attn_prefill needs for these sizes (0 when
  * the sequence fits one segment and n <= 3).  Host only; -1 cast to size_t on
- * error.  For the feature-blocked shapes (d = 16 with n >= 4, and d = 32, 64)
- * it includes one block of (d_v + 1) floats per head-token per 176-row
- * feature block. */
+ * error.  For states of several 176-row feature blocks (d = 16 with n >= 4,
+ * and n = 3 at d = 32, 64) it includes a row of d_v + 4 floats per
+ * head-token per feature block. */
 size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n, int chunk);
 
 /* Chunked prefill (section 3.5): for every head and every t in [0, N)
