@@ -388,10 +388,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # 300 untimed steps (about 20 ms of prefill): the per-call time settles only
-    # after some tens of milliseconds of sustained work (69 us in the first
-    # few milliseconds, 61-62 us from then on)
-    ap.add_argument("--warmup", type=int, default=300)
+    # 1000 untimed steps (about 60 ms of prefill): the per-call time settles
+    # only after tens of milliseconds of sustained work (69 us in the first
+    # few milliseconds, 60-61 us after 300 steps, 58.6-58.8 us after 1000)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
