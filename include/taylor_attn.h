@@ -85,7 +85,8 @@ int64_t taylor_state_numel(int d, int d_v, int n);
 int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStream_t stream);
 
 /* Bytes of device workspace taylor_attn_prefill needs for these sizes (0 when
- * the sequence fits one segment and n <= 3).  Host only; -1 cast to size_t on
+ * the sequence fits one segment and the state one 176-row block, i.e. D <= 176).
+ * Host only; -1 cast to size_t on
  * error.  For states of several 176-row feature blocks (d = 16 with n >= 4,
  * and n = 3 at d = 32, 64) it includes a row of d_v + 4 floats per
  * head-token per feature block. */
@@ -103,14 +104,15 @@ size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n
  *   chunk : d = 16, n = 1..3: 32 or 64 for TAYLOR_F32 inputs; 32, 64 or 128
  *           for TAYLOR_BF16.  d = 16 with n = 4..6, and d = 32, 64: 32 or 64
  *           for either input type.
- *   in_dtype selects the matrix-core arithmetic at d = 16, n = 1..3: float32
- *   inputs use float32 MFMA throughout; bfloat16 inputs use bfloat16 MFMA
- *   with float32 accumulation and a float32 state.  d = 16 with n = 4..6, and
- *   d = 32, 64, compute in float32 for both input types (bfloat16 inputs are
- *   widened); their states are split into blocks of 176 rows handled by
- *   separate workgroups (6, 28, 116 blocks for d = 16, n = 4, 5, 6; 4 and 13
- *   for n = 3 at d = 32, 64), and the workspace then also holds each block's
- *   share of the outputs.
+ *   Arithmetic: float32 inputs use float32 MFMA throughout.  bfloat16 inputs
+ *   use bfloat16 MFMA with float32 accumulation and a float32 state at d = 16
+ *   for n = 1, 2 (any chunk) and for n = 3 with chunk 64 or 128; everywhere
+ *   else (n = 3 with chunk 32, d = 16 with n = 4..6, d = 32 and 64) they are
+ *   widened and computed in float32.  Those float32 paths split the state into
+ *   blocks of 176 rows handled by separate workgroups (1 block for n = 3 at
+ *   d = 16; 6, 28, 116 blocks for n = 4, 5, 6; 4 and 13 for n = 3 at d = 32,
+ *   64); with more than one block the workspace also holds each block's share
+ *   of the outputs.
  *   workspace : device, at least taylor_prefill_workspace_bytes(...) bytes
  *   (may be NULL when that is 0); it is scratch, its contents are undefined
  *   afterwards (any contents are fine on entry).  o must not alias q, k, v or
