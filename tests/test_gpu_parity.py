@@ -244,6 +244,28 @@ def test_prefill_short_lengths(rsp, N):
     assert oracle.rel_err_rowwise(got, ref) <= TOL["f32"]
 
 
+@pytest.mark.parametrize("n,d,dtype,chunk", [(3, 16, "bf16", 64), (3, 16, "f32", 32), (5, 16, "f32", 32),
+                                             (1, 16, "bf16", 128), (3, 64, "bf16", 64)])
+def test_empty_calls_leave_state_unchanged(rsp, n, d, dtype, chunk):
+    """No tokens (N = 0) and no streams (B = 0): the calls succeed, return empty
+    outputs and leave an arbitrary state bit for bit as it was (Eq. (7) adds
+    nothing when there is no token)."""
+    say("empty calls", n, d, dtype, chunk)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    B, H = 2, 3
+    st = torch.randn(B * H * rsp.state_numel(d, 64, n), device=DEV)
+    before = st.clone()
+    q0 = torch.zeros(B, H, 0, d, device=DEV, dtype=tdt)
+    v0 = torch.zeros(B, H, 0, 64, device=DEV, dtype=tdt)
+    o = rsp.prefill(q0, q0.clone(), v0, st, n, 1.0, chunk=chunk)
+    st0 = torch.zeros(0, device=DEV)
+    od = rsp.decode(torch.zeros(0, H, d, device=DEV, dtype=tdt), torch.zeros(0, H, d, device=DEV, dtype=tdt),
+                    torch.zeros(0, H, 64, device=DEV, dtype=tdt), st0, n, 1.0)
+    torch.cuda.synchronize()
+    assert tuple(o.shape) == (B, H, 0, 64) and tuple(od.shape) == (0, H, 64)
+    assert torch.equal(st, before)
+
+
 @pytest.mark.parametrize("a", [0.7, 2.0, 3.3])
 @pytest.mark.parametrize("chunk", [64, 128])
 def test_bf16_prefill_temperatures(rsp, a, chunk):
