@@ -681,9 +681,6 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
       // token tile are masked to zero, the diagonal tile causally (key
       // 16 kt + 4g + r against token 16 tt + li).
       bf16x8 pb[NKB];
-      // key 16 kt + 4 g + r is kept iff 16 kt + r <= lim (one compare and one
-      // select per element, kt and r being compile-time constants)
-      const int lim = tok - 4 * g;
 #pragma unroll
       for (int kt = 0; kt < 2 * NKB; ++kt) {
         const int key0 = 16 * kt + li;
@@ -693,7 +690,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float p = fmaf(s[r], fmaf(0.5f, s[r], 1.0f), 1.0f);  // s = q.k / a
-          const bool keep = 16 * kt + r <= lim;
+          const bool keep = kt < tt || (kt == tt && 4 * g + r <= li);
           pb[kt >> 1][4 * (kt & 1) + r] = f32_to_bf16(keep ? p : 0.0f);
         }
       }
