@@ -1,0 +1,80 @@
+"""Register budget of every HIP kernel, checked on the CPU.
+
+Each source is compiled for gfx950 with the library's own flags to AMD
+assembly, and the code-object metadata of every kernel is read back: no vector
+register may spill, no kernel may use scratch (private) memory, and scalar
+registers may spill into vector-register lanes only where listed below.  A
+spill that appears with a new template instance or a code change shows up
+here instead of as a slowdown on the GPU.
+"""
+import concurrent.futures as cf
+import importlib.util
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SOURCES = ["taylor_decode.hip", "taylor_prefill.hip", "taylor_prefill_n3.hip", "taylor_prefill_fb.hip"]
+
+# Scalar spills allowed per kernel (mangled-name prefix -> count).  The
+# 128-token n = 3 prefill keeps 3 scalar registers in vector-register lanes.
+SGPR_SPILL_ALLOWANCE = {"_ZN6taylor2n317prefill_n3_kernelILi128E": 3}
+
+
+def _build_module():
+    spec = importlib.util.spec_from_file_location("rsp_build", os.path.join(ROOT, "recurrent_state_phi_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _kernel_metadata(asm: str):
+    """(name, {key: int}) for every kernel in the amdhsa.kernels metadata list."""
+    start = asm.index("amdhsa.kernels:")
+    kernels, cur = [], None
+    for line in asm[start:].splitlines()[1:]:
+        if line.startswith("  - "):
+            cur = {}
+            kernels.append(cur)
+            line = "    " + line[4:]
+        elif not line.startswith("    ") and line.strip():
+            if cur is not None and not line.startswith(" "):
+                break
+        m = re.match(r"^    \.(\w+):\s+(\S+)", line)
+        if cur is not None and m:
+            cur[m.group(1)] = m.group(2)
+    return [(k["name"], k) for k in kernels if "name" in k]
+
+
+@pytest.fixture(scope="module")
+def metadata(tmp_path_factory):
+    b = _build_module()
+    if shutil.which(b.HIPCC) is None and not os.path.exists(b.HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm")
+
+    def compile_one(src):
+        dst = out / (src + ".s")
+        cmd = [b.HIPCC, "-x", "hip", *b.FLAGS, "--cuda-device-only", "-S", os.path.join(b.CSRC, src), "-o", str(dst)]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-2000:]
+        return src, _kernel_metadata(dst.read_text())
+
+    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        return dict(ex.map(compile_one, SOURCES))
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_spills_and_no_scratch(metadata, src):
+    kernels = metadata[src]
+    assert kernels, f"no kernels found in {src}"
+    bad = []
+    for name, k in kernels:
+        allow = next((n for p, n in SGPR_SPILL_ALLOWANCE.items() if name.startswith(p)), 0)
+        if int(k["vgpr_spill_count"]) != 0 or int(k["private_segment_fixed_size"]) != 0 \
+                or int(k["sgpr_spill_count"]) > allow:
+            bad.append((name, k["vgpr_spill_count"], k["sgpr_spill_count"], k["private_segment_fixed_size"]))
+    assert not bad, f"kernels that spill (name, vgpr spills, sgpr spills, scratch bytes): {bad}"
