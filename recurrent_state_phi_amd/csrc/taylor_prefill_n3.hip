@@ -605,6 +605,10 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
       const bf16x8 zeros = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
       const float pair_m = li < 8 ? 1.0f : 0.0f, const_m = li == 8 ? 1.0f : 0.0f;  // rows of tile 8
       const bool tile8 = own.tile8;  // wave-uniform
+      // The update and the state read run at raised wave priority: with two
+      // waves per SIMD, the wave in a run of matrix products issues first and
+      // the other wave's vector work fills the gaps.
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const int t8 = 32 * kb + 8 * g;
@@ -666,6 +670,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
           }
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     }
 
 #pragma unroll
@@ -738,6 +743,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
       const float kb0f = gh == 0 ? 0.5f : 1.0f;  // diagonal tile: weight 1 instead of 2
       const float cB = g >= 2 ? 1.0f : 0.0f, cC = g == 1 ? 1.0f : 0.0f;
       constexpr int kD0[4] = {0, 1, 4, 5};
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kb = 0; kb < 5; ++kb) {
         float f[8];
@@ -766,6 +772,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
         const uint4 tA = *reinterpret_cast<const uint4*>(&L.T[b][li & 1][32 * kb + 8 * g]);
         y[4] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, tA), bphi, y[4]);
       }
+      __builtin_amdgcn_s_setprio(0);
 
       // ---- epilogue (normalised and stored at the start of the next iteration,
       //      when the products have long completed)

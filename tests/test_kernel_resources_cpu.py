@@ -20,8 +20,10 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = ["taylor_decode.hip", "taylor_prefill.hip", "taylor_prefill_n3.hip", "taylor_prefill_fb.hip"]
 
 # Scalar spills allowed per kernel (mangled-name prefix -> count).  The
-# 128-token n = 3 prefill keeps 3 scalar registers in vector-register lanes.
-SGPR_SPILL_ALLOWANCE = {"_ZN6taylor2n317prefill_n3_kernelILi128E": 3}
+# 128-token n = 3 prefill keeps 7 scalar registers in vector-register lanes
+# (3 before its matrix loops ran at raised wave priority; a form of the causal
+# mask that needed 25 cost the long prefill 7%).
+SGPR_SPILL_ALLOWANCE = {"_ZN6taylor2n317prefill_n3_kernelILi128E": 7}
 
 
 def _build_module():
