@@ -262,6 +262,10 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
     //      A state that fits one block (n = 3 at d = 16, n <= 2 at d = 32, 64)
     //      writes o = Y[:d_v] / Y[d_v] directly; otherwise the block's share of
     //      the unnormalised outputs goes to the workspace for the combine pass.
+    //      With several feature blocks, the products below run at raised wave
+    //      priority: the two workgroups of a CU are then mostly in different
+    //      phases, and the one in its matrix phase issues first.
+    if constexpr (kNFB > 1) __builtin_amdgcn_s_setprio(1);
     if constexpr (FULL) {
       // the block's share of the normaliser first: phi_hat(q)_fb . T_fb, plus
       // the row sum of P for block 0; 256 / C consecutive threads per token
@@ -328,6 +332,7 @@ __global__ __launch_bounds__(256, C == 32 ? 2 : 1) void prefill_fb_kernel(const 
         for (int r = 0; r < 4; ++r) Sacc[ft] = mfma_f32_k4(a4[r], b4[r], Sacc[ft]);
       }
     }
+    if constexpr (kNFB > 1) __builtin_amdgcn_s_setprio(0);
     if (tid < kBF) {
       float ts = 0.0f;
 #pragma unroll
