@@ -1093,7 +1093,7 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
 
 // Clears the ticket counter, the error code and the nslots flags, and marks
 // the header as this kernel's.
-__global__ void clear_flags_kernel(int* sync, int nslots) {
+static __global__ void clear_flags_kernel(int* sync, int nslots) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < nslots) sync[kHdr + (size_t)i * kFlagStride] = 0;
   if (i < 3) sync[i] = i == 2 ? kN3Magic : 0;
@@ -1139,6 +1139,17 @@ hipError_t launch(const PrefillArgs& a) {
 
 }  // namespace n3
 
+#ifdef TAYLOR_N3_C128_UNIT
+// The 128-token instances live in their own translation unit, compiled with the
+// default instruction scheduler; this file's 64-token instances are compiled
+// with the one that maximises instruction-level parallelism, which pays for
+// them and not for the 128-token ones.
+hipError_t launch_prefill_n3_bf16_c128(const PrefillArgs& a) {
+  return a.out_bf16 ? n3::launch<128, uint16_t>(a) : n3::launch<128, float>(a);
+}
+#else
+hipError_t launch_prefill_n3_bf16_c128(const PrefillArgs& a);
+
 size_t prefill_n3_workspace_floats(int BH, int nseg) {
   if (nseg <= 1) return 0;
   return n3::header_words(BH, nseg) + (size_t)BH * nseg * n3::kImgFloats;
@@ -1147,9 +1158,10 @@ size_t prefill_n3_workspace_floats(int BH, int nseg) {
 hipError_t launch_prefill_n3_bf16(const PrefillArgs& a) {
   switch (a.chunk) {
     case 64: return a.out_bf16 ? n3::launch<64, uint16_t>(a) : n3::launch<64, float>(a);
-    case 128: return a.out_bf16 ? n3::launch<128, uint16_t>(a) : n3::launch<128, float>(a);
+    case 128: return launch_prefill_n3_bf16_c128(a);
   }
   return hipErrorInvalidValue;
 }
+#endif
 
 }  // namespace taylor

@@ -17,7 +17,8 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SOURCES = ["taylor_decode.hip", "taylor_prefill.hip", "taylor_prefill_n3.hip", "taylor_prefill_fb.hip"]
+SOURCES = ["taylor_decode.hip", "taylor_prefill.hip", "taylor_prefill_n3.hip", "taylor_prefill_n3_c128.hip",
+           "taylor_prefill_fb.hip"]
 
 # Scalar spills allowed per kernel (mangled-name prefix -> count).  The
 # 128-token n = 3 prefill keeps 7 scalar registers in vector-register lanes
@@ -60,7 +61,8 @@ def metadata(tmp_path_factory):
 
     def compile_one(src):
         dst = out / (src + ".s")
-        cmd = [b.HIPCC, "-x", "hip", *b.FLAGS, "--cuda-device-only", "-S", os.path.join(b.CSRC, src), "-o", str(dst)]
+        cmd = [b.HIPCC, "-x", "hip", *b.FLAGS, *b.EXTRA.get(src, []), "--cuda-device-only", "-S",
+               os.path.join(b.CSRC, src), "-o", str(dst)]
         res = subprocess.run(cmd, capture_output=True, text=True)
         assert res.returncode == 0, res.stderr[-2000:]
         return src, _kernel_metadata(dst.read_text())
