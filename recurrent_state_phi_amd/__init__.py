@@ -149,8 +149,15 @@ def _check_tensor(name, t, shape, dtype=None):
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor, n: int, a: float,
             chunk: int = 64, out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None,
-            workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """Chunked prefill; adds the tokens to ``state`` in place and returns o [B,H,N,d_v]."""
+            workspace: torch.Tensor | None = None, check: bool = False) -> torch.Tensor:
+    """Chunked prefill; adds the tokens to ``state`` in place and returns o [B,H,N,d_v].
+
+    Without ``workspace`` one is allocated for the call when the plan needs
+    it.  ``check=True`` waits for the call and raises TaylorError
+    (TAYLOR_ETIMEOUT) if a bounded wait between workgroups ran out, whichever
+    workspace was used; otherwise a caller who wants that report passes its
+    own workspace and calls :func:`prefill_check` on it later.
+    """
     B, H, N, d = q.shape
     d_v = v.shape[-1]
     _check_tensor("q", q, (B, H, N, d))
@@ -169,6 +176,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tens
     _check(_lib.taylor_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state), B, H, N, d, d_v, n,
                                     float(a), chunk, _dtype_code(q.dtype), _dtype_code(out_dtype), ws_ptr,
                                     ws_bytes, _stream_ptr(q.device)))
+    if check:
+        prefill_check(workspace)
     return out
 
 

@@ -9,7 +9,9 @@
 //  1. segment sum: the workgroup runs the state update over its segment from a
 //     zero state (Eq. (6)-(7) summed over the segment; the states are additive
 //     across chunks, section 3.5).  Segment 0 adds the caller's state to its
-//     sum.  The sum A_s is published to the workspace.
+//     sum (it is the only workgroup that reads the caller's state, which the
+//     last segment overwrites with the final state).  The sum A_s is
+//     published to the workspace.
 //  2. prefix: the segments form groups of `gs` consecutive segments.  The last
 //     segment of a group publishes the GROUP sum (its own sum plus those of
 //     the earlier members) in place of its own.  The exclusive prefix of
@@ -1019,29 +1021,33 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
   // the last member of a group publishes the group's sum, unless no group follows
   const bool leader = seg == g0 + gs - 1 && seg < nseg - 1;
 
-  // 1. the segment's own sum (not needed for the last segment)
-  Acc acc;
+  // 1. the segment's own sum (not needed for the last segment).  Segment 0
+  //    adds the caller's state to its sum before publishing it, so that it is
+  //    the only workgroup of the sequence that reads the caller's state: the
+  //    last segment overwrites that state with the final one, and it does so
+  //    only after it has seen (directly, or through a group sum) segment 0's
+  //    flag, which goes up after segment 0's image stores -- built from the
+  //    caller's state -- have completed.
+  Acc acc, pre;
   if (seg < nseg - 1) segment_sum_regs<NW>(lds_raw, own, acc, k, v, bh, N, t_begin, t_end);
   else zero_acc(acc);
+  if (seg == 0) {  // uniform; the whole prefix of segment 0
+    load_caller_state_raw<NW>(st_S, st_T, bh, own, pre);
+    unweight_caller_state<NW>(own, pre);
+    if (nseg > 1) acc_add<NW>(acc, pre, lane);
+  } else {
+    zero_acc(pre);
+  }
   // a segment that is not the last of its group publishes its sum at once
   if (nseg > 1 && !leader && seg < nseg - 1) {  // uniform
     image_store<NW, false>(image_of(seg), acc, acc, w, lane);
     raise_flag(flag_of(seg), 1);
   }
-  // Every segment's prefix starts from the caller's state, loaded after the
-  // publication (which waits for all outstanding memory operations); a leader
-  // loads it only after it has published the group sum.
-  Acc pre;
-  if (leader) {
-    zero_acc(pre);
-  } else {
-    load_caller_state_raw<NW>(st_S, st_T, bh, own, pre);
-    unweight_caller_state<NW>(own, pre);
-  }
-  // 2. prefix = caller's state + sums of the earlier members of the group +
-  //    group sums of the earlier groups (the leader adds the members' sums to
-  //    its own as well, and publishes that as the group sum)
-  if (nseg > 1) {  // uniform
+  // 2. prefix = sums of the earlier members of the group + group sums of the
+  //    earlier groups (segment 0's sum carries the caller's state; the leader
+  //    adds the members' sums to its own as well, and publishes that as the
+  //    group sum)
+  if (nseg > 1 && seg > 0) {  // uniform
     int* err = &sync[1];
     const int r = seg - g0;  // earlier members
     auto source = [&](int i) { return i < r ? g0 + i : (i - r) * gs + gs - 1; };
@@ -1062,11 +1068,8 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
       }
       image_store<NW, false>(image_of(seg), acc, acc, w, lane);
       raise_flag(flag_of(seg), 1);
-      Acc x;
-      load_caller_state_raw<NW>(st_S, st_T, bh, own, x);
-      unweight_caller_state<NW>(own, x);
-      acc_add<NW>(pre, x, lane);
       for (int G = 0; G < grp; ++G) {
+        Acc x;
         wait_flag(flag_of(G * gs + gs - 1), err, wait_limit);
         image_load<NW>(image_of(G * gs + gs - 1), x, w, lane);
         acc_add<NW>(pre, x, lane);

@@ -182,3 +182,19 @@ def test_wait_limit_hook_and_check_without_workspace(rsp):
         lib.taylor_set_wait_limit(prev)
     assert lib.taylor_prefill_check(None, 0, None) == 0
     assert lib.taylor_prefill_check(None, 1 << 20, None) == 0
+
+
+def test_state_views_follow_the_header_layout(rsp):
+    """The header's state layout: first S[b][h][D][d_v] (value index fastest), then
+    T[b][h][D], one flat float32 buffer; state_views must address exactly that."""
+    import torch
+    for (B, H, d, n) in [(2, 3, 16, 3), (1, 2, 16, 1), (2, 1, 32, 2), (1, 1, 16, 5)]:
+        D, dv = rsp.state_width(d, n), 64
+        st = torch.arange(B * H * rsp.state_numel(d, dv, n), dtype=torch.float64).float()
+        S, T = rsp.state_views(st, B, H, n, d=d, d_v=dv)
+        assert tuple(S.shape) == (B, H, D, dv) and tuple(T.shape) == (B, H, D)
+        b, h, r, c = B - 1, H - 1, D - 1, 37
+        assert int(S[b, h, r, c]) == ((b * H + h) * D + r) * dv + c
+        assert int(T[b, h, r]) == B * H * D * dv + (b * H + h) * D + r
+        assert int(S[0, 0, 0, 0]) == 0 and int(T[0, 0, 0]) == B * H * D * dv
+        assert S.data_ptr() == st.data_ptr() and T.is_contiguous() and S.is_contiguous()

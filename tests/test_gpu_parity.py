@@ -51,9 +51,14 @@ def run_prefill(rsp, q, k, v, n, a, chunk, dtype, out_dtype=torch.float32, state
 def oracle_state(k, v, n):
     """A_m = sum_i phi_m(k_i) [v_i; 1]^T stacked over m (Eq. (6)), float64, per head."""
     k = k.astype(np.float64)
-    v1 = np.concatenate([v.astype(np.float64), np.ones(v.shape[:-1] + (1,))], axis=-1)
-    feats = np.concatenate([R.phi(k, m) for m in range(n)], axis=-1)      # [..., N, D]
-    return np.einsum("...nd,...nc->...dc", feats, v1)
+    lead = k.shape[:-2]
+    kf, vf = k.reshape((-1,) + k.shape[-2:]), v.reshape((-1,) + v.shape[-2:])
+    out = []
+    for kh, vh in zip(kf, vf):                       # one head at a time (bounded memory)
+        v1 = np.concatenate([vh.astype(np.float64), np.ones((vh.shape[0], 1))], axis=-1)
+        feats = np.concatenate([R.phi(kh, m) for m in range(n)], axis=-1)   # [N, D]
+        out.append(feats.T @ v1)
+    return np.stack(out).reshape(lead + out[0].shape)
 
 
 # ---------------------------------------------------------------------------
@@ -425,10 +430,15 @@ def test_graph_replay_matches_eager(rsp):
 # the workloads at full size, on sampled rows
 # ---------------------------------------------------------------------------
 def sample_rows(B, H, N, per_head, chunk, seed=0):
+    """Rows to compare: the first and last token of every chunk of every head
+    (every segment of any plan starts and ends on a chunk boundary, so this
+    covers the places where a wrong prefix would show first), plus
+    `per_head` seeded random positions per head."""
     rng = np.random.default_rng(seed)
+    edges = set(range(0, N, chunk)) | set(range(chunk - 1, N, chunk)) | {N - 1}
     rows = []
     for bh in range(B * H):
-        pos = {0, N - 1, chunk - 1, chunk, min(N - 1, 2 * chunk + 1)}
+        pos = set(edges)
         pos.update(rng.integers(0, N, per_head).tolist())
         rows.extend(bh * N + p for p in sorted(pos))
     return np.asarray(rows, np.int64)
@@ -491,10 +501,15 @@ def test_long_prefill_workload(rsp, variant):
     norm = variant == "normalised"
     seed = TI.SEEDS["long" if norm else "long_unnormalised"]
     q, k, v = TI.make_qkv(seed, B, H, N, 16, 64, normalize=norm, scale=4.0, dtype="bf16")
-    got, _ = run_prefill(rsp, q, k, v, 3, 1.0, 128, "bf16")
-    rows = sample_rows(B, H, N, 8, 128)
+    got, st = run_prefill(rsp, q, k, v, 3, 1.0, 128, "bf16")
+    rows = sample_rows(B, H, N, 64, 128)
     ref = oracle.taylor_direct(q, k, v, 3, 1.0, rows=rows)
     assert oracle.rel_err_rowwise(got.reshape(-1, 64)[rows], ref) <= TOL["bf16"]
+    # the final state of every head against the float64 phi-sum of its 65,536 tokens
+    S, T = (x.cpu().numpy().astype(np.float64) for x in rsp.state_views(st, B, H, 3))
+    A = oracle_state(k, v, 3)
+    assert np.abs(T - A[..., 64]).max() <= 2e-2 * np.abs(A[..., 64]).max()
+    assert np.abs(S - A[..., :64]).max() <= 2e-2 * np.abs(A[..., :64]).max()
     rep = oracle.convergence_report(q[:, :1, :256], k[:, :1, :256], v[:, :1, :256], 1.0, 6)
     assert rep["non_converged"] == (not norm)
 

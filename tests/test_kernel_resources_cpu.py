@@ -82,3 +82,94 @@ def test_no_spills_and_no_scratch(metadata, src):
                 or int(k["sgpr_spill_count"]) > allow:
             bad.append((name, k["vgpr_spill_count"], k["sgpr_spill_count"], k["private_segment_fixed_size"]))
     assert not bad, f"kernels that spill (name, vgpr spills, sgpr spills, scratch bytes): {bad}"
+
+
+# ---------------------------------------------------------------------------
+# The hand-over between the workgroups of one sequence in the single-launch
+# n = 3 prefill.  Its correctness rests on the emitted code, not on the HIP
+# memory model: state images move through the workspace with buffer accesses
+# whose cache-policy bit sc1 selects device scope (stores write through the
+# XCD's L2, loads do not hit a stale L2 line; CDNA3/CDNA4 instruction-set
+# reference, the cache-control bits SC0/SC1/NT of vector memory instructions
+# and the memory-scope table they encode), and a writer raises its flag only
+# after every wave has waited for its stores to complete (s_waitcnt vmcnt(0))
+# and met the others at a barrier.  A compiler change that dropped the bit or
+# moved the wait would corrupt prefixes silently, so both are checked here in
+# the assembly of both translation units.
+# ---------------------------------------------------------------------------
+N3_UNITS = ["taylor_prefill_n3.hip", "taylor_prefill_n3_c128.hip"]
+
+
+def _functions(asm: str):
+    """{mangled name: list of instruction lines} for every function in the listing."""
+    out, cur, name = {}, None, None
+    for line in asm.splitlines():
+        m = re.match(r"^(_Z\w+):", line)
+        if m:
+            name, cur = m.group(1), []
+            out[name] = cur
+            continue
+        if cur is not None and line.startswith(".Lfunc_end"):
+            cur, name = None, None
+            continue
+        if cur is not None:
+            s = line.split(";", 1)[0].strip()
+            if s and not s.startswith(".") and not s.endswith(":"):
+                cur.append(s)
+    return out
+
+
+@pytest.fixture(scope="module")
+def n3_asm(tmp_path_factory):
+    b = _build_module()
+    if shutil.which(b.HIPCC) is None and not os.path.exists(b.HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm_n3")
+    res = {}
+    for src in N3_UNITS:
+        dst = out / (src + ".s")
+        cmd = [b.HIPCC, "-x", "hip", *b.FLAGS, *b.EXTRA.get(src, []), "--cuda-device-only", "-S",
+               os.path.join(b.CSRC, src), "-o", str(dst)]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        res[src] = {k: v for k, v in _functions(dst.read_text()).items() if "prefill_n3_kernel" in k}
+    return res
+
+
+@pytest.mark.parametrize("src", N3_UNITS)
+def test_n3_image_accesses_are_device_scope(n3_asm, src):
+    fns = n3_asm[src]
+    assert len(fns) == 2, f"expected the float and bfloat16-output instances in {src}, got {list(fns)}"
+    for name, ins in fns.items():
+        buf = [i for i in ins if i.startswith("buffer_load") or i.startswith("buffer_store")]
+        assert any(i.startswith("buffer_store") for i in buf) and any(i.startswith("buffer_load") for i in buf), name
+        missing = [i for i in buf if not re.search(r"\bsc1\b", i)]
+        assert not missing, f"{name}: image accesses without the device-scope bit: {missing[:4]}"
+        # flag polls are device-scope loads of the header
+        polls = [i for i in ins if i.startswith("global_load_dword ") and re.search(r"\bsc1\b", i)]
+        assert polls, f"{name}: no device-scope flag poll found"
+
+
+@pytest.mark.parametrize("src", N3_UNITS)
+def test_n3_flag_raised_only_after_stores_complete(n3_asm, src):
+    """Every flag store (a device-scope dword store into the header other than the
+    error word at byte 4) is preceded, with no vector store in between, by an
+    s_barrier, and before that by an s_waitcnt that waits for vmcnt(0)."""
+    store = re.compile(r"^(buffer_store|global_store|flat_store|global_atomic|buffer_atomic|flat_atomic)")
+    for name, ins in n3_asm[src].items():
+        flags = [j for j, i in enumerate(ins)
+                 if i.startswith("global_store_dword ") and re.search(r"\bsc1\b", i) and "offset:4 " not in i + " "]
+        # a plain segment's publication and a group leader's
+        assert len(flags) >= 2, f"{name}: expected at least two flag stores, found {len(flags)}"
+        for j in flags:
+            seen_barrier = seen_wait = False
+            for i in reversed(ins[:j]):
+                if i.startswith("s_barrier"):
+                    seen_barrier = True
+                elif seen_barrier and i.startswith("s_waitcnt") and "vmcnt(0)" in i:
+                    seen_wait = True
+                    break
+                elif store.match(i):
+                    break
+            assert seen_barrier and seen_wait, \
+                f"{name}: flag store {ins[j]!r} not preceded by s_waitcnt vmcnt(0) and s_barrier"

@@ -303,3 +303,84 @@ def test_inputs_are_seeded_and_per_head():
     assert np.array_equal(q1[1, 0], q2[1, 0]) and np.array_equal(v1[1, 0], v2[1, 0])
     assert np.array_equal(TI.round_bf16(q1), q1)
     assert np.allclose(np.linalg.norm(q1, axis=-1), 1.0, atol=1e-2)
+
+
+# --------------------------------------------------------------------------
+# The error measures themselves: every GPU parity gate goes through
+# rel_err_rowwise, so it is pinned on hand-computed arrays whose value tells
+# the row-wise max-norm ratio apart from the plausible slips (a global ratio,
+# a mean over rows, the wrong axis, an element-wise ratio, a row 2-norm).
+# --------------------------------------------------------------------------
+def test_rel_err_rowwise_hand_computed():
+    ref = np.array([[1.0, -4.0, 2.0],
+                    [0.5, 0.25, -0.5]])
+    o = ref + np.array([[0.4, 0.0, 0.0],
+                        [0.0, 0.0, -0.1]])
+    # row 0: 0.4 / 4 = 0.1; row 1: 0.1 / 0.5 = 0.2 -> max 0.2
+    assert oracle.rel_err_rowwise(o, ref) == pytest.approx(0.2, rel=1e-15)
+    # the slips give other numbers on the same arrays
+    d = np.abs(o - ref)
+    assert d.max() / np.abs(ref).max() == pytest.approx(0.1)                           # global ratio
+    assert np.mean(d.max(1) / np.abs(ref).max(1)) == pytest.approx(0.15)               # mean over rows
+    assert np.max(d.max(0) / np.abs(ref).max(0)) == pytest.approx(0.4)                 # columns as rows
+    assert np.max(d / np.abs(ref)) == pytest.approx(0.4)                               # element-wise
+    assert np.max(np.linalg.norm(d, axis=1) / np.linalg.norm(ref, axis=1)) != pytest.approx(0.2)
+    # symmetric in the sign of the error, scaled by the reference only
+    assert oracle.rel_err_rowwise(2 * ref - o, ref) == pytest.approx(0.2, rel=1e-15)
+    assert oracle.rel_err_rowwise(o, ref) != pytest.approx(oracle.rel_err_rowwise(ref, o))
+
+
+def test_rel_err_rowwise_rows_are_last_axis_vectors():
+    """[..., d_v] arrays: every leading index is a row; permuting rows does not matter."""
+    rng = np.random.default_rng(5)
+    ref = rng.standard_normal((2, 3, 4, 5))
+    o = ref.copy()
+    o[1, 2, 3, 0] += 0.5                      # one element of one row
+    want = 0.5 / np.abs(ref[1, 2, 3]).max()
+    assert oracle.rel_err_rowwise(o, ref) == pytest.approx(want, rel=1e-15)
+    perm = rng.permutation(24)
+    assert oracle.rel_err_rowwise(o.reshape(24, 5)[perm], ref.reshape(24, 5)[perm]) == pytest.approx(want, rel=1e-15)
+    assert oracle.rel_err_rowwise(ref, ref) == 0.0
+    # a non-finite output row is never hidden
+    o[0, 0, 0, 1] = np.nan
+    assert not oracle.rel_err_rowwise(o, ref) <= 1.0
+
+
+def test_rel_err_frobenius_hand_computed():
+    ref = np.array([[3.0, 0.0], [0.0, 4.0]])            # ||ref||_F = 5
+    o = ref + np.array([[0.0, 0.3], [0.4, 0.0]])        # ||o - ref||_F = 0.5
+    assert oracle.rel_err_frobenius(o, ref) == pytest.approx(0.1, rel=1e-15)
+
+
+def test_arg_stats_hand_computed():
+    """max and mean of |q_t.k_i / a| over the causal pairs i <= t only (section 5.9)."""
+    q = np.array([[[1.0, 0.0], [0.0, -2.0]]], np.float32)
+    k = np.array([[[3.0, 0.0], [1.0, 1.0]]], np.float32)
+    # pairs (t, i): (0, 0) -> 3/2; (1, 0) -> 0; (1, 1) -> -2/2, |.| = 1
+    mx, mean = oracle.arg_stats(q, k, 2.0)
+    assert mx == 1.5
+    assert mean == pytest.approx((1.5 + 0.0 + 1.0) / 3, rel=1e-15)
+    # the non-causal pair (0, 1) = 1/2 and the signed mean would give other values
+    assert mean != pytest.approx((1.5 + 0.5 + 0.0 + 1.0) / 4)
+    assert mean != pytest.approx((1.5 + 0.0 - 1.0) / 3)
+    # a subset of rows: row 1 alone has the pairs (1, 0) and (1, 1)
+    mx1, mean1 = oracle.arg_stats(q, k, 2.0, rows=[1])
+    assert (mx1, mean1) == (1.0, 0.5)
+
+
+def test_arg_stats_matches_brute_force():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((3, 7, 4)).astype(np.float32)
+    k = rng.standard_normal((3, 7, 4)).astype(np.float32)
+    a = 0.7
+    vals = [abs(float(np.dot(q[b, t].astype(np.float64), k[b, i].astype(np.float64))) / a)
+            for b in range(3) for t in range(7) for i in range(t + 1)]
+    mx, mean = oracle.arg_stats(q, k, a)
+    assert mx == pytest.approx(max(vals), rel=1e-14)
+    assert mean == pytest.approx(sum(vals) / len(vals), rel=1e-13)
+    rows = [0, 8, 20]                          # (b, t) = (0, 0), (1, 1), (2, 6)
+    sub = [abs(float(np.dot(q[r // 7, r % 7].astype(np.float64), k[r // 7, i].astype(np.float64)))) / a
+           for r in rows for i in range(r % 7 + 1)]
+    mx2, mean2 = oracle.arg_stats(q, k, a, rows=rows)
+    assert mx2 == pytest.approx(max(sub), rel=1e-14)
+    assert mean2 == pytest.approx(sum(sub) / len(sub), rel=1e-13)
