@@ -134,6 +134,42 @@ int taylor_attn_decode(const void* q, const void* k, const void* v, void* o, flo
                        int B, int H, int d, int d_v, int n, float a,
                        taylor_dtype in_dtype, taylor_dtype out_dtype, hipStream_t stream);
 
+/* ---- Exact causal softmax attention: the comparison method ---------------
+ * Eq. (1) with the exponential kernel itself, o_t = sum_{i<=t} e^{q_t.k_i/a} v_i /
+ * sum_{i<=t} e^{q_t.k_i/a}: what the paper measures the Taylor states against
+ * (prefill, section 5.5; decode against a growing key-value cache, section
+ * 5.6; accuracy of the n-term kernel, sections 5.7 and 5.9).  Computed with
+ * the running maximum subtracted inside the exponential (a factor that
+ * cancels in the ratio).  Only d = 16, d_v = 64 are built (else
+ * TAYLOR_EUNSUPPORTED, nothing launched).
+ *   bfloat16 inputs: bfloat16 matrix-core operands, the weights rounded to
+ *   bfloat16 for the weighted sum of v and the normaliser summed from the same
+ *   rounded weights, float32 accumulation.  float32 inputs: float32
+ *   throughout. */
+
+/* Causal softmax attention over q, k, v [B, H, N, d / d_v] (no earlier
+ * context); o [B, H, N, d_v] in out_dtype.  Allocates nothing, needs no
+ * workspace.  N = 0 or B*H = 0 is a no-op. */
+int taylor_softmax_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int d_v,
+                           float a, taylor_dtype in_dtype, taylor_dtype out_dtype, hipStream_t stream);
+
+/* Bytes of workspace taylor_softmax_decode needs for a cache of `cap`
+ * positions (one partial result of 68 floats per head per range of 2048
+ * keys).  Host only; -1 cast to size_t on invalid arguments. */
+size_t taylor_softmax_decode_workspace_bytes(int B, int H, int cap, int d, int d_v);
+
+/* One decode step of every head against its key-value cache (section 5.6).
+ *   k_cache [B, H, cap, d], v_cache [B, H, cap, d_v], in_dtype, device: positions
+ *   0 .. pos-1 hold the earlier tokens; the call writes k, v ([B, H, d],
+ *   [B, H, d_v]) at position pos and then computes o [B, H, d_v] for q
+ *   [B, H, d] over positions 0 .. pos (the token attends to itself).
+ *   Every stream of the batch is at the same position.  0 <= pos < cap.
+ *   workspace: device, at least taylor_softmax_decode_workspace_bytes(B, H,
+ *   pos + 1, ...) bytes, 16-byte aligned, scratch. */
+int taylor_softmax_decode(const void* q, const void* k, const void* v, void* o, void* k_cache, void* v_cache, int B,
+                          int H, int pos, int cap, int d, int d_v, float a, taylor_dtype in_dtype,
+                          taylor_dtype out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Description of the last failure on the calling thread ("" if none). */
 const char* taylor_last_error(void);
 

@@ -21,7 +21,8 @@ import torch
 __all__ = [
     "LIB_PATH", "TaylorError", "state_width", "state_numel", "new_state", "state_init",
     "state_views", "prefill_workspace_bytes", "prefill", "decode", "set_phase_events",
-    "prefill_check", "set_wait_limit", "EXPORTED_SYMBOLS",
+    "prefill_check", "set_wait_limit", "softmax_prefill", "softmax_decode", "softmax_decode_workspace_bytes",
+    "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtaylor_attn.so")
@@ -32,7 +33,8 @@ _CODES = {0: "TAYLOR_OK", -1: "TAYLOR_EINVAL", -2: "TAYLOR_EUNSUPPORTED", -3: "T
 EXPORTED_SYMBOLS = (
     "taylor_state_width", "taylor_state_numel", "taylor_state_init", "taylor_prefill_workspace_bytes",
     "taylor_attn_prefill", "taylor_attn_decode", "taylor_last_error", "taylor_set_phase_events",
-    "taylor_prefill_check", "taylor_set_wait_limit",
+    "taylor_prefill_check", "taylor_set_wait_limit", "taylor_softmax_prefill",
+    "taylor_softmax_decode_workspace_bytes", "taylor_softmax_decode",
 )
 
 
@@ -71,6 +73,13 @@ _lib.taylor_prefill_check.argtypes = [_vp, _sz, _vp]
 _lib.taylor_prefill_check.restype = _i
 _lib.taylor_set_wait_limit.argtypes = [_i]
 _lib.taylor_set_wait_limit.restype = _i
+_lib.taylor_softmax_prefill.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
+_lib.taylor_softmax_prefill.restype = _i
+_lib.taylor_softmax_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
+_lib.taylor_softmax_decode_workspace_bytes.restype = _sz
+_lib.taylor_softmax_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp, _sz,
+                                       _vp]
+_lib.taylor_softmax_decode.restype = _i
 
 
 def raw_library() -> ctypes.CDLL:
@@ -223,3 +232,52 @@ def set_wait_limit(polls: int) -> int:
     if prev < 0:
         raise TaylorError(-1, _lib.taylor_last_error().decode())
     return prev
+
+
+# ---- exact causal softmax attention (the comparison method, Eq. (1)) ----------
+def softmax_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, a: float,
+                    out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Causal softmax attention over q, k [B,H,N,d], v [B,H,N,d_v]; returns o [B,H,N,d_v]."""
+    B, H, N, d = q.shape
+    d_v = v.shape[-1]
+    _check_tensor("q", q, (B, H, N, d))
+    _check_tensor("k", k, (B, H, N, d), q.dtype)
+    _check_tensor("v", v, (B, H, N, d_v), q.dtype)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, H, N, d_v), dtype=out_dtype, device=q.device)
+    _check_tensor("out", out, (B, H, N, d_v), out_dtype)
+    _check(_lib.taylor_softmax_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), B, H, N, d, d_v, float(a),
+                                       _dtype_code(q.dtype), _dtype_code(out_dtype), _stream_ptr(q.device)))
+    return out
+
+
+def softmax_decode_workspace_bytes(B: int, H: int, cap: int, d: int = 16, d_v: int = 64) -> int:
+    r = int(_lib.taylor_softmax_decode_workspace_bytes(B, H, cap, d, d_v))
+    if r == ctypes.c_size_t(-1).value:
+        raise TaylorError(-1, "invalid arguments to taylor_softmax_decode_workspace_bytes")
+    return r
+
+
+def softmax_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   pos: int, a: float, workspace: torch.Tensor, out_dtype: torch.dtype | None = None,
+                   out: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step against the cache: writes k, v [B,H,d / d_v] at ``pos`` of
+    k_cache [B,H,cap,d] / v_cache [B,H,cap,d_v] and attends over 0..pos."""
+    B, H, d = q.shape
+    d_v = v.shape[-1]
+    cap = k_cache.shape[2]
+    _check_tensor("q", q, (B, H, d))
+    _check_tensor("k", k, (B, H, d), q.dtype)
+    _check_tensor("v", v, (B, H, d_v), q.dtype)
+    _check_tensor("k_cache", k_cache, (B, H, cap, d), q.dtype)
+    _check_tensor("v_cache", v_cache, (B, H, cap, d_v), q.dtype)
+    _check_tensor("workspace", workspace, (workspace.numel(),), torch.float32)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=out_dtype, device=q.device)
+    _check_tensor("out", out, (B, H, d_v), out_dtype)
+    _check(_lib.taylor_softmax_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(k_cache), _ptr(v_cache), B, H,
+                                      int(pos), cap, d, d_v, float(a), _dtype_code(q.dtype), _dtype_code(out_dtype),
+                                      _ptr(workspace), workspace.numel() * 4, _stream_ptr(q.device)))
+    return out

@@ -17,7 +17,8 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libtaylor_attn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["taylor_abi.cpp", "taylor_decode.hip", "taylor_prefill.hip", "taylor_prefill_n3.hip",
-           "taylor_prefill_n3_c128.hip", "taylor_prefill_fb.hip"]
+           "taylor_prefill_n3_c128.hip", "taylor_prefill_fb.hip",
+           "softmax_attn.hip"]
 # per-source extra flags: the 64-token n = 3 prefill is scheduled for
 # instruction-level parallelism (measured faster for it, slower for 128 tokens)
 EXTRA = {"taylor_prefill_n3.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}

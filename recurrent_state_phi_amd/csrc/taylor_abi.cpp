@@ -168,4 +168,55 @@ int taylor_set_wait_limit(int polls) {
   return g_wait_limit.exchange(polls);
 }
 
+int taylor_softmax_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int d_v,
+                           float a, taylor_dtype in_dtype, taylor_dtype out_dtype, hipStream_t stream) {
+  if (int e = check_dtypes(in_dtype, out_dtype)) return e;
+  if (B < 0 || H < 0 || N < 0) return fail(TAYLOR_EINVAL, "taylor_softmax_prefill: B, H, N must be >= 0");
+  if (!(a > 0.0f) || a == __builtin_inff()) return fail(TAYLOR_EINVAL, "taylor_softmax_prefill: a must be finite and > 0");
+  if (d != taylor::kD || d_v != taylor::kDV)
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_softmax_prefill: only d = 16, d_v = 64 are built");
+  if ((int64_t)B * H == 0 || N == 0) return TAYLOR_OK;
+  if (!q || !k || !v || !o) return fail(TAYLOR_EINVAL, "taylor_softmax_prefill: NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(TAYLOR_EINVAL, "taylor_softmax_prefill: q, k, v and o must be 16-byte aligned");
+  if ((int64_t)B * H * ((N + 63) / 64) > ((int64_t)1 << 31) - 1)
+    return fail(TAYLOR_EINVAL, "taylor_softmax_prefill: sizes out of range");
+  taylor::SoftmaxPrefillArgs args{q, k, v, o, B * H, N, a, in_dtype == TAYLOR_BF16, out_dtype == TAYLOR_BF16, stream};
+  const hipError_t e = taylor::launch_softmax_prefill(args);
+  if (e != hipSuccess) return hip_fail(e, "taylor_softmax_prefill: kernel launch");
+  return TAYLOR_OK;
+}
+
+size_t taylor_softmax_decode_workspace_bytes(int B, int H, int cap, int d, int d_v) {
+  if (B < 0 || H < 0 || cap < 1 || d != taylor::kD || d_v != taylor::kDV) return (size_t)-1;
+  return taylor::softmax_decode_workspace_floats(B * H, cap) * sizeof(float);
+}
+
+int taylor_softmax_decode(const void* q, const void* k, const void* v, void* o, void* k_cache, void* v_cache, int B,
+                          int H, int pos, int cap, int d, int d_v, float a, taylor_dtype in_dtype,
+                          taylor_dtype out_dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (int e = check_dtypes(in_dtype, out_dtype)) return e;
+  if (B < 0 || H < 0) return fail(TAYLOR_EINVAL, "taylor_softmax_decode: B and H must be >= 0");
+  if (cap < 1 || pos < 0 || pos >= cap) return fail(TAYLOR_EINVAL, "taylor_softmax_decode: need 0 <= pos < cap");
+  if (!(a > 0.0f) || a == __builtin_inff()) return fail(TAYLOR_EINVAL, "taylor_softmax_decode: a must be finite and > 0");
+  if (d != taylor::kD || d_v != taylor::kDV)
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_softmax_decode: only d = 16, d_v = 64 are built");
+  if ((int64_t)B * H == 0) return TAYLOR_OK;
+  if (!q || !k || !v || !o || !k_cache || !v_cache) return fail(TAYLOR_EINVAL, "taylor_softmax_decode: NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(k_cache) ||
+      !aligned16(v_cache))
+    return fail(TAYLOR_EINVAL, "taylor_softmax_decode: tensors must be 16-byte aligned");
+  const size_t need = taylor::softmax_decode_workspace_floats(B * H, pos + 1) * sizeof(float);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+    return fail(TAYLOR_EINVAL, "taylor_softmax_decode: workspace too small or unaligned (need " +
+                                   std::to_string(need) + " bytes, see taylor_softmax_decode_workspace_bytes)");
+  if ((int64_t)B * H * taylor::softmax_decode_splits(pos + 1) > ((int64_t)1 << 31) - 1)
+    return fail(TAYLOR_EINVAL, "taylor_softmax_decode: sizes out of range");
+  taylor::SoftmaxDecodeArgs args{q, k, v, o, k_cache, v_cache, static_cast<float*>(workspace), B * H, pos, cap, a,
+                                 in_dtype == TAYLOR_BF16, out_dtype == TAYLOR_BF16, stream};
+  const hipError_t e = taylor::launch_softmax_decode(args);
+  if (e != hipSuccess) return hip_fail(e, "taylor_softmax_decode: kernel launch");
+  return TAYLOR_OK;
+}
+
 }  // extern "C"

@@ -75,4 +75,28 @@ hipError_t launch_segment_scan(const float* st_S, const float* st_T, float* W_S,
 // Whether a (d, n, chunk, input dtype) combination is compiled.
 bool prefill_supported(int d, int n, int chunk, bool in_bf16);
 
+// Exact causal softmax attention (softmax_attn.hip), d = 16, d_v = 64.
+struct SoftmaxPrefillArgs {
+  const void* q; const void* k; const void* v; void* o;
+  int BH, N;
+  float a;
+  bool in_bf16, out_bf16;
+  hipStream_t stream;
+};
+struct SoftmaxDecodeArgs {
+  const void* q; const void* k; const void* v; void* o;
+  void* k_cache; void* v_cache;
+  float* workspace;
+  int BH, pos, cap;
+  float a;
+  bool in_bf16, out_bf16;
+  hipStream_t stream;
+};
+hipError_t launch_softmax_prefill(const SoftmaxPrefillArgs& a);
+hipError_t launch_softmax_decode(const SoftmaxDecodeArgs& a);
+// Key ranges of one decode step over `len` keys, and the workspace floats of
+// a cache of `cap` positions.
+int softmax_decode_splits(int len);
+size_t softmax_decode_workspace_floats(int BH, int cap);
+
 }  // namespace taylor

@@ -198,3 +198,30 @@ def test_state_views_follow_the_header_layout(rsp):
         assert int(T[b, h, r]) == B * H * D * dv + (b * H + h) * D + r
         assert int(S[0, 0, 0, 0]) == 0 and int(T[0, 0, 0]) == B * H * D * dv
         assert S.data_ptr() == st.data_ptr() and T.is_contiguous() and S.is_contiguous()
+
+
+def test_softmax_entry_points_validate_before_launch(rsp):
+    """The exact-softmax baseline's entry points: shapes other than d = 16, d_v = 64 are
+    not built, bad sizes and pointers are rejected, empty calls do nothing, and the
+    decode workspace is one 68-float partial per head per 2048-key range."""
+    lib = rsp.raw_library()
+    pre = lib.taylor_softmax_prefill
+    assert pre(None, None, None, None, 1, 1, 10, 16, 64, 1.0, 1, 0, None) == -1     # NULL
+    assert pre(None, None, None, None, 1, 1, 10, 32, 64, 1.0, 1, 0, None) == -2     # d not built
+    assert pre(None, None, None, None, 1, 1, 10, 16, 32, 1.0, 1, 0, None) == -2
+    assert pre(None, None, None, None, 1, 1, 10, 16, 64, 0.0, 1, 0, None) == -1     # a <= 0
+    assert pre(None, None, None, None, 1, 1, -1, 16, 64, 1.0, 1, 0, None) == -1
+    assert pre(None, None, None, None, 1, 1, 0, 16, 64, 1.0, 1, 0, None) == 0       # empty
+    assert pre(16, 16, 16, 8, 1, 1, 10, 16, 64, 1.0, 1, 0, None) == -1              # misaligned
+    assert b"aligned" in lib.taylor_last_error()
+    ws = rsp.softmax_decode_workspace_bytes
+    assert ws(64, 8, 65792) == 64 * 8 * 33 * 68 * 4
+    assert ws(1, 1, 2048) == 68 * 4 and ws(1, 1, 2049) == 2 * 68 * 4
+    dec = lib.taylor_softmax_decode
+    args = lambda pos, cap, wsb=1 << 20, d=16: (16, 16, 16, 16, 16, 16, 2, 2, pos, cap, d, 64, 1.0, 1, 0, 16, wsb, None)
+    assert dec(*args(5, 5)) == -1                        # pos must be < cap
+    assert dec(*args(-1, 5)) == -1
+    assert dec(*args(1, 4, d=64)) == -2
+    assert dec(*args(3000, 4000, wsb=2 * 2 * 68 * 4)) == -1   # two ranges need twice that
+    assert b"workspace" in lib.taylor_last_error()
+    assert dec(None, None, None, None, None, None, 0, 2, 0, 4, 16, 64, 1.0, 1, 0, None, 0, None) == 0

@@ -1,0 +1,194 @@
+"""GPU parity of the exact causal softmax kernels (the comparison method, Eq. (1) of
+"A Taylor-Series Route to Linear-Time Transformers with a Fixed Number of
+Recurrent States", arXiv 2610.20637, sections 5.5-5.6) against the float64
+oracle's softmax, through the C ABI.
+
+Tolerances as for the Taylor path (max over rows of ||o_t - o^_t||_inf /
+||o^_t||_inf): 1e-4 for float32 inputs, 2e-2 for bfloat16 inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import taylor_inputs as TI
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def rsp():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import recurrent_state_phi_amd as rsp
+    return rsp
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def to_dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV).to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+
+
+def run_prefill(rsp, q, k, v, a, dtype, out_dtype=torch.float32):
+    o = rsp.softmax_prefill(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), a, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_softmax_tiny_all_outputs(rsp, dtype):
+    say("softmax prefill tiny", dtype)
+    q, k, v = TI.make_qkv(TI.SEEDS["tiny"], 1, 1, 256, 16, 64, dtype=dtype)
+    ref = oracle.softmax(q, k, v, 1.0)
+    assert oracle.rel_err_rowwise(run_prefill(rsp, q, k, v, 1.0, dtype), ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("N", [1, 2, 15, 63, 64, 65, 200, 1000])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_softmax_ragged_lengths(rsp, N, dtype):
+    """Partial last key block and query block, several heads."""
+    say("softmax prefill ragged", N, dtype)
+    q, k, v = TI.make_qkv(200 + N, 2, 3, N, 16, 64, dtype=dtype)
+    ref = oracle.softmax(q, k, v, 1.0)
+    assert oracle.rel_err_rowwise(run_prefill(rsp, q, k, v, 1.0, dtype), ref) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("a", [0.5, 2.0, 4.0])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_softmax_temperatures_and_large_scores(rsp, a, dtype):
+    """Temperatures of section 5 and unnormalised q, k ~ N(0, 4^2): scores up to a few
+    hundred, where the running maximum keeps every exponent <= 0."""
+    say("softmax prefill a / large scores", a, dtype)
+    q, k, v = TI.make_qkv(210, 1, 2, 700, 16, 64, normalize=False, scale=4.0, dtype=dtype)
+    assert np.abs(np.einsum("bhtd,bhsd->bhts", q, k)).max() / a > 50
+    ref = oracle.softmax(q, k, v, a)
+    assert oracle.rel_err_rowwise(run_prefill(rsp, q, k, v, a, dtype), ref) <= TOL[dtype]
+
+
+def test_softmax_bf16_output(rsp):
+    say("softmax prefill bf16 out")
+    q, k, v = TI.make_qkv(211, 1, 2, 500, 16, 64, dtype="bf16")
+    ref = oracle.softmax(q, k, v, 1.0)
+    assert oracle.rel_err_rowwise(run_prefill(rsp, q, k, v, 1.0, "bf16", torch.bfloat16), ref) <= TOL["bf16"]
+
+
+def test_softmax_equal_keys_is_running_mean(rsp):
+    """All keys equal: every weight of row t is the same, o_t is the mean of v_0..v_t
+    (a closed form of Eq. (1) that does not need the oracle)."""
+    say("softmax equal keys")
+    q, k, v = TI.make_qkv(212, 1, 2, 1000, 16, 64)
+    k = np.ascontiguousarray(np.broadcast_to(k[:, :, :1], k.shape))
+    mean = np.cumsum(v.astype(np.float64), axis=-2) / np.arange(1, 1001)[:, None]
+    assert oracle.rel_err_rowwise(run_prefill(rsp, q, k, v, 1.0, "f32"), mean) <= TOL["f32"]
+
+
+def sample_rows(B, H, N, per_head, block=64, seed=0):
+    rng = np.random.default_rng(seed)
+    edges = set(range(0, N, block)) | set(range(block - 1, N, block)) | {N - 1}
+    rows = []
+    for bh in range(B * H):
+        pos = set(edges) | set(rng.integers(0, N, per_head).tolist())
+        rows.extend(bh * N + p for p in sorted(pos))
+    return np.asarray(rows, np.int64)
+
+
+def test_softmax_prefill_workload_sampled(rsp):
+    """The prefill workload's shape, B=4, H=8, N=8192, bfloat16: the first and last row of
+    every 64-query block and 48 random rows per head against the oracle."""
+    say("softmax prefill workload 4x8x8192 bf16")
+    B, H, N = 4, 8, 8192
+    q, k, v = TI.make_qkv(TI.SEEDS["prefill"], B, H, N, 16, 64, dtype="bf16")
+    got = run_prefill(rsp, q, k, v, 1.0, "bf16")
+    rows = sample_rows(B, H, N, 48)
+    ref = oracle.softmax(q, k, v, 1.0, rows=rows)
+    assert oracle.rel_err_rowwise(got.reshape(-1, 64)[rows], ref) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------------------
+# decode against the key-value cache
+# ---------------------------------------------------------------------------
+def run_decode(rsp, q, k, v, N0, steps, dtype, cap=None):
+    """Cache holds tokens 0..N0-1; then `steps` decode calls append and attend."""
+    B, H = q.shape[:2]
+    cap = cap or (N0 + steps)
+    qd, kd, vd = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    tdt = qd.dtype
+    kc = torch.zeros(B, H, cap, 16, device=DEV, dtype=tdt)
+    vc = torch.zeros(B, H, cap, 64, device=DEV, dtype=tdt)
+    kc[:, :, :N0] = kd[:, :, :N0]
+    vc[:, :, :N0] = vd[:, :, :N0]
+    ws = torch.empty(rsp.softmax_decode_workspace_bytes(B, H, cap) // 4, device=DEV)
+    outs = []
+    for t in range(N0, N0 + steps):
+        outs.append(rsp.softmax_decode(qd[:, :, t].contiguous(), kd[:, :, t].contiguous(), vd[:, :, t].contiguous(),
+                                       kc, vc, t, 1.0, ws))
+    torch.cuda.synchronize()
+    return torch.stack(outs, dim=2).cpu().numpy().astype(np.float64), kc, vc, kd, vd
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N0,steps", [(0, 70), (2040, 12), (5000, 5)])
+def test_softmax_decode_vs_oracle(rsp, dtype, N0, steps):
+    """From an empty cache, across the 2048-key range boundary of the split, and with
+    three ranges: every output against the oracle, and the appended keys and values
+    land in the cache bit for bit."""
+    say("softmax decode", dtype, N0, steps)
+    q, k, v = TI.make_qkv(220, 2, 3, N0 + steps, 16, 64, dtype=dtype)
+    got, kc, vc, kd, vd = run_decode(rsp, q, k, v, N0, steps, dtype)
+    ref = oracle.softmax(q, k, v, 1.0)[:, :, N0:]
+    assert oracle.rel_err_rowwise(got, ref) <= TOL[dtype]
+    assert torch.equal(kc, kd) and torch.equal(vc, vd)
+
+
+def test_softmax_decode_equals_prefill(rsp):
+    """Decode steps continuing a cache equal the prefill rows of the same tokens
+    (both compute Eq. (1) for row t over keys 0..t)."""
+    say("softmax decode == prefill rows")
+    N0, steps = 300, 20
+    q, k, v = TI.make_qkv(221, 1, 2, N0 + steps, 16, 64)
+    dec, *_ = run_decode(rsp, q, k, v, N0, steps, "f32")
+    pre = run_prefill(rsp, q, k, v, 1.0, "f32")[:, :, N0:]
+    assert oracle.rel_err_rowwise(dec, pre) <= TOL["f32"]
+
+
+def test_softmax_decode_workload_sampled(rsp):
+    """B=64 streams, H=8, a bfloat16 cache of 65,536 context tokens, then 256 steps:
+    eight sampled heads against the oracle over all 65,536 + s + 1 keys."""
+    say("softmax decode workload 64x8, ctx 65536, 256 steps")
+    B, H, N0, steps = 64, 8, 65536, 256
+    cap = N0 + steps
+    heads = [(0, 0), (9, 4), (31, 7), (63, 5)]
+    g = torch.Generator(device=DEV).manual_seed(4321)
+    kc = torch.randn(B, H, cap, 16, device=DEV, generator=g)
+    kc = (kc / kc.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    vc = torch.randn(B, H, cap, 64, device=DEV, generator=g).to(torch.bfloat16)
+    qs = torch.randn(B, H, steps, 16, device=DEV, generator=g)
+    qs = (qs / qs.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    host = {}
+    for b, h in heads:
+        q1, k1, v1 = TI.head_qkv(TI.SEEDS["decode"], b, h, cap, 16, 64, dtype="bf16")
+        host[(b, h)] = (q1, k1, v1)
+        kc[b, h] = torch.from_numpy(k1).to(DEV).to(torch.bfloat16)
+        vc[b, h] = torch.from_numpy(v1).to(DEV).to(torch.bfloat16)
+        qs[b, h] = torch.from_numpy(q1[N0:]).to(DEV).to(torch.bfloat16)
+    # the step tokens are read from the inputs and written at their position
+    ks = kc[:, :, N0:].permute(2, 0, 1, 3).contiguous()
+    vs = vc[:, :, N0:].permute(2, 0, 1, 3).contiguous()
+    qs = qs.permute(2, 0, 1, 3).contiguous()
+    kc[:, :, N0:] = 0
+    vc[:, :, N0:] = 0
+    ws = torch.empty(rsp.softmax_decode_workspace_bytes(B, H, cap) // 4, device=DEV)
+    outs = torch.empty(steps, B, H, 64, device=DEV)
+    for s in range(steps):
+        rsp.softmax_decode(qs[s], ks[s], vs[s], kc, vc, N0 + s, 1.0, ws, out=outs[s])
+    got = outs.cpu().numpy().astype(np.float64)
+    for b, h in heads:
+        q1, k1, v1 = host[(b, h)]
+        ref = oracle.softmax(q1, k1, v1, 1.0, rows=np.arange(N0, cap))
+        assert oracle.rel_err_rowwise(got[:, b, h], ref) <= TOL["bf16"], (b, h)
