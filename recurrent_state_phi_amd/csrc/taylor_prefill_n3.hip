@@ -9,9 +9,7 @@
 //  1. segment sum: the workgroup runs the state update over its segment from a
 //     zero state (Eq. (6)-(7) summed over the segment; the states are additive
 //     across chunks, section 3.5).  Segment 0 adds the caller's state to its
-//     sum (it is the only workgroup that reads the caller's state, which the
-//     last segment overwrites with the final state).  The sum A_s is
-//     published to the workspace.
+//     sum.  The sum A_s is published to the workspace.
 //  2. prefix: the segments form groups of `gs` consecutive segments.  The last
 //     segment of a group publishes the GROUP sum (its own sum plus those of
 //     the earlier members) in place of its own.  The exclusive prefix of
@@ -84,7 +82,9 @@ constexpr int kKTRows = 16;
 //   [kHdr + kFlagStride * (b * nseg + s)]  flag of segment s of sequence b:
 //                          nonzero once its image is published (one flag per
 //                          256 bytes: polls of different flags do not queue
-//                          on the same memory line)
+//                          on the same memory line); the last segment never
+//                          publishes, and its slot counts the segments that
+//                          have finished reading the caller's state
 //   then BH*nseg state images: the segment sums (group sums at the last
 //   member of a group)
 // The header (counter, error, flags) is cleared by a small kernel before every
@@ -323,6 +323,40 @@ __device__ __forceinline__ int wait_flag(const int* flag, int* err, int limit) {
   }
   __hip_atomic_store(err, kN3ErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return 0;
+}
+
+// The caller's state is read by every segment of a sequence (for its prefix)
+// and overwritten in place by the last one (with the final state).  Every
+// segment but the last therefore reports, once its loads of the caller's
+// state have completed, on a per-sequence counter (the last segment's flag
+// slot, which never carries a flag); the last segment waits for all nseg - 1
+// reports before its final store.  The order is the same as for the images:
+// every wave waits for its loads to return, the waves meet at a barrier, one
+// thread bumps the counter; the writer's stores are issued only after it has
+// seen the full count.  The wait is bounded like the others, and practically
+// free: it comes after the last segment's whole replay.
+struct WaitArgs {
+  uintptr_t sync;
+  int slot, want, limit;
+};
+
+__device__ __forceinline__ void report_state_read(int* ctr) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void wait_count(const int* ctr, int want, int* err, int limit) {
+  for (int i = 0; i < limit; ++i) {
+    const int v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (v >= want) {
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(4);
+  }
+  __hip_atomic_store(err, kN3ErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- the caller's state layout <-> registers ------------------------------
@@ -998,6 +1032,7 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
   constexpr size_t kLdsBytes = kA > kAbiImg * 4 ? kA : kAbiImg * 4;
   __shared__ __align__(16) unsigned char lds_raw[kLdsBytes];
   __shared__ int s_ticket;
+  __shared__ WaitArgs s_wait;
   float* img = reinterpret_cast<float*>(lds_raw);
 
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15;
@@ -1011,6 +1046,13 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
     ticket = __builtin_amdgcn_readfirstlane(s_ticket);
   }
   const int bh = ticket / nseg, seg = ticket % nseg;
+  if (tid == 0 && seg == nseg - 1) {  // the final wait's operands, for after the replay
+    volatile WaitArgs* sw = &s_wait;
+    sw->sync = reinterpret_cast<uintptr_t>(sync);
+    sw->slot = ticket;                        // = head0 + nseg - 1, the counter's slot
+    sw->want = sync != nullptr ? nseg - 1 : 0;  // no other segment: nothing to wait for
+    sw->limit = wait_limit;
+  }
   const int t_begin = seg * cps * C;
   const int t_end = min(N, t_begin + cps * C);
   const Own<NW> own(w, li);
@@ -1021,33 +1063,30 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
   // the last member of a group publishes the group's sum, unless no group follows
   const bool leader = seg == g0 + gs - 1 && seg < nseg - 1;
 
-  // 1. the segment's own sum (not needed for the last segment).  Segment 0
-  //    adds the caller's state to its sum before publishing it, so that it is
-  //    the only workgroup of the sequence that reads the caller's state: the
-  //    last segment overwrites that state with the final one, and it does so
-  //    only after it has seen (directly, or through a group sum) segment 0's
-  //    flag, which goes up after segment 0's image stores -- built from the
-  //    caller's state -- have completed.
-  Acc acc, pre;
+  // 1. the segment's own sum (not needed for the last segment)
+  Acc acc;
   if (seg < nseg - 1) segment_sum_regs<NW>(lds_raw, own, acc, k, v, bh, N, t_begin, t_end);
   else zero_acc(acc);
-  if (seg == 0) {  // uniform; the whole prefix of segment 0
-    load_caller_state_raw<NW>(st_S, st_T, bh, own, pre);
-    unweight_caller_state<NW>(own, pre);
-    if (nseg > 1) acc_add<NW>(acc, pre, lane);
-  } else {
-    zero_acc(pre);
-  }
   // a segment that is not the last of its group publishes its sum at once
   if (nseg > 1 && !leader && seg < nseg - 1) {  // uniform
     image_store<NW, false>(image_of(seg), acc, acc, w, lane);
     raise_flag(flag_of(seg), 1);
   }
-  // 2. prefix = sums of the earlier members of the group + group sums of the
-  //    earlier groups (segment 0's sum carries the caller's state; the leader
-  //    adds the members' sums to its own as well, and publishes that as the
-  //    group sum)
-  if (nseg > 1 && seg > 0) {  // uniform
+  // Every segment's prefix starts from the caller's state, loaded after the
+  // publication (which waits for all outstanding memory operations); a leader
+  // loads it only after it has published the group sum.
+  Acc pre;
+  if (leader) {
+    zero_acc(pre);
+  } else {
+    load_caller_state_raw<NW>(st_S, st_T, bh, own, pre);
+    unweight_caller_state<NW>(own, pre);
+    if (nseg > 1 && seg < nseg - 1) report_state_read(flag_of(nseg - 1));  // uniform
+  }
+  // 2. prefix = caller's state + sums of the earlier members of the group +
+  //    group sums of the earlier groups (the leader adds the members' sums to
+  //    its own as well, and publishes that as the group sum)
+  if (nseg > 1) {  // uniform
     int* err = &sync[1];
     const int r = seg - g0;  // earlier members
     auto source = [&](int i) { return i < r ? g0 + i : (i - r) * gs + gs - 1; };
@@ -1068,8 +1107,12 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
       }
       image_store<NW, false>(image_of(seg), acc, acc, w, lane);
       raise_flag(flag_of(seg), 1);
+      Acc x;
+      load_caller_state_raw<NW>(st_S, st_T, bh, own, x);
+      unweight_caller_state<NW>(own, x);
+      report_state_read(flag_of(nseg - 1));
+      acc_add<NW>(pre, x, lane);
       for (int G = 0; G < grp; ++G) {
-        Acc x;
         wait_flag(flag_of(G * gs + gs - 1), err, wait_limit);
         image_load<NW>(image_of(G * gs + gs - 1), x, w, lane);
         acc_add<NW>(pre, x, lane);
@@ -1091,7 +1134,17 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
   }
   // 3. replay from the prefix
   segment_pass<C, NW, TOUT>(*reinterpret_cast<LB*>(lds_raw), own, pre, q, k, v, o, bh, N, t_begin, t_end, inv_a);
-  if (seg == nseg - 1) store_caller_state<NW>(img, st_S, st_T, bh, own, pre);
+  if (seg == nseg - 1) {  // uniform
+    // the wait's operands come back from LDS (stored at the start), so that
+    // none of them occupies a register during the replay
+    volatile WaitArgs* sw = &s_wait;
+    const int want = __builtin_amdgcn_readfirstlane(sw->want);
+    if (want > 0) {  // uniform
+      int* const sy = reinterpret_cast<int*>(sw->sync);
+      wait_count(&sy[kHdr + (size_t)sw->slot * kFlagStride], want, &sy[1], sw->limit);
+    }
+    store_caller_state<NW>(img, st_S, st_T, bh, own, pre);
+  }
 }
 
 // Clears the ticket counter, the error code and the nslots flags, and marks

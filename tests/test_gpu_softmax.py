@@ -192,3 +192,26 @@ def test_softmax_decode_workload_sampled(rsp):
         q1, k1, v1 = host[(b, h)]
         ref = oracle.softmax(q1, k1, v1, 1.0, rows=np.arange(N0, cap))
         assert oracle.rel_err_rowwise(got[:, b, h], ref) <= TOL["bf16"], (b, h)
+
+
+def test_softmax_f32_reference_precision_at_order_sweep(rsp):
+    """The bench reports err(n) of the n-term kernel against this library's float32
+    softmax at the order-sweep workload (B=2, H=8, N=4096, float32, a=1).  That
+    reference must sit far below the smallest err(n) reported (about 1e-5 at n = 6):
+    its Frobenius error against the float64 oracle on sampled rows is <= 2e-6, and
+    err(n) measured against it equals err(n) against the oracle to 1%."""
+    say("softmax f32 reference precision, order sweep shape")
+    B, H, N = 2, 8, 4096
+    q, k, v = TI.make_qkv(TI.SEEDS["order_sweep"], B, H, N, 16, 64)
+    got = run_prefill(rsp, q, k, v, 1.0, "f32")
+    rows = sample_rows(B, H, N, 64)
+    ref = oracle.softmax(q, k, v, 1.0, rows=rows)
+    sm = got.reshape(-1, 64)[rows]
+    assert oracle.rel_err_frobenius(sm, ref) <= 2e-6
+    assert oracle.rel_err_rowwise(sm, ref) <= 2e-5
+    for n in (3, 6):
+        st = rsp.new_state(B, H, n, device=DEV)
+        o = rsp.prefill(to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32"), st, n, 1.0, chunk=32)
+        tay = o.cpu().numpy().astype(np.float64).reshape(-1, 64)[rows]
+        e_oracle, e_kernel = oracle.rel_err_frobenius(tay, ref), oracle.rel_err_frobenius(tay, sm)
+        assert abs(e_kernel - e_oracle) <= 0.01 * e_oracle, (n, e_oracle, e_kernel)
