@@ -20,8 +20,13 @@ SOURCES = ["taylor_abi.cpp", "taylor_decode.hip", "taylor_prefill.hip", "taylor_
            "taylor_prefill_n3_c128.hip", "taylor_prefill_fb.hip",
            "softmax_attn.hip"]
 # per-source extra flags: the 64-token n = 3 prefill is scheduled for
-# instruction-level parallelism (measured faster for it, slower for 128 tokens)
-EXTRA = {"taylor_prefill_n3.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# instruction-level parallelism (measured faster for it, slower for 128 tokens);
+# the n <= 2 prefill and the softmax kernels keep matrix-core results in
+# ordinary vector registers (by default the compiler places them in the
+# accumulation registers and copies every one back with a vector instruction)
+VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+EXTRA = {"taylor_prefill_n3.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+         "taylor_prefill.hip": VGPR_MFMA, "softmax_attn.hip": VGPR_MFMA}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", CSRC, "-I", INCLUDE]

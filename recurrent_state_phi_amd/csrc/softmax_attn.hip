@@ -12,15 +12,21 @@
 //   * Scores S^T = K Q^T per 16-key tile on the matrix cores: lane (li, g)
 //     ends up with query li and keys 16 kt + 4g + r -- for one query, 16 of
 //     the block's 64 keys per lane, the other 48 in the lanes 16 and 32 apart.
-//   * exp2 of (score * log2(e) / a - m) on the vector ALU.
+//   * exp2 of (score * log2(e) / a - m) on the vector ALU, straight on the
+//     hardware exponential.  m is moved (and the accumulators rescaled) only
+//     when a row's block maximum exceeds it by more than 8 in log2 units, so
+//     most blocks skip the cross-lane maximum and the rescale; the weights
+//     stay <= 2^8, and any m shared by the lanes of a query cancels exactly.
 //   * O^T += V^T P^T on the matrix cores: the lane's weights are already in
 //     the B-operand layout (query li, keys of its lane group), and the output
 //     O^T has the query on the lane as well, so the rescale by exp2(m_old -
 //     m_new) is one multiply per accumulator.  V^T comes from LDS: every wave
-//     loads 16 keys of V as natural 16-byte row pieces and transposes them on
-//     the matrix cores (a product with one-hot operands, exact for bfloat16),
-//     so the LDS stores are 8-byte rows; double-buffered, one barrier per key
-//     block.
+//     loads 32 keys x 32 columns of V as natural 16-byte row pieces and
+//     transposes them on the matrix cores (a product with one-hot operands,
+//     exact for bfloat16), storing them in the k-slot order of the products,
+//     so LDS is written and read in 16-byte row pieces (row stride 144 bytes:
+//     16 lanes of a 16-byte access cover all 64 banks once); double-buffered,
+//     one barrier per key block.
 //   bfloat16 inputs: bfloat16 operands, float32 accumulation, the weights
 //   rounded to bfloat16 for the product and the normaliser summed from the
 //   same rounded weights (so the output is an exact weighted mean of the
@@ -50,6 +56,7 @@ constexpr int kVS = 72;    // row stride (bf16) of V^T in LDS
 constexpr int kVF = 68;    // row stride (float) of V in LDS, float32 path
 constexpr int kSplit = 2048;  // keys per decode workgroup
 constexpr int kPart = 68;     // floats per decode partial: m, l, 2 pad, 64 values
+constexpr int kBufWord3 = 0x00020000;  // buffer descriptor word 3 (gfx9: 32-bit data, raw)
 
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
   const bf16x2 p = {f32_to_bf16(lo), f32_to_bf16(hi)};
@@ -81,6 +88,21 @@ __device__ __forceinline__ float block_max(const float (&x)[4][4]) {
 }
 
 // ---- prefill, bfloat16 inputs ------------------------------------------------
+// exp2 on the hardware unit directly: every argument here is <= 0, and results
+// below the smallest normal float are weights too small to matter (they flush
+// to zero), so the range handling of exp2f is not needed.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum over the four lane groups (lanes li, li + 16, li + 32, li + 48) on the
+// vector ALU: the gfx950 lane swaps exchange rows 0 <-> 1 and 2 <-> 3 of 16
+// lanes, then the two halves of 32 lanes.
+__device__ __forceinline__ float group_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <typename TOUT>
 __global__ __launch_bounds__(256) void prefill_bf16_kernel(const uint16_t* __restrict__ q,
                                                            const uint16_t* __restrict__ k,
@@ -112,67 +134,96 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const uint16_t* __res
     sel0 = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
     sel1 = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
   }
+  // A operand with ones in row 0: ones . P^T puts the row sums of the rounded
+  // weights in row 0 of a tile (lanes 0..15)
+  const uint32_t one2 = li == 0 ? 0x3F803F80u : 0u;
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[4] = {zero, zero, zero, zero};  // O^T: lane (li, g) holds columns 16 ct + 4g + r of query li
-  float m = -__builtin_inff(), lsum = 0.0f;
+  f32x4 lacc = zero;                        // row 0: the normaliser of query li
+  float m = -__builtin_inff();              // running maximum of the raw scores (see block())
+  const float margin = 8.0f / scale;        // 2^8 in weight, in raw score units
 
-  for (int kb = 0; kb <= qb; ++kb) {
+  // loads of one key block: wave w stages keys 32h..32h+31 (h = w / 2) of
+  // the block for value columns 32c..32c+31 (c = w % 2): lane (li, g) takes
+  // columns 32c + 8g..8g+7 of keys 32h + li and 32h + 16 + li; and the four
+  // 16-key tiles of K (dimensions 4g..4g+3).  Buffer loads over this head's
+  // rows: the key block's offset is a scalar, the lane's offset a constant,
+  // and rows past N read as zero (the resource's byte limit).
+  const int vh = w >> 1, vc = w & 1;
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v + base * kDV), 0, N * kDV * 2, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + base * kD), 0, N * kD * 2, kBufWord3);
+  const int vo0 = (32 * vh + li) * kDV * 2 + (32 * vc + 8 * g) * 2, vo1 = vo0 + 16 * kDV * 2;
+  const int ko = li * kD * 2 + 8 * g;
+  uint4 pv[2];
+  uint2 pk[4];
+  auto issue = [&](int kb) {
+    const int k0 = kb * kKB;
+    pv[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo0, k0 * kDV * 2, 0));
+    pv[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, vo1, k0 * kDV * 2, 0));
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+      pk[kt] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, ko + 16 * kt * kD * 2,
+                                                                              k0 * kD * 2, 0));
+  };
+
+  auto block = [&](int kb, auto diag_c) {
+    constexpr bool DIAG = decltype(diag_c)::value;
     const int k0 = kb * kKB, buf = kb & 1;
-    // V^T of this wave's 16 keys: A = rows of V (key li, columns 8g..8g+7 and
-    // 32+8g..), times the one-hot operands -> lane (column li, g) holds keys
-    // 4g..4g+3 of the tile
-    {
-      const int key = k0 + 16 * w + li;
-      const size_t r = base + min(key, N - 1);
-      const uint4 z4 = make_uint4(0, 0, 0, 0);
-      const uint4 ra = *reinterpret_cast<const uint4*>(v + r * kDV + 8 * g);
-      const uint4 rb = *reinterpret_cast<const uint4*>(v + r * kDV + 32 + 8 * g);
-      const bf16x8 va = __builtin_bit_cast(bf16x8, key < N ? ra : z4);
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, key < N ? rb : z4);
-      const f32x4 d[4] = {mfma_bf16_k32(va, sel0, zero), mfma_bf16_k32(va, sel1, zero),
-                          mfma_bf16_k32(vb, sel0, zero), mfma_bf16_k32(vb, sel1, zero)};
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        *reinterpret_cast<uint2*>(&VT[buf][16 * ct + li][16 * w + 4 * g]) =
-            make_uint2(pack2(d[ct][0], d[ct][1]), pack2(d[ct][2], d[ct][3]));
-    }
-    // scores: S^T = K Q^T per 16-key tile; lane (li, g) gets keys 16 kt + 4g + r of query li
+    // V^T of this wave's 32 keys x 32 columns into LDS, in the k-slot order
+    // of the P.V products (row = value column, slot 8g + r = key 4g + r and
+    // slot 8g + 4 + r = key 16 + 4g + r of the 32-key half): the one-hot
+    // products give lane (column li, g) keys 4g..4g+3 of each 16-key tile, so
+    // its 8 slots are one 16-byte row piece.  And the scores S^T = K Q^T.
     f32x4 s[4];
+    {
+      const bf16x8 v0 = __builtin_bit_cast(bf16x8, pv[0]), v1 = __builtin_bit_cast(bf16x8, pv[1]);
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      const int key = min(k0 + 16 * kt + li, N - 1);
-      const bf16x4 ak = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(k + (base + key) * kD + 4 * g));
-      s[kt] = mfma_bf16_k16(ak, bq, zero);
+      for (int kt = 0; kt < 4; ++kt) s[kt] = mfma_bf16_k16(__builtin_bit_cast(bf16x4, pk[kt]), bq, zero);
+      const f32x4 d00 = mfma_bf16_k32(v0, sel0, zero), d01 = mfma_bf16_k32(v0, sel1, zero);
+      const f32x4 d10 = mfma_bf16_k32(v1, sel0, zero), d11 = mfma_bf16_k32(v1, sel1, zero);
+      if (kb < qb) issue(kb + 1);  // uniform: the next block's loads fly during this block
+      *reinterpret_cast<uint4*>(&VT[buf][32 * vc + li][32 * vh + 8 * g]) =
+          make_uint4(pack2(d00[0], d00[1]), pack2(d00[2], d00[3]), pack2(d10[0], d10[1]), pack2(d10[2], d10[3]));
+      *reinterpret_cast<uint4*>(&VT[buf][32 * vc + 16 + li][32 * vh + 8 * g]) =
+          make_uint4(pack2(d01[0], d01[1]), pack2(d01[2], d01[3]), pack2(d11[0], d11[1]), pack2(d11[2], d11[3]));
     }
-    __syncthreads();  // V^T of the block is in LDS
-
-    // log2-domain scores; keys after the query (and past N) get -inf.  Only
-    // the diagonal block can hold either.
-    float x[4][4];
-    const bool diag = kb == qb;  // uniform
+    // keys after the query (and past N) only occur in the diagonal block
+    if constexpr (DIAG) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s[kt][r] = k0 + 16 * kt + 4 * g + r > qi ? -__builtin_inff() : s[kt][r];
+    }
+    float mx = s[0][0];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + 16 * kt + 4 * g + r;
-        x[kt][r] = (diag && key > qi) ? -__builtin_inff() : s[kt][r] * scale;
-      }
-    const float m_new = fmaxf(m, block_max(x));  // finite: key k0 <= qi in every block
-    const float alpha = exp2f(m - m_new);        // 0 on the first block (m = -inf)
-    uint32_t pw[4][2];
-    float psum = 0.0f;
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][r]);
+    // The running maximum m moves only when some row's block maximum exceeds
+    // it by more than `margin` (8 in log2 units): any m common to the four
+    // lane groups of a query leaves the ratio unchanged, and with this rule
+    // every weight stays <= 2^8.  On the first block m = -inf, so it is set.
+    if (__any(mx > m + margin)) {  // uniform
+      mx = group_max(mx);
+      const float m_new = fmaxf(m, mx);  // finite: key k0 <= qi in every block
+      const float alpha = fast_exp2((m - m_new) * scale);  // 0 while m = -inf
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 4; r += 2) {
-        const uint32_t u = pack2(exp2f(x[kt][r] - m_new), exp2f(x[kt][r + 1] - m_new));
-        pw[kt][r / 2] = u;
-        psum += lo_f(u) + hi_f(u);  // the rounded weights, as used in the product
-      }
+      for (int ct = 0; ct < 4; ++ct) acc[ct] *= alpha;
+      lacc *= alpha;
+      m = m_new;
     }
-    lsum = lsum * alpha + psum;
+    const float off = m * scale;
+    uint32_t pw[4][2];
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[ct] *= alpha;
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; r += 2)
+        pw[kt][r / 2] = pack2(fast_exp2(fmaf(s[kt][r], scale, -off)), fast_exp2(fmaf(s[kt][r + 1], scale, -off)));
+    __syncthreads();  // V^T of the block is in LDS
     // O^T += V^T P^T over the two 32-key halves: k-slots 8g..8g+3 are keys
     // 32h + 4g + r, k-slots 8g+4..8g+7 keys 32h + 16 + 4g + r, on both sides
 #pragma unroll
@@ -181,17 +232,20 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const uint16_t* __res
                                                                pw[2 * h + 1][1]));
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const uint2 a0 = *reinterpret_cast<const uint2*>(&VT[buf][16 * ct + li][32 * h + 4 * g]);
-        const uint2 a1 = *reinterpret_cast<const uint2*>(&VT[buf][16 * ct + li][32 * h + 16 + 4 * g]);
-        acc[ct] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, make_uint4(a0.x, a0.y, a1.x, a1.y)), bp, acc[ct]);
+        const uint4 a = *reinterpret_cast<const uint4*>(&VT[buf][16 * ct + li][32 * h + 8 * g]);
+        acc[ct] = mfma_bf16_k32(__builtin_bit_cast(bf16x8, a), bp, acc[ct]);
       }
+      lacc = mfma_bf16_k32(ones, bp, lacc);
     }
-    m = m_new;
-  }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
+  };
+
+  issue(0);
+  for (int kb = 0; kb < qb; ++kb) block(kb, std::false_type{});
+  block(qb, std::true_type{});
+
+  const float l = __shfl(lacc[0], li);  // row 0 of the tile sits in lanes 0..15
   if (qi < N) {
-    const float inv = 1.0f / lsum;
+    const float inv = 1.0f / l;
     TOUT* orow = o + (base + qi) * kDV + 4 * g;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) store4<TOUT>(orow + 16 * ct, acc[ct] * inv);
@@ -250,13 +304,13 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(const float* __restric
         x[kt][r] = (diag && key > qi) ? -__builtin_inff() : s[kt][r] * scale;
       }
     const float m_new = fmaxf(m, block_max(x));
-    const float alpha = exp2f(m - m_new);
+    const float alpha = fast_exp2(m - m_new);
     float p[4][4], psum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[kt][r] = exp2f(x[kt][r] - m_new);
+        p[kt][r] = fast_exp2(x[kt][r] - m_new);
         psum += p[kt][r];
       }
     lsum = lsum * alpha + psum;

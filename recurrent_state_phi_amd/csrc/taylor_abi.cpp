@@ -179,7 +179,7 @@ int taylor_softmax_prefill(const void* q, const void* k, const void* v, void* o,
   if (!q || !k || !v || !o) return fail(TAYLOR_EINVAL, "taylor_softmax_prefill: NULL tensor pointer");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(TAYLOR_EINVAL, "taylor_softmax_prefill: q, k, v and o must be 16-byte aligned");
-  if ((int64_t)B * H * ((N + 63) / 64) > ((int64_t)1 << 31) - 1)
+  if ((int64_t)B * H * ((N + 63) / 64) > ((int64_t)1 << 31) - 1 || (int64_t)N * d_v * 4 > ((int64_t)1 << 31) - 1)
     return fail(TAYLOR_EINVAL, "taylor_softmax_prefill: sizes out of range");
   taylor::SoftmaxPrefillArgs args{q, k, v, o, B * H, N, a, in_dtype == TAYLOR_BF16, out_dtype == TAYLOR_BF16, stream};
   const hipError_t e = taylor::launch_softmax_prefill(args);
