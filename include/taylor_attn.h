@@ -126,6 +126,24 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, fl
                         taylor_dtype in_dtype, taylor_dtype out_dtype,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* taylor_attn_prefill for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and results without the workspace.  Its
+ * scratch is a fixed 32 MiB device array, one per GPU the library runs on,
+ * held until the process ends; this call allocates nothing and calls no
+ * allocating routine.  A plan that needs more (taylor_prefill_workspace_bytes
+ * > 32 MiB: d = 16 with n >= 4, whose per-block partial outputs are large,
+ * and the wide heads) returns TAYLOR_EINVAL with the size in the message and
+ * launches nothing; every plan with n <= 3 at d = 16 fits.  All calls on one
+ * GPU share its array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  Whatever a call
+ * leaves in the array is cleared or overwritten by the next before it is
+ * read.  A time-out of a wait between workgroups cannot be queried for this
+ * variant (taylor_prefill_check needs the workspace pointer). */
+int taylor_attn_prefill_noalloc(const void* q, const void* k, const void* v, void* o, float* state,
+                                int B, int H, int N, int d, int d_v, int n, float a, int chunk,
+                                taylor_dtype in_dtype, taylor_dtype out_dtype, hipStream_t stream);
+
 /* One decode step per head (section 3.3, Eq. (7), then Eq. (5)): update the
  * state with the new token first, then read it (the token attends to itself).
  *   q, k : device [B, H, d]; v, o : device [B, H, d_v]; dtypes as above.

@@ -22,7 +22,7 @@ __all__ = [
     "LIB_PATH", "TaylorError", "state_width", "state_numel", "new_state", "state_init",
     "state_views", "prefill_workspace_bytes", "prefill", "decode", "set_phase_events",
     "prefill_check", "set_wait_limit", "softmax_prefill", "softmax_decode", "softmax_decode_workspace_bytes",
-    "EXPORTED_SYMBOLS",
+    "prefill_noalloc", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtaylor_attn.so")
@@ -34,7 +34,7 @@ EXPORTED_SYMBOLS = (
     "taylor_state_width", "taylor_state_numel", "taylor_state_init", "taylor_prefill_workspace_bytes",
     "taylor_attn_prefill", "taylor_attn_decode", "taylor_last_error", "taylor_set_phase_events",
     "taylor_prefill_check", "taylor_set_wait_limit", "taylor_softmax_prefill",
-    "taylor_softmax_decode_workspace_bytes", "taylor_softmax_decode",
+    "taylor_softmax_decode_workspace_bytes", "taylor_softmax_decode", "taylor_attn_prefill_noalloc",
 )
 
 
@@ -63,6 +63,8 @@ _lib.taylor_prefill_workspace_bytes.argtypes = [_i, _i, _i, _i, _i, _i, _i]
 _lib.taylor_prefill_workspace_bytes.restype = _sz
 _lib.taylor_attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp, _sz, _vp]
 _lib.taylor_attn_prefill.restype = _i
+_lib.taylor_attn_prefill_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp]
+_lib.taylor_attn_prefill_noalloc.restype = _i
 _lib.taylor_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
 _lib.taylor_attn_decode.restype = _i
 _lib.taylor_last_error.argtypes = []
@@ -187,6 +189,27 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tens
                                     ws_bytes, _stream_ptr(q.device)))
     if check:
         prefill_check(workspace)
+    return out
+
+
+def prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor, n: int, a: float,
+                    chunk: int = 64, out_dtype: torch.dtype | None = None,
+                    out: torch.Tensor | None = None) -> torch.Tensor:
+    """prefill() through taylor_attn_prefill_noalloc: the library's fixed per-device
+    scratch instead of a workspace (pass ``out`` to allocate nothing here either)."""
+    B, H, N, d = q.shape
+    d_v = v.shape[-1]
+    _check_tensor("q", q, (B, H, N, d))
+    _check_tensor("k", k, (B, H, N, d), q.dtype)
+    _check_tensor("v", v, (B, H, N, d_v), q.dtype)
+    _check_tensor("state", state, (B * H * state_numel(d, d_v, n),), torch.float32)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, H, N, d_v), dtype=out_dtype, device=q.device)
+    _check_tensor("out", out, (B, H, N, d_v), out_dtype)
+    _check(_lib.taylor_attn_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state), B, H, N, d, d_v, n,
+                                            float(a), chunk, _dtype_code(q.dtype), _dtype_code(out_dtype),
+                                            _stream_ptr(q.device)))
     return out
 
 

@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "taylor_device.h"
@@ -47,6 +48,44 @@ int check_dtypes(taylor_dtype in, taylor_dtype out) {
 
 int hip_fail(hipError_t e, const char* what) {
   return fail(TAYLOR_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---- the prefill's scratch for callers that cannot allocate ------------------
+// One fixed array per device, held until the process ends.  In host code the
+// name `scratch` is only a stand-in for the symbol: its device address comes
+// from hipGetSymbolAddress, once per device (with that device current), and
+// only that address is ever handed to kernels.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array, or nullptr (message set).
+void* device_scratch(int* code) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *code = hip_fail(e, "taylor_attn_prefill_noalloc: hipGetDevice");
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *code = fail(TAYLOR_EUNSUPPORTED, "taylor_attn_prefill_noalloc: device index beyond 63");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *code = hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                       "taylor_attn_prefill_noalloc: hipGetSymbolAddress(scratch)");
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -131,6 +170,35 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, fl
   const hipError_t e = taylor::launch_prefill(args);
   if (e != hipSuccess) return hip_fail(e, "taylor_attn_prefill: kernel launch");
   return TAYLOR_OK;
+}
+
+int taylor_attn_prefill_noalloc(const void* q, const void* k, const void* v, void* o, float* state, int B, int H,
+                                int N, int d, int d_v, int n, float a, int chunk, taylor_dtype in_dtype,
+                                taylor_dtype out_dtype, hipStream_t stream) {
+  // Anything taylor_attn_prefill rejects, or does without a workspace, goes
+  // there unchanged (same checks, same messages, nothing launched on error);
+  // then the plan's workspace size is checked against the fixed scratch.
+  const bool bad = check_dtypes(in_dtype, out_dtype) != TAYLOR_OK || B < 0 || H < 0 || N < 0 || !(a > 0.0f) ||
+                   a == __builtin_inff() || !shape_supported(d, d_v, n) ||
+                   !taylor::prefill_supported(d, n, chunk, in_dtype == TAYLOR_BF16) || (int64_t)B * H == 0 ||
+                   N == 0 || !q || !k || !v || !o || !state || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+                   !aligned16(o) || !aligned16(state) || (int64_t)B * H > (1 << 24);
+  if (bad)
+    return taylor_attn_prefill(q, k, v, o, state, B, H, N, d, d_v, n, a, chunk, in_dtype, out_dtype, nullptr, 0,
+                               stream);
+  const size_t need = taylor::plan_prefill(B * H, N, d, n, chunk).workspace_floats * sizeof(float);
+  if (need > kScratchBytes)
+    return fail(TAYLOR_EINVAL, "taylor_attn_prefill_noalloc: this call needs " + std::to_string(need) +
+                                   " bytes of workspace; the fixed scratch holds " + std::to_string(kScratchBytes) +
+                                   " (use taylor_attn_prefill with a workspace)");
+  if (need == 0)
+    return taylor_attn_prefill(q, k, v, o, state, B, H, N, d, d_v, n, a, chunk, in_dtype, out_dtype, nullptr, 0,
+                               stream);
+  int code = TAYLOR_OK;
+  void* ws = device_scratch(&code);
+  if (ws == nullptr) return code;
+  return taylor_attn_prefill(q, k, v, o, state, B, H, N, d, d_v, n, a, chunk, in_dtype, out_dtype, ws,
+                             kScratchBytes, stream);
 }
 
 int taylor_attn_decode(const void* q, const void* k, const void* v, void* o, float* state, int B, int H, int d,

@@ -225,3 +225,19 @@ def test_softmax_entry_points_validate_before_launch(rsp):
     assert dec(*args(3000, 4000, wsb=2 * 2 * 68 * 4)) == -1   # two ranges need twice that
     assert b"workspace" in lib.taylor_last_error()
     assert dec(None, None, None, None, None, None, 0, 2, 0, 4, 16, 64, 1.0, 1, 0, None, 0, None) == 0
+
+
+def test_noalloc_prefill_rejects_before_any_device_work(rsp):
+    """taylor_attn_prefill_noalloc: argument errors as taylor_attn_prefill reports them,
+    and a plan whose workspace exceeds the fixed 32 MiB scratch (n = 4 at this size
+    needs about 121 MiB) is refused with the size in the message; nothing launches."""
+    lib = rsp.raw_library()
+    f = lib.taylor_attn_prefill_noalloc
+    assert f(None, None, None, None, None, 1, 1, 10, 16, 64, 3, 1.0, 64, 1, 0, None) == -1      # NULL
+    assert f(None, None, None, None, None, 1, 1, 10, 24, 64, 3, 1.0, 64, 1, 0, None) == -2      # shape
+    assert f(None, None, None, None, None, 1, 1, 10, 16, 64, 3, 1.0, 48, 1, 0, None) == -2      # chunk
+    assert f(16, 16, 16, 16, 16, 1, 1, 10, 16, 64, 3, 0.0, 64, 1, 0, None) == -1               # a
+    assert f(None, None, None, None, None, 0, 1, 10, 16, 64, 3, 1.0, 64, 1, 0, None) == 0       # empty
+    assert f(16, 16, 16, 16, 16, 2, 8, 4096, 16, 64, 4, 1.0, 32, 0, 0, None) == -1
+    msg = lib.taylor_last_error()
+    assert b"33554432" in msg and b"workspace" in msg
