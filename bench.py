@@ -353,6 +353,65 @@ def long_prefill(torch, rsp, dev, reps=5):
             "whole_call_hbm_frac": alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def decode_bf16_state(torch, rsp, dev, B, window=64, steps=256):
+    """Decode against a bfloat16-stored state (bfloat16 S, float32 T) with an exact
+    window of the last `window` tokens folded in every `window` steps, n=3, float32
+    q/k/v, H=8: microseconds per step over 256 steps (four folds), HIP-graph replay.
+    Algorithmic bytes per head and step: the bfloat16 S and float32 T read once, the
+    window tokens read (on average (K-1)/2 of them), the new token written, q, k, v
+    and o, and a K-th of the fold (S read and written, T, the K window tokens)."""
+    H, d, dv, n, a = DECODE["H"], DECODE["d"], DECODE["d_v"], 3, DECODE["a"]
+    D = state_width(d, n)
+    g = torch.Generator(device=dev).manual_seed(1012)
+    st32 = rsp.new_state(B, H, n, device=dev)
+    st32.copy_(torch.rand(st32.shape, device=dev, generator=g))  # values do not change the cost
+    sb = rsp.new_state_bf16(B, H, n, device=dev)
+    rsp.state_to_bf16(st32, sb, B, H, n)
+    del st32
+    qs = torch.randn(steps, B, H, d, device=dev, generator=g)
+    ks = torch.randn(steps, B, H, d, device=dev, generator=g)
+    vs = torch.randn(steps, B, H, dv, device=dev, generator=g)
+    qs, ks = qs / qs.norm(dim=-1, keepdim=True), ks / ks.norm(dim=-1, keepdim=True)
+    wk = torch.zeros(B, H, window, d, device=dev)
+    wv = torch.zeros(B, H, window, dv, device=dev)
+    outs = torch.empty(steps, B, H, dv, device=dev)
+
+    def run():
+        for s in range(steps):
+            rsp.decode_bf16state(qs[s], ks[s], vs[s], sb, wk, wv, s % window, n, a, out=outs[s])
+
+    run()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg, stream=side):
+        run()
+    torch.cuda.synchronize()
+    cg.replay()
+    torch.cuda.synchronize()
+    reps = 5
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    e[0].record()
+    for r in range(reps):
+        cg.replay()
+        e[r + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(e[i].elapsed_time(e[i + 1]) * 1000.0 / steps for i in range(reps))
+    us = e[0].elapsed_time(e[reps]) * 1000.0 / (steps * reps)
+    tok = 4.0 * (d + dv)
+    per_head = (2.0 * D * dv + 4.0 * D + (window - 1) / 2.0 * tok + tok + 4.0 * (2 * d + 2 * dv)
+                + (2 * 2.0 * D * dv + 2 * 4.0 * D + window * tok) / window)
+    nbytes = B * H * per_head
+    fp32_bytes = decode_algorithmic(dict(DECODE, B=B))[0]
+    return {"workload": f"decode B={B} H={H} n=3, bf16 S + fp32 T state ({B * H * D * (2 * dv + 4) / 1e6:.0f} MB), "
+                        f"exact window of {window} fp32 tokens folded every {window} steps, {steps} steps",
+            "us_per_step": us, "us_min": per[0], "us_median": per[reps // 2],
+            "algorithmic_bytes_per_step": nbytes, "fp32_state_bytes_per_step": fp32_bytes,
+            "roofline": {"bound": "hbm", "achieved": nbytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}}
+
+
 SOFTMAX_PREFILL_NS = (256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
 SOFTMAX_DECODE_CTX = (1024, 4096, 16384, 65536)
 EXP_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9   # v_exp_f32: quarter of the 16 lanes per SIMD per cycle
@@ -606,6 +665,9 @@ def main():
                 "frac": big_bytes / (big_best["mean"] * 1e-6) / 1e9 / HBM_PEAK_GBS,
                 "algorithmic_bytes_per_step": big_bytes},
         }
+        print("[bench] decode against a bf16-stored state", file=sys.stderr, flush=True)
+        extra["decode_bf16_state"] = {"B64": decode_bf16_state(torch, rsp, dev, 64),
+                                      "B1024": decode_bf16_state(torch, rsp, dev, 1024)}
         print("[bench] softmax decode against a bf16 key-value cache", file=sys.stderr, flush=True)
         extra["softmax_decode_comparison"] = softmax_decode_comparison(torch, rsp, dev, best["mean"])
     if args.only == "all" and not args.no_secondary:

@@ -152,6 +152,42 @@ int taylor_attn_decode(const void* q, const void* k, const void* v, void* o, flo
                        int B, int H, int d, int d_v, int n, float a,
                        taylor_dtype in_dtype, taylor_dtype out_dtype, hipStream_t stream);
 
+/* ---- bfloat16 state storage (section 5.8 sizes the states in bfloat16) -----
+ * A state whose S part (the D x d_v block) is kept in bfloat16, with T (the
+ * ones-column, D floats) in float32, and decode steps against it.  Rounding the
+ * state after every token would lose most tokens' increments (a row of S sums
+ * the whole context, one token's term is below half a bfloat16 unit of it), so
+ * the last tokens are kept exactly in a window of K (k, v) pairs, read with the
+ * same weights p_n(q.k / a) as the state, and folded into the bfloat16 S once
+ * every K tokens (one rounding per K tokens).  Outputs are the n-term Taylor
+ * attention of Eq. (5) over all keys; the bfloat16 base is the only lossy part.
+ * Built for d = 16, d_v = 64, n <= 3, 1 <= K <= 128.
+ * Layout of a bfloat16 state (16-byte aligned, device): S[B][H][D][d_v] as
+ * bfloat16 (value index fastest, rows and weights as in the float32 state),
+ * then T[B][H][D] as float32.  Window: win_k [B, H, K, d], win_v [B, H, K, d_v]
+ * in in_dtype, caller-owned; its contents between folds belong to the state. */
+
+/* Bytes per head of a bfloat16 state: D * d_v * 2 + D * 4.  Host only; -1 on
+ * invalid arguments. */
+int64_t taylor_state_bf16_bytes(int d, int d_v, int n);
+
+/* Round a float32 state (e.g. after a prefill) to the bfloat16 layout above
+ * (round to nearest even; T copied).  The window starts empty (step 0). */
+int taylor_state_to_bf16(const float* state, void* state_bf16, int B, int H, int d, int d_v, int n,
+                         hipStream_t stream);
+
+/* One decode step against a bfloat16 state.  `step` (0 <= step < window) is
+ * the number of tokens in the window since the last fold; the call writes the
+ * token (k, v) into window slot `step`, computes
+ *   o = (phi_hat(q) [S | T] + sum_{j <= step} p_n(q.k_j / a) [v_j; 1])[:d_v] / (same)[d_v],
+ * and when step == window - 1 folds the window into the state (the next call
+ * then passes step 0).  Every stream of the batch is at the same step.  No
+ * workspace; allocates nothing. */
+int taylor_attn_decode_bf16state(const void* q, const void* k, const void* v, void* o, void* state_bf16,
+                                 void* win_k, void* win_v, int step, int window, int B, int H, int d, int d_v,
+                                 int n, float a, taylor_dtype in_dtype, taylor_dtype out_dtype,
+                                 hipStream_t stream);
+
 /* ---- Exact causal softmax attention: the comparison method ---------------
  * Eq. (1) with the exponential kernel itself, o_t = sum_{i<=t} e^{q_t.k_i/a} v_i /
  * sum_{i<=t} e^{q_t.k_i/a}: what the paper measures the Taylor states against

@@ -22,7 +22,8 @@ __all__ = [
     "LIB_PATH", "TaylorError", "state_width", "state_numel", "new_state", "state_init",
     "state_views", "prefill_workspace_bytes", "prefill", "decode", "set_phase_events",
     "prefill_check", "set_wait_limit", "softmax_prefill", "softmax_decode", "softmax_decode_workspace_bytes",
-    "prefill_noalloc", "EXPORTED_SYMBOLS",
+    "prefill_noalloc", "state_bf16_bytes", "new_state_bf16", "state_to_bf16", "state_bf16_views",
+    "decode_bf16state", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtaylor_attn.so")
@@ -35,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "taylor_attn_prefill", "taylor_attn_decode", "taylor_last_error", "taylor_set_phase_events",
     "taylor_prefill_check", "taylor_set_wait_limit", "taylor_softmax_prefill",
     "taylor_softmax_decode_workspace_bytes", "taylor_softmax_decode", "taylor_attn_prefill_noalloc",
+    "taylor_state_bf16_bytes", "taylor_state_to_bf16", "taylor_attn_decode_bf16state",
 )
 
 
@@ -65,6 +67,13 @@ _lib.taylor_attn_prefill.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i
 _lib.taylor_attn_prefill.restype = _i
 _lib.taylor_attn_prefill_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i, _i, _i, _vp]
 _lib.taylor_attn_prefill_noalloc.restype = _i
+_lib.taylor_state_bf16_bytes.argtypes = [_i, _i, _i]
+_lib.taylor_state_bf16_bytes.restype = _i64
+_lib.taylor_state_to_bf16.argtypes = [_vp, _vp, _i, _i, _i, _i, _i, _vp]
+_lib.taylor_state_to_bf16.restype = _i
+_lib.taylor_attn_decode_bf16state.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i,
+                                              _i, _vp]
+_lib.taylor_attn_decode_bf16state.restype = _i
 _lib.taylor_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
 _lib.taylor_attn_decode.restype = _i
 _lib.taylor_last_error.argtypes = []
@@ -303,4 +312,57 @@ def softmax_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_cache: t
     _check(_lib.taylor_softmax_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(k_cache), _ptr(v_cache), B, H,
                                       int(pos), cap, d, d_v, float(a), _dtype_code(q.dtype), _dtype_code(out_dtype),
                                       _ptr(workspace), workspace.numel() * 4, _stream_ptr(q.device)))
+    return out
+
+
+# ---- bfloat16 state storage with an exact window of recent tokens ------------
+def state_bf16_bytes(d: int, d_v: int, n: int) -> int:
+    """Bytes per head of a bfloat16 state (bfloat16 S, float32 T)."""
+    return int(_lib.taylor_state_bf16_bytes(d, d_v, n))
+
+
+def new_state_bf16(B: int, H: int, n: int, d: int = 16, d_v: int = 64, device="cuda") -> torch.Tensor:
+    """An uninitialised bfloat16-state buffer (uint8, see :func:`state_bf16_views`)."""
+    return torch.empty(B * H * state_bf16_bytes(d, d_v, n), dtype=torch.uint8, device=device)
+
+
+def state_to_bf16(state: torch.Tensor, state_bf16: torch.Tensor, B: int, H: int, n: int, d: int = 16,
+                  d_v: int = 64) -> torch.Tensor:
+    """Round a float32 state into a bfloat16-state buffer (enqueued on the current stream)."""
+    _check_tensor("state", state, (B * H * state_numel(d, d_v, n),), torch.float32)
+    _check_tensor("state_bf16", state_bf16, (B * H * state_bf16_bytes(d, d_v, n),), torch.uint8)
+    _check(_lib.taylor_state_to_bf16(_ptr(state), _ptr(state_bf16), B, H, d, d_v, n, _stream_ptr(state.device)))
+    return state_bf16
+
+
+def state_bf16_views(state_bf16: torch.Tensor, B: int, H: int, n: int, d: int = 16, d_v: int = 64):
+    """(S [B,H,D,d_v] bfloat16, T [B,H,D] float32) views of a bfloat16-state buffer."""
+    D = state_width(d, n)
+    ns = B * H * D * d_v * 2
+    S = state_bf16[:ns].view(torch.bfloat16).view(B, H, D, d_v)
+    T = state_bf16[ns: ns + B * H * D * 4].view(torch.float32).view(B, H, D)
+    return S, T
+
+
+def decode_bf16state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state_bf16: torch.Tensor,
+                     win_k: torch.Tensor, win_v: torch.Tensor, step: int, n: int, a: float,
+                     out_dtype: torch.dtype | None = None, out: torch.Tensor | None = None) -> torch.Tensor:
+    """One decode step against a bfloat16 state with a window of win_k.shape[2] tokens;
+    ``step`` = tokens in the window since the last fold (folds when it reaches K - 1)."""
+    B, H, d = q.shape
+    d_v = v.shape[-1]
+    K = win_k.shape[2]
+    _check_tensor("q", q, (B, H, d))
+    _check_tensor("k", k, (B, H, d), q.dtype)
+    _check_tensor("v", v, (B, H, d_v), q.dtype)
+    _check_tensor("state_bf16", state_bf16, (B * H * state_bf16_bytes(d, d_v, n),), torch.uint8)
+    _check_tensor("win_k", win_k, (B, H, K, d), q.dtype)
+    _check_tensor("win_v", win_v, (B, H, K, d_v), q.dtype)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=out_dtype, device=q.device)
+    _check_tensor("out", out, (B, H, d_v), out_dtype)
+    _check(_lib.taylor_attn_decode_bf16state(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_bf16), _ptr(win_k),
+                                             _ptr(win_v), int(step), K, B, H, d, d_v, n, float(a),
+                                             _dtype_code(q.dtype), _dtype_code(out_dtype), _stream_ptr(q.device)))
     return out

@@ -287,4 +287,50 @@ int taylor_softmax_decode(const void* q, const void* k, const void* v, void* o, 
   return TAYLOR_OK;
 }
 
+int64_t taylor_state_bf16_bytes(int d, int d_v, int n) {
+  if (d_v < 1) return -1;
+  const int64_t D = taylor_state_width(d, n);
+  return D < 0 ? -1 : D * (int64_t)d_v * 2 + D * 4;
+}
+
+int taylor_state_to_bf16(const float* state, void* state_bf16, int B, int H, int d, int d_v, int n,
+                         hipStream_t stream) {
+  if (B < 0 || H < 0) return fail(TAYLOR_EINVAL, "taylor_state_to_bf16: B and H must be >= 0");
+  if (d != taylor::kD || d_v != taylor::kDV || n < 1 || n > 3)
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_state_to_bf16: only d = 16, d_v = 64, n <= 3 are built");
+  if ((int64_t)B * H == 0) return TAYLOR_OK;
+  if (!state || !state_bf16) return fail(TAYLOR_EINVAL, "taylor_state_to_bf16: NULL pointer");
+  if (!aligned16(state) || !aligned16(state_bf16))
+    return fail(TAYLOR_EINVAL, "taylor_state_to_bf16: buffers must be 16-byte aligned");
+  const hipError_t e = taylor::launch_state_to_bf16(state, state_bf16, B * H, (int)taylor_state_width(d, n), stream);
+  if (e != hipSuccess) return hip_fail(e, "taylor_state_to_bf16: kernel launch");
+  return TAYLOR_OK;
+}
+
+int taylor_attn_decode_bf16state(const void* q, const void* k, const void* v, void* o, void* state_bf16,
+                                 void* win_k, void* win_v, int step, int window, int B, int H, int d, int d_v,
+                                 int n, float a, taylor_dtype in_dtype, taylor_dtype out_dtype, hipStream_t stream) {
+  if (int e = check_dtypes(in_dtype, out_dtype)) return e;
+  if (B < 0 || H < 0) return fail(TAYLOR_EINVAL, "taylor_attn_decode_bf16state: B and H must be >= 0");
+  if (!(a > 0.0f) || a == __builtin_inff())
+    return fail(TAYLOR_EINVAL, "taylor_attn_decode_bf16state: a must be finite and > 0");
+  if (d != taylor::kD || d_v != taylor::kDV || n < 1 || n > 3)
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_attn_decode_bf16state: only d = 16, d_v = 64, n <= 3 are built");
+  if (window < 1 || window > taylor::bf16_decode_max_window() || step < 0 || step >= window)
+    return fail(TAYLOR_EINVAL, "taylor_attn_decode_bf16state: need 1 <= window <= " +
+                                   std::to_string(taylor::bf16_decode_max_window()) + " and 0 <= step < window");
+  if ((int64_t)B * H == 0) return TAYLOR_OK;
+  if ((int64_t)B * H > (1 << 30)) return fail(TAYLOR_EINVAL, "taylor_attn_decode_bf16state: B*H out of range");
+  if (!q || !k || !v || !o || !state_bf16 || !win_k || !win_v)
+    return fail(TAYLOR_EINVAL, "taylor_attn_decode_bf16state: NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state_bf16) ||
+      !aligned16(win_k) || !aligned16(win_v))
+    return fail(TAYLOR_EINVAL, "taylor_attn_decode_bf16state: buffers must be 16-byte aligned");
+  taylor::Bf16DecodeArgs args{q, k, v, o, state_bf16, win_k, win_v, B * H, n, step, window, a,
+                              in_dtype == TAYLOR_BF16, out_dtype == TAYLOR_BF16, stream};
+  const hipError_t e = taylor::launch_decode_bf16state(args);
+  if (e != hipSuccess) return hip_fail(e, "taylor_attn_decode_bf16state: kernel launch");
+  return TAYLOR_OK;
+}
+
 }  // extern "C"

@@ -99,4 +99,19 @@ hipError_t launch_softmax_decode(const SoftmaxDecodeArgs& a);
 int softmax_decode_splits(int len);
 size_t softmax_decode_workspace_floats(int BH, int cap);
 
+// Decode against a bfloat16-stored state with an exact window of recent tokens
+// (taylor_decode_bf16.hip), d = 16, d_v = 64, n <= 3.
+struct Bf16DecodeArgs {
+  const void* q; const void* k; const void* v; void* o;
+  void* state;  // bfloat16 S of all heads, then float32 T
+  void* win_k; void* win_v;
+  int BH, n, step, window;
+  float a;
+  bool in_bf16, out_bf16;
+  hipStream_t stream;
+};
+hipError_t launch_decode_bf16state(const Bf16DecodeArgs& a);
+hipError_t launch_state_to_bf16(const float* state, void* state_bf16, int BH, int D, hipStream_t stream);
+int bf16_decode_max_window();
+
 }  // namespace taylor
