@@ -10,6 +10,10 @@ with a Fixed Number of Recurrent States" (arXiv 2610.20637).
 * :func:`taylor_direct` -- section 3.1, Eq. (1) with exp replaced by the
   n-term polynomial of Eq. (2); the plain O(N^2) causal sum (C, float64).
 * :func:`softmax` -- exact causal softmax, Eq. (1) (C, float64).
+* :func:`hybrid_direct` -- the eviction-fed hybrid of "Tensor Cache:
+  Eviction-conditioned Associative Memory for Transformers" (sections 3.1-3.2)
+  with the Taylor kernel as its memory: exp weights inside the window of the
+  last W keys, p_n weights for the evicted keys (C, float64).
 * :mod:`oracle.recurrent` -- the recurrent state form of sections 3.2-3.4
   (float64 NumPy), used to pin the direct form and to check exported states.
 * :func:`rel_err_rowwise`, :func:`convergence_report` -- the error measures
@@ -57,6 +61,9 @@ def _lib():
         lib.oracle_set_num_threads.restype = None
         lib.oracle_taylor_weights.argtypes = [_dp, _i64, ctypes.c_int, ctypes.c_double, _dp]
         lib.oracle_taylor_weights.restype = None
+        lib.oracle_hybrid_direct.argtypes = [_fp, _fp, _fp, _i64, _i64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_double, _i64, _lp, _i64, _dp]
+        lib.oracle_hybrid_direct.restype = None
         _LIB = lib
     return _LIB
 
@@ -126,6 +133,24 @@ def softmax(q, k, v, a: float, rows=None):
     o = np.empty((nrows, dv), np.float64)
     _lib().oracle_softmax(q.ctypes.data_as(_fp), k.ctypes.data_as(_fp), v.ctypes.data_as(_fp),
                           BH, N, d, dv, float(a), rp, nrows, o.ctypes.data_as(_dp))
+    if r is None:
+        o = o.reshape(q.shape[:-1] + (dv,))
+    return o
+
+
+def hybrid_direct(q, k, v, n: int, a: float, window: int, rows=None):
+    """Eviction-fed hybrid, float64, direct O(N^2) sum ("Tensor Cache", sections
+    3.1-3.2, with the Taylor-state page's Eq. (2) for the memory): for row t the keys
+    i > t - window weigh exp(q.k/a) (the window), the keys i <= t - window weigh
+    p_n(q.k/a) (evicted into the memory); one normaliser.  window = 0 is the n-term
+    kernel, window >= N exact softmax."""
+    q, k, v, BH, N, d = _prep(q, k, v)
+    dv = v.shape[-1]
+    r, rp = _rows_arg(rows)
+    nrows = BH * N if r is None else r.size
+    o = np.empty((nrows, dv), np.float64)
+    _lib().oracle_hybrid_direct(q.ctypes.data_as(_fp), k.ctypes.data_as(_fp), v.ctypes.data_as(_fp),
+                                BH, N, d, dv, int(n), float(a), int(window), rp, nrows, o.ctypes.data_as(_dp))
     if r is None:
         o = o.reshape(q.shape[:-1] + (dv,))
     return o

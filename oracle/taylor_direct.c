@@ -151,3 +151,40 @@ void oracle_arg_stats(const float* q, const float* k, int64_t BH, int64_t N, int
     *sum_abs = gsum;
     *npairs = gcnt;
 }
+
+/* Eviction-fed hybrid ("Tensor Cache: Eviction-conditioned Associative
+ * Memory for Transformers", sections 3.1-3.2: a FIFO window of the last W
+ * key-value pairs read by exact softmax attention, and a memory written only
+ * with the pairs the window evicts), with the memory read through the n-term
+ * Taylor kernel of the Taylor-state page (Eq. (2) there).  Every earlier token
+ * feeds exactly one read path: for row t the keys i > t - W are in the window
+ * and weigh exp(q.k/a); the keys i <= t - W have been evicted into the memory
+ * and weigh p_n(q.k/a).  Both paths share one normaliser:
+ *   o_t = sum_{i<=t} w_i v_i / sum_{i<=t} w_i.
+ * W = 0 is the pure Taylor kernel, W >= t + 1 exact softmax.  The plain
+ * definition, exp without any shift (the inputs it is used on keep |q.k/a|
+ * small). */
+void oracle_hybrid_direct(const float* q, const float* k, const float* v,
+                          int64_t BH, int64_t N, int d, int dv, int n, double a, int64_t W,
+                          const int64_t* rows, int64_t nrows, double* o) {
+    if (rows == NULL) nrows = BH * N;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t flat = rows ? rows[r] : r;
+        const int64_t bh = flat / N, t = flat % N;
+        const float* qt = q + (size_t)flat * d;
+        const float* kb = k + (size_t)bh * N * d;
+        const float* vb = v + (size_t)bh * N * dv;
+        double* out = o + (size_t)r * dv;
+        for (int c = 0; c < dv; ++c) out[c] = 0.0;
+        double z = 0.0;
+        for (int64_t i = 0; i <= t; ++i) {
+            const double y = dot_f64(qt, kb + (size_t)i * d, d) / a;
+            const double w = (i > t - W) ? exp(y) : taylor_weight(y, n);
+            const float* vi = vb + (size_t)i * dv;
+            for (int c = 0; c < dv; ++c) out[c] += w * (double)vi[c];
+            z += w;
+        }
+        for (int c = 0; c < dv; ++c) out[c] /= z;
+    }
+}

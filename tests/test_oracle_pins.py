@@ -384,3 +384,49 @@ def test_arg_stats_matches_brute_force():
     mx2, mean2 = oracle.arg_stats(q, k, a, rows=rows)
     assert mx2 == pytest.approx(max(sub), rel=1e-14)
     assert mean2 == pytest.approx(sum(sub) / len(sub), rel=1e-13)
+
+
+# --------------------------------------------------------------------------
+# The eviction-fed hybrid ("Tensor Cache: Eviction-conditioned Associative
+# Memory for Transformers", sections 3.1-3.2, with the Taylor kernel as the
+# memory): window keys weigh exp(q.k/a), evicted keys p_n(q.k/a).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 3, 4])
+def test_hybrid_limits_are_taylor_and_softmax(n):
+    """No window: every key is in the memory (the n-term kernel).  A window as long
+    as the sequence: nothing is evicted (exact softmax)."""
+    q, k, v = TI.make_qkv(61, 1, 2, 90, 16, 64)
+    assert oracle.rel_err_rowwise(oracle.hybrid_direct(q, k, v, n, 1.3, 0), oracle.taylor_direct(q, k, v, n, 1.3)) \
+        <= 1e-14
+    assert oracle.rel_err_rowwise(oracle.hybrid_direct(q, k, v, n, 1.3, 90), oracle.softmax(q, k, v, 1.3)) <= 1e-13
+    assert oracle.rel_err_rowwise(oracle.hybrid_direct(q, k, v, n, 1.3, 500), oracle.softmax(q, k, v, 1.3)) <= 1e-13
+
+
+@pytest.mark.parametrize("W", [1, 5, 17])
+def test_hybrid_window_partition_closed_form(W):
+    """All keys equal: row t's score s is the same for every key, so with
+    n_w = min(W, t + 1) keys in the window and the other t + 1 - n_w evicted,
+    o_t = (e^s * sum_window v + p_n(s) * sum_evicted v) / (n_w e^s + (t + 1 - n_w) p_n(s)).
+    An off-by-one in the window boundary changes n_w and fails this."""
+    n, a, N = 3, 0.7, 40
+    q, k, v = TI.make_qkv(62, 1, 1, N, 8, 5)
+    k = np.ascontiguousarray(np.broadcast_to(k[:, :, :1], k.shape))
+    got = oracle.hybrid_direct(q, k, v, n, a, W)[0, 0]
+    vv = v[0, 0].astype(np.float64)
+    for t in range(N):
+        s = float(q[0, 0, t].astype(np.float64) @ k[0, 0, 0].astype(np.float64)) / a
+        e, p = math.exp(s), 1 + s + s * s / 2
+        nw = min(W, t + 1)
+        win, ev = vv[t + 1 - nw: t + 1].sum(0), vv[: t + 1 - nw].sum(0)
+        want = (e * win + p * ev) / (nw * e + (t + 1 - nw) * p)
+        assert np.abs(got[t] - want).max() <= 1e-14 * max(1.0, np.abs(want).max()), t
+
+
+def test_hybrid_error_falls_with_the_window():
+    """With unit-norm q, k the hybrid sits between the n-term kernel and softmax, and
+    its error against softmax shrinks as the window grows (plausibility)."""
+    q, k, v = TI.make_qkv(63, 1, 1, 600, 16, 64)
+    ref = oracle.softmax(q, k, v, 1.0)
+    errs = [oracle.rel_err_frobenius(oracle.hybrid_direct(q, k, v, 2, 1.0, W), ref) for W in (0, 64, 256, 599)]
+    assert all(errs[i + 1] < errs[i] for i in range(3))
+    assert errs[0] == pytest.approx(oracle.rel_err_frobenius(oracle.taylor_direct(q, k, v, 2, 1.0), ref))
