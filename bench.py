@@ -412,6 +412,85 @@ def decode_bf16_state(torch, rsp, dev, B, window=64, steps=256):
                          "unit": "GB/s", "frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}}
 
 
+def decode_method_comparison(torch, rsp, dev, W=256, steps=256):
+    """The same 64 x 8 streams after a 65,536-token context, float32 q/k/v, a=1, n=3,
+    decoded three ways for 256 steps: the Taylor state (fp32), the eviction-fed hybrid
+    (exact softmax over a window of the last W tokens, the Taylor state for the
+    evicted ones), and exact softmax over a float32 key-value cache.  Reports each
+    method's microseconds per step (HIP-graph replay) and the Frobenius-relative
+    error of the Taylor and hybrid outputs against the softmax kernel's."""
+    B, H, d, dv, n, a = DECODE["B"], DECODE["H"], DECODE["d"], DECODE["d_v"], 3, DECODE["a"]
+    N0 = DECODE["N0"]
+    cap = N0 + steps
+    g = torch.Generator(device=dev).manual_seed(1013)
+    st_t = rsp.new_state(B, H, n, device=dev)
+    st_h = rsp.new_state(B, H, n, device=dev)
+    wk = torch.empty(B, H, W, d, device=dev)
+    wv = torch.empty(B, H, W, dv, device=dev)
+    kc = torch.empty(B, H, cap, d, device=dev)
+    vc = torch.empty(B, H, cap, dv, device=dev)
+    for t0 in range(0, N0, 8192):
+        qx = torch.randn(B, H, 8192, d, device=dev, generator=g)
+        kx = torch.randn(B, H, 8192, d, device=dev, generator=g)
+        vx = torch.randn(B, H, 8192, dv, device=dev, generator=g)
+        qx, kx = qx / qx.norm(dim=-1, keepdim=True), kx / kx.norm(dim=-1, keepdim=True)
+        rsp.prefill(qx, kx, vx, st_t, n, a, chunk=64)
+        m = min(8192, N0 - W - t0)
+        rsp.prefill(qx[:, :, :m].contiguous(), kx[:, :, :m].contiguous(), vx[:, :, :m].contiguous(), st_h, n, a,
+                    chunk=64)
+        if t0 + 8192 == N0:  # positions N0 - 8192 .. N0 - 1 (a multiple of W before): ring slot i % W
+            rsp.hybrid_fill_window(kx, vx, wk, wv)
+        kc[:, :, t0:t0 + 8192] = kx
+        vc[:, :, t0:t0 + 8192] = vx
+        del qx, kx, vx
+    qs = torch.randn(steps, B, H, d, device=dev, generator=g)
+    ks = torch.randn(steps, B, H, d, device=dev, generator=g)
+    vs = torch.randn(steps, B, H, dv, device=dev, generator=g)
+    qs, ks = qs / qs.norm(dim=-1, keepdim=True), ks / ks.norm(dim=-1, keepdim=True)
+    ws = torch.empty(rsp.softmax_decode_workspace_bytes(B, H, cap) // 4, device=dev)
+    outs = {name: torch.empty(steps, B, H, dv, device=dev) for name in ("taylor", "hybrid", "softmax")}
+    runs = {
+        "taylor": lambda: [rsp.decode(qs[s], ks[s], vs[s], st_t, n, a, out=outs["taylor"][s]) for s in range(steps)],
+        "hybrid": lambda: [rsp.hybrid_decode(qs[s], ks[s], vs[s], st_h, wk, wv, N0 + s, n, a, out=outs["hybrid"][s])
+                           for s in range(steps)],
+        "softmax": lambda: [rsp.softmax_decode(qs[s], ks[s], vs[s], kc, vc, N0 + s, a, ws, out=outs["softmax"][s])
+                            for s in range(steps)],
+    }
+    res = {}
+    saved = {}
+    for name, fn in runs.items():
+        fn()  # the outputs of the first pass, from the context's state, are the ones compared
+        torch.cuda.synchronize()
+        saved[name] = outs[name].clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg, stream=side):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        cg.replay()
+        e0.record()
+        cg.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"us_per_step": e0.elapsed_time(e1) * 1000.0 / steps}
+        del cg
+    ref = saved["softmax"].double()
+    for name in ("taylor", "hybrid"):
+        res[name]["err_vs_softmax_frobenius"] = float((saved[name].double() - ref).norm() / ref.norm())
+    D = state_width(d, n)
+    hy_bytes = B * H * (2 * 4.0 * D * (dv + 1) + W * 4.0 * (d + dv) + 2 * 4.0 * (d + dv) + 4.0 * (2 * d + 2 * dv))
+    us = res["hybrid"]["us_per_step"]
+    res["hybrid"]["roofline"] = {"bound": "hbm", "achieved": hy_bytes / (us * 1e-6) / 1e9, "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": hy_bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                 "algorithmic_bytes_per_step": hy_bytes}
+    return {"workload": f"decode B={B} H={H} n=3 a=1, float32 q/k/v, after a {N0}-token context, {steps} steps: "
+                        f"Taylor state, eviction-fed hybrid (softmax window of {W}, Taylor state for the evicted "
+                        "tokens), exact softmax over a float32 cache",
+            **res}
+
+
 SOFTMAX_PREFILL_NS = (256, 512, 1024, 2048, 4096, 8192, 16384, 32768)
 SOFTMAX_DECODE_CTX = (1024, 4096, 16384, 65536)
 EXP_PEAK_PER_S = 256 * 4 * 16 / 4 * 2.4e9   # v_exp_f32: quarter of the 16 lanes per SIMD per cycle
@@ -668,6 +747,8 @@ def main():
         print("[bench] decode against a bf16-stored state", file=sys.stderr, flush=True)
         extra["decode_bf16_state"] = {"B64": decode_bf16_state(torch, rsp, dev, 64),
                                       "B1024": decode_bf16_state(torch, rsp, dev, 1024)}
+        print("[bench] decode methods compared: Taylor, hybrid, softmax", file=sys.stderr, flush=True)
+        extra["decode_methods"] = decode_method_comparison(torch, rsp, dev)
         print("[bench] softmax decode against a bf16 key-value cache", file=sys.stderr, flush=True)
         extra["softmax_decode_comparison"] = softmax_decode_comparison(torch, rsp, dev, best["mean"])
     if args.only == "all" and not args.no_secondary:

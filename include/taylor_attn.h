@@ -188,6 +188,33 @@ int taylor_attn_decode_bf16state(const void* q, const void* k, const void* v, vo
                                  int n, float a, taylor_dtype in_dtype, taylor_dtype out_dtype,
                                  hipStream_t stream);
 
+/* ---- Eviction-fed hybrid ------------------------------------------------------
+ * "Tensor Cache: Eviction-conditioned Associative Memory for Transformers"
+ * (sections 3.1-3.2): a FIFO window of the last W key-value pairs read by
+ * exact softmax, and a memory written only with the pairs the window evicts;
+ * here the memory is the n-term Taylor state above (that page fuses its two
+ * paths with a learned gate; without training, both paths share one
+ * normaliser).  For the token at position t:
+ *   o_t = (sum_{t-W < i <= t} e^{q.k_i/a} [v_i; 1] + phi_hat(q_t) A)[:d_v] / (same)[d_v],
+ * A = the float32 state of the tokens i <= t - W (layout as above).  W = 1 ..
+ * 1024, d = 16, d_v = 64, n <= 3.  Window ring: win_k [B, H, W, d], win_v
+ * [B, H, W, d_v] in in_dtype; position i lives in slot i % W. */
+
+/* Fill the ring from a context of N tokens (k, v [B, H, N, d / d_v]): its last
+ * min(N, W) tokens go to their slots.  Together with a prefill of the first
+ * max(0, N - W) tokens into the state, this is the hybrid's state after N
+ * tokens. */
+int taylor_hybrid_fill_window(const void* k, const void* v, void* win_k, void* win_v, int B, int H, int N,
+                              int window, int d, int d_v, taylor_dtype in_dtype, hipStream_t stream);
+
+/* One decode step at position pos (the number of earlier tokens; all streams
+ * alike): the token at pos - W (if pos >= W) leaves the window and is added to
+ * the state (write-on-evict, Eq. (7) of the Taylor-state page); the new token
+ * takes its slot; o is computed as above.  No workspace. */
+int taylor_hybrid_decode(const void* q, const void* k, const void* v, void* o, float* state, void* win_k,
+                         void* win_v, int pos, int window, int B, int H, int d, int d_v, int n, float a,
+                         taylor_dtype in_dtype, taylor_dtype out_dtype, hipStream_t stream);
+
 /* ---- Exact causal softmax attention: the comparison method ---------------
  * Eq. (1) with the exponential kernel itself, o_t = sum_{i<=t} e^{q_t.k_i/a} v_i /
  * sum_{i<=t} e^{q_t.k_i/a}: what the paper measures the Taylor states against

@@ -23,7 +23,7 @@ __all__ = [
     "state_views", "prefill_workspace_bytes", "prefill", "decode", "set_phase_events",
     "prefill_check", "set_wait_limit", "softmax_prefill", "softmax_decode", "softmax_decode_workspace_bytes",
     "prefill_noalloc", "state_bf16_bytes", "new_state_bf16", "state_to_bf16", "state_bf16_views",
-    "decode_bf16state", "EXPORTED_SYMBOLS",
+    "decode_bf16state", "hybrid_fill_window", "hybrid_decode", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtaylor_attn.so")
@@ -37,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "taylor_prefill_check", "taylor_set_wait_limit", "taylor_softmax_prefill",
     "taylor_softmax_decode_workspace_bytes", "taylor_softmax_decode", "taylor_attn_prefill_noalloc",
     "taylor_state_bf16_bytes", "taylor_state_to_bf16", "taylor_attn_decode_bf16state",
+    "taylor_hybrid_fill_window", "taylor_hybrid_decode",
 )
 
 
@@ -74,6 +75,10 @@ _lib.taylor_state_to_bf16.restype = _i
 _lib.taylor_attn_decode_bf16state.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i,
                                               _i, _vp]
 _lib.taylor_attn_decode_bf16state.restype = _i
+_lib.taylor_hybrid_fill_window.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]
+_lib.taylor_hybrid_fill_window.restype = _i
+_lib.taylor_hybrid_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
+_lib.taylor_hybrid_decode.restype = _i
 _lib.taylor_attn_decode.argtypes = [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
 _lib.taylor_attn_decode.restype = _i
 _lib.taylor_last_error.argtypes = []
@@ -365,4 +370,42 @@ def decode_bf16state(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state_bf
     _check(_lib.taylor_attn_decode_bf16state(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state_bf16), _ptr(win_k),
                                              _ptr(win_v), int(step), K, B, H, d, d_v, n, float(a),
                                              _dtype_code(q.dtype), _dtype_code(out_dtype), _stream_ptr(q.device)))
+    return out
+
+
+# ---- eviction-fed hybrid: softmax window + Taylor state for the evicted tokens --
+def hybrid_fill_window(k: torch.Tensor, v: torch.Tensor, win_k: torch.Tensor, win_v: torch.Tensor) -> None:
+    """Put the last min(N, W) tokens of a context k [B,H,N,d], v [B,H,N,d_v] into
+    their ring slots (position i in slot i % W)."""
+    B, H, N, d = k.shape
+    d_v = v.shape[-1]
+    W = win_k.shape[2]
+    _check_tensor("k", k, (B, H, N, d))
+    _check_tensor("v", v, (B, H, N, d_v), k.dtype)
+    _check_tensor("win_k", win_k, (B, H, W, d), k.dtype)
+    _check_tensor("win_v", win_v, (B, H, W, d_v), k.dtype)
+    _check(_lib.taylor_hybrid_fill_window(_ptr(k), _ptr(v), _ptr(win_k), _ptr(win_v), B, H, N, W, d, d_v,
+                                          _dtype_code(k.dtype), _stream_ptr(k.device)))
+
+
+def hybrid_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, state: torch.Tensor, win_k: torch.Tensor,
+                  win_v: torch.Tensor, pos: int, n: int, a: float, out_dtype: torch.dtype | None = None,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """One hybrid decode step at position ``pos`` (window W = win_k.shape[2])."""
+    B, H, d = q.shape
+    d_v = v.shape[-1]
+    W = win_k.shape[2]
+    _check_tensor("q", q, (B, H, d))
+    _check_tensor("k", k, (B, H, d), q.dtype)
+    _check_tensor("v", v, (B, H, d_v), q.dtype)
+    _check_tensor("state", state, (B * H * state_numel(d, d_v, n),), torch.float32)
+    _check_tensor("win_k", win_k, (B, H, W, d), q.dtype)
+    _check_tensor("win_v", win_v, (B, H, W, d_v), q.dtype)
+    out_dtype = out_dtype or torch.float32
+    if out is None:
+        out = torch.empty((B, H, d_v), dtype=out_dtype, device=q.device)
+    _check_tensor("out", out, (B, H, d_v), out_dtype)
+    _check(_lib.taylor_hybrid_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(state), _ptr(win_k), _ptr(win_v),
+                                     int(pos), W, B, H, d, d_v, n, float(a), _dtype_code(q.dtype),
+                                     _dtype_code(out_dtype), _stream_ptr(q.device)))
     return out

@@ -333,4 +333,47 @@ int taylor_attn_decode_bf16state(const void* q, const void* k, const void* v, vo
   return TAYLOR_OK;
 }
 
+int taylor_hybrid_fill_window(const void* k, const void* v, void* win_k, void* win_v, int B, int H, int N, int window,
+                              int d, int d_v, taylor_dtype in_dtype, hipStream_t stream) {
+  if (in_dtype != TAYLOR_F32 && in_dtype != TAYLOR_BF16)
+    return fail(TAYLOR_EINVAL, "taylor_hybrid_fill_window: dtype must be TAYLOR_F32 or TAYLOR_BF16");
+  if (B < 0 || H < 0 || N < 0) return fail(TAYLOR_EINVAL, "taylor_hybrid_fill_window: B, H, N must be >= 0");
+  if (d != taylor::kD || d_v != taylor::kDV)
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_hybrid_fill_window: only d = 16, d_v = 64 are built");
+  if (window < 1 || window > taylor::hybrid_max_window())
+    return fail(TAYLOR_EINVAL, "taylor_hybrid_fill_window: need 1 <= window <= " +
+                                   std::to_string(taylor::hybrid_max_window()));
+  if ((int64_t)B * H == 0 || N == 0) return TAYLOR_OK;
+  if ((int64_t)B * H > 65535) return fail(TAYLOR_EINVAL, "taylor_hybrid_fill_window: B*H out of range (<= 65535)");
+  if (!k || !v || !win_k || !win_v) return fail(TAYLOR_EINVAL, "taylor_hybrid_fill_window: NULL pointer");
+  const hipError_t e = taylor::launch_hybrid_fill_window(k, v, win_k, win_v, B * H, N, window, in_dtype == TAYLOR_BF16,
+                                                         stream);
+  if (e != hipSuccess) return hip_fail(e, "taylor_hybrid_fill_window: kernel launch");
+  return TAYLOR_OK;
+}
+
+int taylor_hybrid_decode(const void* q, const void* k, const void* v, void* o, float* state, void* win_k, void* win_v,
+                         int pos, int window, int B, int H, int d, int d_v, int n, float a, taylor_dtype in_dtype,
+                         taylor_dtype out_dtype, hipStream_t stream) {
+  if (int e = check_dtypes(in_dtype, out_dtype)) return e;
+  if (B < 0 || H < 0) return fail(TAYLOR_EINVAL, "taylor_hybrid_decode: B and H must be >= 0");
+  if (!(a > 0.0f) || a == __builtin_inff()) return fail(TAYLOR_EINVAL, "taylor_hybrid_decode: a must be finite and > 0");
+  if (d != taylor::kD || d_v != taylor::kDV || n < 1 || n > 3)
+    return fail(TAYLOR_EUNSUPPORTED, "taylor_hybrid_decode: only d = 16, d_v = 64, n <= 3 are built");
+  if (window < 1 || window > taylor::hybrid_max_window() || pos < 0)
+    return fail(TAYLOR_EINVAL, "taylor_hybrid_decode: need 1 <= window <= " +
+                                   std::to_string(taylor::hybrid_max_window()) + " and pos >= 0");
+  if ((int64_t)B * H == 0) return TAYLOR_OK;
+  if ((int64_t)B * H > (1 << 30)) return fail(TAYLOR_EINVAL, "taylor_hybrid_decode: B*H out of range");
+  if (!q || !k || !v || !o || !state || !win_k || !win_v) return fail(TAYLOR_EINVAL, "taylor_hybrid_decode: NULL pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(state) || !aligned16(win_k) ||
+      !aligned16(win_v))
+    return fail(TAYLOR_EINVAL, "taylor_hybrid_decode: buffers must be 16-byte aligned");
+  taylor::HybridDecodeArgs args{q, k, v, o, state, win_k, win_v, B * H, n, pos, window, a,
+                                in_dtype == TAYLOR_BF16, out_dtype == TAYLOR_BF16, stream};
+  const hipError_t e = taylor::launch_hybrid_decode(args);
+  if (e != hipSuccess) return hip_fail(e, "taylor_hybrid_decode: kernel launch");
+  return TAYLOR_OK;
+}
+
 }  // extern "C"

@@ -114,4 +114,19 @@ hipError_t launch_decode_bf16state(const Bf16DecodeArgs& a);
 hipError_t launch_state_to_bf16(const float* state, void* state_bf16, int BH, int D, hipStream_t stream);
 int bf16_decode_max_window();
 
+// Eviction-fed hybrid decode (taylor_hybrid.hip), d = 16, d_v = 64, n <= 3.
+struct HybridDecodeArgs {
+  const void* q; const void* k; const void* v; void* o;
+  float* state;
+  void* win_k; void* win_v;
+  int BH, n, pos, window;
+  float a;
+  bool in_bf16, out_bf16;
+  hipStream_t stream;
+};
+hipError_t launch_hybrid_decode(const HybridDecodeArgs& a);
+hipError_t launch_hybrid_fill_window(const void* k, const void* v, void* wk, void* wv, int BH, int N, int W,
+                                     bool in_bf16, hipStream_t stream);
+int hybrid_max_window();
+
 }  // namespace taylor

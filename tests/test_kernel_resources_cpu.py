@@ -18,7 +18,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SOURCES = ["taylor_decode.hip", "taylor_prefill.hip", "taylor_prefill_n3.hip", "taylor_prefill_n3_c128.hip",
-           "taylor_prefill_fb.hip", "softmax_attn.hip", "taylor_decode_bf16.hip"]
+           "taylor_prefill_fb.hip", "softmax_attn.hip", "taylor_decode_bf16.hip",
+           "taylor_hybrid.hip"]
 
 # Scalar spills allowed per kernel (mangled-name prefix -> count).  The
 # 128-token n = 3 prefill keeps 8 scalar registers in vector-register lanes
