@@ -196,46 +196,85 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const TIN* __restrict__ 
   finish<TOUT>(acc, dacc, o, bh, tid);
 }
 
-// The fold: S <- round_bf16(S + sum_{j<K} phi(k_j) v_j^T), T <- T + sum_j phi(k_j),
-// the K window tokens staged in LDS; thread (rg, cc) owns rows rg + 32i and
-// value columns 8cc..8cc+7 (float32 sums, one rounding per element).
+// The fold: S <- round_bf16(S + sum_{j<K} phi(k_j) v_j^T), T <- T + sum_j phi(k_j).
+// The S increment is the product phi(K_w)^T V_w (D x K times K x d_v) on the
+// float32 matrix cores (16x16x4): wave w accumulates the 16-row feature tiles
+// w, w + 4, w + 8 against the four 16-column tiles; the A operand (feature of
+// row 16 ft + li for token 4s + g) is formed from the staged keys as it is
+// needed.  Each element of S is rounded once.
 template <int NT, typename TIN>
 __global__ __launch_bounds__(kThreads) void fold_kernel(uint16_t* __restrict__ S, float* __restrict__ T,
                                                         const TIN* __restrict__ wk, const TIN* __restrict__ wv,
                                                         int window) {
   constexpr int D = state_width(NT);
-  constexpr int kRows = (D + kRG - 1) / kRG;
+  constexpr int NFT = (D + 15) / 16;  // 16-row feature tiles
+  constexpr int TPW = (NFT + 3) / 4;  // tiles per wave (at most)
   __shared__ float ks[kMaxWin][kD + 1];
-  __shared__ __align__(16) float vs[kMaxWin][kDV];
-  const int bh = blockIdx.x, tid = threadIdx.x, rg = tid >> 3, cc = tid & 7;
-  for (int i = tid; i < window * kD; i += kThreads)
-    ks[i / kD][i % kD] = Elem<TIN>::load(wk, (size_t)bh * window * kD + i);
-  for (int i = tid; i < window * kDV; i += kThreads)
-    vs[i / kDV][i % kDV] = Elem<TIN>::load(wv, (size_t)bh * window * kDV + i);
+  __shared__ __align__(16) float vs[kMaxWin][kDV + 4];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kpad = (window + 3) & ~3;  // whole k-steps of 4 tokens; padding tokens are zero
+  for (int i = tid; i < kpad * kD; i += kThreads) {
+    const int j = i / kD;
+    ks[j][i % kD] = j < window ? Elem<TIN>::load(wk, (size_t)bh * window * kD + i) : 0.0f;
+  }
+  for (int i = tid; i < kpad * kDV; i += kThreads) {
+    const int j = i / kDV;
+    vs[j][i % kDV] = j < window ? Elem<TIN>::load(wv, (size_t)bh * window * kDV + i) : 0.0f;
+  }
   __syncthreads();
-  uint16_t* __restrict__ Sh = S + (size_t)bh * D * kDV;
   const float4 ones = make_float4(1.f, 1.f, 1.f, 1.f);
+  // T: one row per thread (padding tokens have phi_0 = 1, so they are skipped)
+  if (tid < D) {
+    const uint32_t code = kTab.code[tid];
+    const float wt = kTab.weight[tid];
+    float tadd = 0.f;
+    for (int j = 0; j < window; ++j) tadd += feature_value(code, wt, ks[j], ones);
+    T[(size_t)bh * D + tid] += tadd;
+  }
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[TPW][4];
+  uint32_t code[TPW];
+  float wt[TPW];
 #pragma unroll
-  for (int i = 0; i < kRows; ++i) {
-    const int r = rg + kRG * i;
-    if (r >= D) break;
-    const uint32_t code = kTab.code[r];
-    const float wt = kTab.weight[r];
-    float add[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, tadd = 0.f;
-    for (int j = 0; j < window; ++j) {
-      const float f = feature_value(code, wt, ks[j], ones);
+  for (int i = 0; i < TPW; ++i) {
+    const int r = min(16 * (w + 4 * i) + li, D - 1);
+    code[i] = kTab.code[r];
+    wt[i] = 16 * (w + 4 * i) + li < D ? kTab.weight[r] : 0.0f;  // rows past D contribute nothing
 #pragma unroll
-      for (int e = 0; e < 8; ++e) add[e] += f * vs[j][8 * cc + e];
-      tadd += f;
+    for (int ct = 0; ct < 4; ++ct) acc[i][ct] = zero;
+  }
+  for (int s4 = 0; s4 < kpad; s4 += 4) {
+    const int j = s4 + g;  // token of this lane's k-slot
+    float bv[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) bv[ct] = vs[j][16 * ct + li];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      if (w + 4 * i < NFT) {  // uniform
+        const float f = feature_value(code[i], wt[i], ks[j], ones);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) acc[i][ct] = mfma_f32_k4(f, bv[ct], acc[i][ct]);
+      }
     }
-    uint4* p = reinterpret_cast<uint4*>(Sh + (size_t)r * kDV + 8 * cc);
-    const uint4 old = *p;
-    const uint32_t w4[4] = {old.x, old.y, old.z, old.w};
-    uint32_t nw[4];
+  }
+  // lane (li, g) holds rows 16 ft + 4g + r, column 16 ct + li: add and round
+  uint16_t* __restrict__ Sh = S + (size_t)bh * D * kDV;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) nw[e] = pack_bf(bf_lo(w4[e]) + add[2 * e], bf_hi(w4[e]) + add[2 * e + 1]);
-    *p = make_uint4(nw[0], nw[1], nw[2], nw[3]);
-    if (cc == 0) T[(size_t)bh * D + r] += tadd;
+  for (int i = 0; i < TPW; ++i) {
+    if (w + 4 * i >= NFT) continue;  // uniform
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * (w + 4 * i) + 4 * g + r;
+      if (row < D) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          uint16_t* p = Sh + (size_t)row * kDV + 16 * ct + li;
+          const float old = __uint_as_float((uint32_t)*p << 16);
+          *p = __builtin_bit_cast(uint16_t, f32_to_bf16(old + acc[i][ct][r]));
+        }
+      }
+    }
   }
 }
 
