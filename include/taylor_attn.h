@@ -259,8 +259,9 @@ const char* taylor_last_error(void);
  * launch, events[1] after the segment-sum kernel, events[2] after the scan
  * kernel and events[3] after the chunk kernel, all on its stream (events of
  * phases that do not run are recorded back to back; for n = 3 with bfloat16
- * inputs events[1] and events[2] both follow the small kernel that clears the
- * workspace flags, and events[3] follows the single prefill kernel).
+ * inputs events[1] follows the small kernel that clears the workspace flags,
+ * and events[2] and events[3] are recorded by the dispatch of the single
+ * prefill kernel itself, at its start and its end).
  * count == 0 turns it off.  The events stay owned by the caller. */
 int taylor_set_phase_events(hipEvent_t* events, int count);
 

@@ -61,6 +61,8 @@
 // y = x rotated by 8h and z = x rotated by 8h + 2gh, the lane's 8 features of a
 // k block are y_s z_{(s + d) mod 16} for compile-time s and d, so the query
 // features need no runtime register indexing.
+#include <hip/hip_ext.h>
+
 #include <type_traits>
 
 #include "taylor_device.h"
@@ -1183,13 +1185,17 @@ hipError_t launch(const PrefillArgs& a) {
     hipLaunchKernelGGL(clear_flags_kernel, dim3((nslots + 255) / 256), dim3(256), 0, a.stream, sync, nslots);
   }
   if (ev) {
+    // events 2 and 3 are recorded by the dispatch itself, at the kernel's
+    // start and end (no launch gap inside the interval)
     (void)hipEventRecord(ev[1], a.stream);
-    (void)hipEventRecord(ev[2], a.stream);
+    hipExtLaunchKernelGGL((prefill_n3_kernel<C, TOUT>), dim3(a.BH * pl.nseg), dim3(64 * waves_for<C>()), 0, a.stream,
+                          ev[2], ev[3], 0, q, k, v, static_cast<TOUT*>(a.o), st_S, st_T, sync, sums, a.N, pl.nseg,
+                          pl.chunks_per_seg, group_size(pl.nseg), inv_a, a.wait_limit);
+  } else {
+    hipLaunchKernelGGL((prefill_n3_kernel<C, TOUT>), dim3(a.BH * pl.nseg), dim3(64 * waves_for<C>()), 0, a.stream,
+                       q, k, v, static_cast<TOUT*>(a.o), st_S, st_T, sync, sums, a.N, pl.nseg, pl.chunks_per_seg,
+                       group_size(pl.nseg), inv_a, a.wait_limit);
   }
-  hipLaunchKernelGGL((prefill_n3_kernel<C, TOUT>), dim3(a.BH * pl.nseg), dim3(64 * waves_for<C>()), 0, a.stream, q,
-                     k, v, static_cast<TOUT*>(a.o), st_S, st_T, sync, sums, a.N, pl.nseg, pl.chunks_per_seg,
-                     group_size(pl.nseg), inv_a, a.wait_limit);
-  if (ev) (void)hipEventRecord(ev[3], a.stream);
   return hipGetLastError();
 }
 
