@@ -17,7 +17,7 @@ INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libtaylor_attn.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["taylor_abi.cpp", "taylor_decode.hip", "taylor_prefill.hip", "taylor_prefill_n3.hip",
-           "taylor_prefill_n3_c128.hip", "taylor_prefill_fb.hip",
+           "taylor_prefill_n3_c128.hip", "taylor_prefill_fb.hip", "taylor_prefill_small.hip",
            "softmax_attn.hip", "taylor_decode_bf16.hip",
            "taylor_hybrid.hip"]
 # per-source extra flags: the 64-token n = 3 prefill is scheduled for
@@ -27,7 +27,7 @@ SOURCES = ["taylor_abi.cpp", "taylor_decode.hip", "taylor_prefill.hip", "taylor_
 # accumulation registers and copies every one back with a vector instruction)
 VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 EXTRA = {"taylor_prefill_n3.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-         "taylor_prefill.hip": VGPR_MFMA, "softmax_attn.hip": VGPR_MFMA}
+         "softmax_attn.hip": VGPR_MFMA, "taylor_prefill_small.hip": VGPR_MFMA}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", CSRC, "-I", INCLUDE]

@@ -156,6 +156,10 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, fl
     return fail(TAYLOR_EINVAL, "taylor_attn_prefill: q, k, v, o and state must be 16-byte aligned");
   if ((int64_t)B * H > (1 << 24) || (int64_t)N * chunk > ((int64_t)1 << 40))
     return fail(TAYLOR_EINVAL, "taylor_attn_prefill: sizes out of range");
+  // n <= 2 at d = 16: one 512-thread workgroup per 256-token segment
+  if (d == 16 && n <= 2 &&
+      (int64_t)B * H * ((N + taylor::kSmallSegment - 1) / taylor::kSmallSegment) >= (1 << 23))
+    return fail(TAYLOR_EINVAL, "taylor_attn_prefill: sizes out of range (B*H*ceil(N/256) must be < 2^23 for n <= 2)");
   const taylor::PrefillPlan plan = taylor::plan_prefill(B * H, N, d, n, chunk);
   const size_t need = plan.workspace_floats * sizeof(float);
   if (need > 0) {

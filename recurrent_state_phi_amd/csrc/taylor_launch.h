@@ -55,6 +55,13 @@ size_t prefill_n3_workspace_floats(int BH, int nseg);
 constexpr int kN3Magic = 0x54617933;
 constexpr int kN3ErrTimeout = 1;
 
+// n = 1, 2 at d = 16 (taylor_prefill_small.hip): one launch over segments of
+// 256 tokens (16-token chunks inside, whatever the requested chunk), with a
+// look-back across segments, and the workspace it needs.
+hipError_t launch_prefill_small(const PrefillArgs& a);
+size_t prefill_small_workspace_floats(int BH, int N, int n);
+constexpr int kSmallSegment = 256;
+
 // Feature-blocked prefill, chunk 32 or 64 (taylor_prefill_fb.hip): d = 16
 // with n = 3 (one block; bfloat16 inputs with chunk 64 or 128 take the
 // single-launch n = 3 kernel instead), 4, 5, 6, and d = 32, 64 with n = 1, 2,
@@ -63,9 +70,6 @@ constexpr int kN3ErrTimeout = 1;
 hipError_t launch_prefill_fb(const PrefillArgs& a);
 int prefill_fb_blocks(int d, int n);
 size_t prefill_fb_output_floats(int BH, int N, int d, int n);
-// Whether the plan for head dimension d and order n is the feature-blocked
-// one (its workspace also covers the single-launch n = 3 kernel).
-inline bool prefill_uses_fb(int d, int n) { return d != 16 || n >= 3; }
 
 // Exclusive scan of the per-segment state sums in place, seeded with the
 // caller's state (taylor_prefill.hip).
