@@ -89,7 +89,10 @@ int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStre
  * Host only; -1 cast to size_t on
  * error.  For states of several 176-row feature blocks (d = 16 with n >= 4,
  * and n = 3 at d = 32, 64) it includes a row of d_v + 4 floats per
- * head-token per feature block. */
+ * head-token per feature block.  For n = 1, 2 at d = 16 (segments of 256
+ * tokens, so 0 for N <= 256) it is a 64-word header, one flag word per
+ * segment rounded up to 64 words, and two state images per segment of 1,108
+ * (n = 2) or 68 (n = 1) floats; `chunk` does not change it. */
 size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n, int chunk);
 
 /* Chunked prefill (section 3.5): for every head and every t in [0, N)
@@ -103,12 +106,14 @@ size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n
  *   a > 0 : temperature.
  *   chunk : d = 16, n = 1..3: 32 or 64 for TAYLOR_F32 inputs; 32, 64 or 128
  *           for TAYLOR_BF16.  d = 16 with n = 4..6, and d = 32, 64: 32 or 64
- *           for either input type.
+ *           for either input type.  At d = 16 with n = 1, 2 the value is
+ *           checked but the kernel always evaluates chunks of 16 tokens inside
+ *           segments of 256 (the outputs agree to float32 rounding).
  *   Arithmetic: float32 inputs use float32 MFMA throughout.  bfloat16 inputs
  *   use bfloat16 MFMA with float32 accumulation and a float32 state at d = 16
- *   for n = 1, 2 (any chunk) and for n = 3 with chunk 64 or 128; everywhere
- *   else (n = 3 with chunk 32, d = 16 with n = 4..6, d = 32 and 64) they are
- *   widened and computed in float32.  Those float32 paths split the state into
+ *   for n = 3 with chunk 64 or 128; everywhere else (d = 16 with n = 1, 2, n =
+ *   3 with chunk 32, d = 16 with n = 4..6, d = 32 and 64) they are widened
+ *   and computed in float32.  Those float32 paths split the state into
  *   blocks of 176 rows handled by separate workgroups (1 block for n = 3 at
  *   d = 16; 6, 28, 116 blocks for n = 4, 5, 6; 4 and 13 for n = 3 at d = 32,
  *   64); with more than one block the workspace also holds each block's share
@@ -117,10 +122,12 @@ size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n
  *   (may be NULL when that is 0); it is scratch, its contents are undefined
  *   afterwards (any contents are fine on entry).  o must not alias q, k, v or
  *   state.
- *   n = 3 with bfloat16 inputs (chunk 64 or 128) runs as one kernel in which
- *   the workgroups of a sequence's segments pass their state sums to each
- *   other through the workspace; every such wait is bounded, and
- *   taylor_prefill_check reports whether one ran out. */
+ *   n = 1, 2 at d = 16 and n = 3 with bfloat16 inputs (chunk 64 or 128) run
+ *   as one kernel in which the workgroups of a sequence's segments pass their
+ *   state sums to each other through the workspace; every such wait is
+ *   bounded, and taylor_prefill_check reports whether one ran out.  Which
+ *   sums each segment adds, and in which order, depends only on the sizes, so
+ *   repeated calls give the same bits. */
 int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, float* state,
                         int B, int H, int N, int d, int d_v, int n, float a, int chunk,
                         taylor_dtype in_dtype, taylor_dtype out_dtype,
@@ -133,8 +140,10 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, fl
  * held until the process ends; this call allocates nothing and calls no
  * allocating routine.  A plan that needs more (taylor_prefill_workspace_bytes
  * > 32 MiB: d = 16 with n >= 4, whose per-block partial outputs are large,
- * and the wide heads) returns TAYLOR_EINVAL with the size in the message and
- * launches nothing; every plan with n <= 3 at d = 16 fits.  All calls on one
+ * the wide heads, and n = 1, 2 at d = 16 beyond about 3,780 (n = 2) or
+ * 61,000 (n = 1) segments of 256 tokens over all heads) returns
+ * TAYLOR_EINVAL with the size in the message and launches nothing; every
+ * plan with n = 3 at d = 16 fits.  All calls on one
  * GPU share its array: calls that overlap in time on one GPU (other streams,
  * other threads) race and must be serialised by the caller.  Whatever a call
  * leaves in the array is cleared or overwritten by the next before it is
@@ -258,16 +267,17 @@ const char* taylor_last_error(void);
  * taylor_attn_prefill on this thread records events[0] before its first
  * launch, events[1] after the segment-sum kernel, events[2] after the scan
  * kernel and events[3] after the chunk kernel, all on its stream (events of
- * phases that do not run are recorded back to back; for n = 3 with bfloat16
- * inputs events[1] follows the small kernel that clears the workspace flags,
- * and events[2] and events[3] are recorded by the dispatch of the single
- * prefill kernel itself, at its start and its end).
+ * phases that do not run are recorded back to back).  For the single-kernel
+ * paths (n = 1, 2 at d = 16; n = 3 with bfloat16 inputs) events[1] follows
+ * the small kernel that clears the workspace flags and events[2], events[3]
+ * bracket the prefill kernel (for n = 3 they are recorded by its dispatch
+ * itself, at its start and its end).
  * count == 0 turns it off.  The events stay owned by the caller. */
 int taylor_set_phase_events(hipEvent_t* events, int count);
 
 /* Outcome of the waits between workgroups in the last taylor_attn_prefill that
- * used `workspace` (n = 3, bfloat16 inputs, more than one segment per
- * sequence).  Waits for the work queued on `stream` (the one call here that
+ * used `workspace` (n = 1, 2 at d = 16, or n = 3 with bfloat16 inputs, with
+ * more than one segment per sequence).  Waits for the work queued on `stream` (the one call here that
  * synchronises), then returns TAYLOR_OK, or TAYLOR_ETIMEOUT if a wait ran
  * out, in which case that call's outputs and state are wrong.  A workspace
  * that such a call did not use (NULL, too small, or last used by another
