@@ -61,21 +61,22 @@ def decode_algorithmic(cfg):
     return heads * (2 * state_bytes + io), heads
 
 
-def measured_traffic():
-    """HBM bytes per launch of the chunk kernel from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None
-    when the kernel source has changed since the counters were taken."""
+def measured_traffic(profile="prefill_n3_hbm_traffic.md", source="taylor_prefill_n3.hip",
+                     key="traffic_bytes_per_launch"):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration), or None when the
+    kernel source has changed since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "prefill_n3_hbm_traffic.md")
-    src = os.path.join(ROOT, "recurrent_state_phi_amd", "csrc", "taylor_prefill_n3.hip")
+    path = os.path.join(ROOT, "profiles", profile)
+    src = os.path.join(ROOT, "recurrent_state_phi_amd", "csrc", source)
     try:
         fields = dict(l.split(": ", 1) for l in open(path).read().splitlines() if ": " in l and not l.startswith(" "))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    if fields.get("kernel_source_sha256", "").strip() != sha:
+    if fields.get("kernel_source_sha256", "").strip() != sha or key not in fields:
         return None
-    return float(fields["traffic_bytes_per_launch"])
+    return float(fields[key])
 
 
 def make_prefill_inputs(torch, dev):
@@ -289,6 +290,9 @@ def order_sweep(torch, rsp, dev, reps=10):
                         "state_rows": D, "err_vs_softmax_frobenius": err,
                         "roofline": {"bound": bound, "frac": max(t_mfma, t_hbm) / (ms * 1e-3),
                                      "algorithmic_flops": flops, "algorithmic_bytes": nbytes}}
+        if n <= 2:  # the single-launch kernel's measured HBM bytes per call (rocprofv3 counters)
+            out[f"n{n}"]["roofline"]["traffic"] = measured_traffic(
+                "prefill_small_hbm_traffic.md", "taylor_prefill_small.hip", f"traffic_bytes_per_launch_n{n}")
         del ws, o, st
     return {"workload": "order sweep B=2 H=8 N=4096 d=16 d_v=64 a=1, float32 q/k/v/out, normalised Gaussian q,k "
                         "(n = 1..4 configured; n = 5, 6 added)",
@@ -710,7 +714,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the order-sweep and long-prefill lines")
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "order_sweep"], default="all")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -734,6 +738,9 @@ def main():
         return
 
     import recurrent_state_phi_amd as rsp
+    if args.only == "order_sweep":  # the order-sweep line alone (for profiling its kernels)
+        print(json.dumps({"order_sweep": order_sweep(torch, rsp, dev)}), flush=True)
+        return
     if args.only == "decode":
         eager, graph = time_decode(torch, rsp, dev, use_graph=not args.no_graph)
         print(json.dumps({"decode_us_per_token_eager": eager, "decode_us_per_token_graph": graph}), flush=True)
