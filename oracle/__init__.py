@@ -23,7 +23,9 @@ Pins (tests/test_oracle_pins.py): closed forms (n=1 running mean, t=0, equal
 keys, a -> inf), the recurrent form in both the full tensor-power basis and the
 symmetric basis, the softmax limit with a pointwise Taylor-remainder bound, the
 state widths, rank and SVD bounds of section 5.4, the memory sizes of
-section 5.8 and the signed-weight fractions of section 5.10.
+section 5.8, the signed-weight fractions of section 5.10, the error measures
+and |q.k/a| statistics on hand-computed cases, and the hybrid's two limits and
+window partition.
 """
 from __future__ import annotations
 
