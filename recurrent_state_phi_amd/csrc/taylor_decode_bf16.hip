@@ -201,18 +201,35 @@ __global__ __launch_bounds__(kThreads) void read_kernel(const TIN* __restrict__ 
 // float32 matrix cores (16x16x4): wave w accumulates the 16-row feature tiles
 // w, w + 4, w + 8 against the four 16-column tiles; the A operand (feature of
 // row 16 ft + li for token 4s + g) is formed from the staged keys as it is
-// needed.  Each element of S is rounded once.
+// needed, and the same features summed over the tokens give T's increment.
+// The head's bfloat16 rows of S are loaded as 16-byte units before anything
+// else, so they arrive while the products run; the increment goes through
+// LDS (where the window was) so that every thread adds, rounds and stores
+// whole 16-byte units.  Each element of S is rounded once.
 template <int NT, typename TIN>
 __global__ __launch_bounds__(kThreads) void fold_kernel(uint16_t* __restrict__ S, float* __restrict__ T,
                                                         const TIN* __restrict__ wk, const TIN* __restrict__ wv,
                                                         int window) {
   constexpr int D = state_width(NT);
-  constexpr int NFT = (D + 15) / 16;  // 16-row feature tiles
-  constexpr int TPW = (NFT + 3) / 4;  // tiles per wave (at most)
-  __shared__ float ks[kMaxWin][kD + 1];
-  __shared__ __align__(16) float vs[kMaxWin][kDV + 4];
+  constexpr int NFT = (D + 15) / 16;                     // 16-row feature tiles
+  constexpr int TPW = (NFT + 3) / 4;                     // tiles per wave (at most)
+  constexpr int NU = (D * 8 + kThreads - 1) / kThreads;  // 16-byte units of S per thread
+  constexpr int kIS = kDV + 4;                           // row stride of the staged increment
+  constexpr int kLds = kMaxWin * (kD + 1) + kMaxWin * (kDV + 4);
+  static_assert(D * kIS <= kLds, "the increment fits where the window was staged");
+  __shared__ __align__(16) float lds[kLds];
+  float(*ks)[kD + 1] = reinterpret_cast<float(*)[kD + 1]>(lds);
+  float(*vs)[kDV + 4] = reinterpret_cast<float(*)[kDV + 4]>(lds + kMaxWin * (kD + 1));
+  float* inc = lds;  // [D][kIS], after the products
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, li = lane & 15, g = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* __restrict__ Sh = S + (size_t)bh * D * kDV;
+  uint4 sv[NU];  // units tid, tid + kThreads, ... of the head's S (8 bfloat16 each)
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int e = tid + kThreads * u;
+    sv[u] = e < D * 8 ? *reinterpret_cast<const uint4*>(Sh + (size_t)e * 8) : make_uint4(0u, 0u, 0u, 0u);
+  }
   const int kpad = (window + 3) & ~3;  // whole k-steps of 4 tokens; padding tokens are zero
   for (int i = tid; i < kpad * kD; i += kThreads) {
     const int j = i / kD;
@@ -224,16 +241,9 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(uint16_t* __restrict__ S
   }
   __syncthreads();
   const float4 ones = make_float4(1.f, 1.f, 1.f, 1.f);
-  // T: one row per thread (padding tokens have phi_0 = 1, so they are skipped)
-  if (tid < D) {
-    const uint32_t code = kTab.code[tid];
-    const float wt = kTab.weight[tid];
-    float tadd = 0.f;
-    for (int j = 0; j < window; ++j) tadd += feature_value(code, wt, ks[j], ones);
-    T[(size_t)bh * D + tid] += tadd;
-  }
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[TPW][4];
+  float tsum[TPW];
   uint32_t code[TPW];
   float wt[TPW];
 #pragma unroll
@@ -241,6 +251,7 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(uint16_t* __restrict__ S
     const int r = min(16 * (w + 4 * i) + li, D - 1);
     code[i] = kTab.code[r];
     wt[i] = 16 * (w + 4 * i) + li < D ? kTab.weight[r] : 0.0f;  // rows past D contribute nothing
+    tsum[i] = 0.0f;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) acc[i][ct] = zero;
   }
@@ -253,13 +264,23 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(uint16_t* __restrict__ S
     for (int i = 0; i < TPW; ++i) {
       if (w + 4 * i < NFT) {  // uniform
         const float f = feature_value(code[i], wt[i], ks[j], ones);
+        tsum[i] += j < window ? f : 0.0f;  // padding tokens have phi_0 = 1: not counted in T
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) acc[i][ct] = mfma_f32_k4(f, bv[ct], acc[i][ct]);
       }
     }
   }
-  // lane (li, g) holds rows 16 ft + 4g + r, column 16 ct + li: add and round
-  uint16_t* __restrict__ Sh = S + (size_t)bh * D * kDV;
+  // T of row 16 ft + li: the lane's tokens, then the other lane groups' (xor 16, 32)
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    float ts = tsum[i];
+    ts += __shfl_xor(ts, 16);
+    ts += __shfl_xor(ts, 32);
+    const int row = 16 * (w + 4 * i) + li;
+    if (w + 4 * i < NFT && g == 0 && row < D) T[(size_t)bh * D + row] += ts;
+  }
+  __syncthreads();  // every wave is done with the staged window
+  // lane (li, g) holds rows 16 ft + 4g + r, column 16 ct + li of the increment
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     if (w + 4 * i >= NFT) continue;  // uniform
@@ -268,12 +289,24 @@ __global__ __launch_bounds__(kThreads) void fold_kernel(uint16_t* __restrict__ S
       const int row = 16 * (w + 4 * i) + 4 * g + r;
       if (row < D) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          uint16_t* p = Sh + (size_t)row * kDV + 16 * ct + li;
-          const float old = __uint_as_float((uint32_t)*p << 16);
-          *p = __builtin_bit_cast(uint16_t, f32_to_bf16(old + acc[i][ct][r]));
-        }
+        for (int ct = 0; ct < 4; ++ct) inc[row * kIS + 16 * ct + li] = acc[i][ct][r];
       }
+    }
+  }
+  __syncthreads();
+  // add and round, 8 values (one 16-byte unit) at a time
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int e = tid + kThreads * u;
+    if (e < D * 8) {
+      const float* x = inc + (e >> 3) * kIS + (e & 7) * 8;
+      const float4 a0 = *reinterpret_cast<const float4*>(x), a1 = *reinterpret_cast<const float4*>(x + 4);
+      uint4 o;
+      o.x = pack_bf(bf_lo(sv[u].x) + a0.x, bf_hi(sv[u].x) + a0.y);
+      o.y = pack_bf(bf_lo(sv[u].y) + a0.z, bf_hi(sv[u].y) + a0.w);
+      o.z = pack_bf(bf_lo(sv[u].z) + a1.x, bf_hi(sv[u].z) + a1.y);
+      o.w = pack_bf(bf_lo(sv[u].w) + a1.z, bf_hi(sv[u].w) + a1.w);
+      *reinterpret_cast<uint4*>(Sh + (size_t)e * 8) = o;
     }
   }
 }
