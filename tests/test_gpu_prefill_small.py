@@ -194,3 +194,55 @@ def test_wait_timeout_is_reported(rsp):
     rsp.prefill_check(ws)
     got = o.cpu().numpy().astype(np.float64)
     assert oracle.rel_err_rowwise(got, oracle.taylor_direct(q, k, v, n, 1.0)) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_many_heads_several_rounds(rsp, dtype):
+    """B=16, H=8, N=4096, n = 2: 2,048 segment workgroups, several rounds of them on
+    the GPU (later rounds find their predecessors long done); sampled rows of every
+    head and the final state of a few heads against the oracle."""
+    say("n<=2 many heads", dtype)
+    B, H, N, n = 16, 8, 4096, 2
+    q, k, v = TI.make_qkv(760, B, H, N, 16, 64, dtype=dtype)
+    st = rsp.new_state(B, H, n, device=DEV)
+    o = rsp.prefill(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), st, n, 1.0, chunk=64, check=True)
+    got = o.float().cpu().numpy().astype(np.float64).reshape(-1, 64)
+    rows = edge_rows(N, 8, B * H, 6)
+    ref = oracle.taylor_direct(q, k, v, n, 1.0, rows=rows)
+    assert oracle.rel_err_rowwise(got[rows], ref) <= TOL[dtype]
+    S, T = (x.cpu().numpy().astype(np.float64) for x in rsp.state_views(st, B, H, n))
+    for b, h in ((0, 0), (7, 3), (15, 7)):
+        A = state_of(k[b, h], v[b, h], n)
+        assert np.abs(S[b, h] - A[:, :64]).max() <= 1e-5 * np.abs(A[:, :64]).max()
+        assert np.abs(T[b, h] - A[:, 64]).max() <= 1e-5 * np.abs(A[:, 64]).max()
+
+
+def test_more_than_4096_segments(rsp):
+    """One head of 1,152,001 tokens, n = 1: 4,501 segments in groups of 68, so both
+    parts of the look-back (67 earlier members, 66 earlier groups) wait on more than
+    64 flags and poll in two reads; sampled rows (segment starts and ends, the chunks
+    around the first group edges, the last segments) and the final state against the
+    oracle."""
+    say("n<=2 4,501 segments")
+    B, H, N, n = 1, 1, 256 * 4500 + 1, 1
+    q, k, v = TI.make_qkv(770, B, H, N, 16, 64)
+    st = rsp.new_state(B, H, n, device=DEV)
+    o = rsp.prefill(to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32"), st, n, 1.0, chunk=64, check=True)
+    got = o.cpu().numpy().astype(np.float64).reshape(-1, 64)
+    G, nseg = 68, (N + SEG - 1) // SEG
+    # first and last token of every segment of the first three groups, of every 40th
+    # segment, and of the last two; the chunks on both sides of the first group edges
+    segs = set(range(3 * G)) | set(range(0, nseg, 40)) | {nseg - 2, nseg - 1}
+    pos = {N - 1}
+    for s in segs:
+        pos |= {s * SEG, min(N - 1, s * SEG + SEG - 1)}
+    for grp in range(3):
+        edge = (grp + 1) * G * SEG
+        pos |= set(range(edge - SEG, min(N, edge + SEG), 16))
+    rows = np.asarray(sorted(pos), np.int64)
+    ref = oracle.taylor_direct(q, k, v, n, 1.0, rows=rows)
+    assert oracle.rel_err_rowwise(got[rows], ref) <= TOL["f32"]
+    S, T = (x.cpu().numpy().astype(np.float64) for x in rsp.state_views(st, B, H, n))
+    assert T[0, 0, 0] == N
+    vs = v[0, 0].astype(np.float64).sum(0)
+    assert np.abs(S[0, 0, 0] - vs).max() <= 1e-5 * np.abs(vs).max() + 1e-3
