@@ -19,9 +19,13 @@
 //  3. replay: it runs the segment again from its prefix, producing the outputs
 //     (Eq. (5)), and the last segment writes the final state.
 //
-// Workgroups take their segment from an atomic ticket counter, and a workgroup
-// only ever waits for segments with a smaller number, which hold smaller
-// tickets: they started before it, are running (or done), and every wait ends.
+// Workgroup b serves sequence b / nseg and takes its segment from that
+// sequence's atomic ticket counter; a workgroup only ever waits for earlier
+// segments of its own sequence, which hold smaller tickets of the same counter:
+// they started before it, are running (or done), and every wait ends.  (One
+// counter per sequence: a single counter for the whole grid serialises its
+// atomics, about 12 ns each, so the last of 512 workgroups would start 6 us
+// late.)
 // Each wait is bounded all the same; a wait that runs out records an error
 // code in the workspace.  The replay reads the segment's q, k, v shortly after
 // step 1 read k and v, mostly from cache.
@@ -78,7 +82,7 @@ constexpr int kQS = 36;    // row stride (bf16) of the doubled q copy
 constexpr int kKTRows = 16;
 
 // Workspace of a multi-segment call (32-bit words):
-//   [0]                    ticket counter
+//   [0]                    unused (zero)
 //   [1]                    error code (kN3ErrTimeout: a wait ran out)
 //   [2]                    kN3Magic (the flags below belong to this kernel)
 //   [kHdr + kFlagStride * (b * nseg + s)]  flag of segment s of sequence b:
@@ -86,7 +90,9 @@ constexpr int kKTRows = 16;
 //                          256 bytes: polls of different flags do not queue
 //                          on the same memory line); the last segment never
 //                          publishes, and its slot counts the segments that
-//                          have finished reading the caller's state
+//                          have finished reading the caller's state;
+//                          word kTicketWord of segment 0's slot is the
+//                          sequence's ticket counter
 //   then BH*nseg state images: the segment sums (group sums at the last
 //   member of a group)
 // The header (counter, error, flags) is cleared by a small kernel before every
@@ -95,6 +101,7 @@ constexpr int kKTRows = 16;
 // lane-major, 16 bytes per lane) and 384 floats of T'.
 constexpr int kHdr = 64;
 constexpr int kFlagStride = 64;
+constexpr int kTicketWord = 32;  // in the second 128-byte half of the slot, away from the flag word
 constexpr int kImgS = 40 * 64 * 4;       // 40 owned (slot, column tile) pairs per workgroup
 constexpr int kImgFloats = kImgS + 384;  // + T': waves x 3 slots x 4 lane groups x 4 rows (8 waves)
 
@@ -238,6 +245,46 @@ struct Own {
 constexpr int kSC1 = 16;                    // buffer cache policy: device scope
 constexpr int kBufWord3 = 0x00020000;       // buffer descriptor word 3 (gfx9: 32-bit data, raw)
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+// Loads of the rows of one segment of q, k and v (row r: token t_begin + r of
+// sequence bh) through buffer descriptors that span the rows r0 .. r0 + span - 1
+// of one call: a row at or past the segment's end reads as zeros (the
+// descriptor's range check), which makes the padding of a partial chunk, and a
+// chunk past the last one, zero without clamping or masking.  The descriptors
+// are rebuilt per call in scalar registers (r0 is wave-uniform), so the offsets
+// stay small whatever the sequence length.
+struct SegRows {
+  const uint16_t *q, *k, *v;
+  size_t row0;
+  int n;
+  __device__ __forceinline__ SegRows(const uint16_t* q_, const uint16_t* k_, const uint16_t* v_, int bh, int N,
+                                     int t_begin, int t_end)
+      : q(q_), k(k_), v(v_), row0((size_t)bh * N + t_begin), n(t_end - t_begin) {}
+  // Lane (li, g) loads row r0 + lr (lr < span): v columns 8g..8g+7 into d[0]
+  // and 32+8g..+7 into d[1], and dimensions 8(g%2)..+7 of k into d[2], or of q
+  // for lanes g >= 2 when WITH_Q.
+  template <bool WITH_Q>
+  __device__ __forceinline__ void load(uint4* d, int r0, int span, int lr, int g) const {
+    // (read back from lane 0: the clamps compile to vector instructions, and a
+    // descriptor in vector registers would need a loop over distinct values)
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(span, n - r0)));
+    const size_t base = row0 + (size_t)__builtin_amdgcn_readfirstlane(max(0, min(r0, n)));
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v + base * kDV), 0, rows * kDV * 2, kBufWord3);
+    d[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lr * kDV * 2 + 16 * g, 0, 0));
+    d[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lr * kDV * 2 + 64 + 16 * g, 0, 0));
+    const int ko = lr * kD * 2 + 16 * (g & 1);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + base * kD), 0, rows * kD * 2, kBufWord3);
+    if (WITH_Q && g >= 2) {
+      const __amdgpu_buffer_rsrc_t rq =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(q + base * kD), 0, rows * kD * 2, kBufWord3);
+      d[2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, ko, 0, 0));
+    } else {
+      d[2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, ko, 0, 0));
+    }
+  }
+};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t image_rsrc(const float* img) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(img), 0, kImgFloats * 4, kBufWord3);
@@ -450,7 +497,7 @@ template <int C, int NW_, typename TOUT>
 __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc& a, const uint16_t* __restrict__ q,
                                              const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                              TOUT* __restrict__ o, int bh, int N, int t_begin, int t_end,
-                                             float inv_a) {
+                                             float inv_a, bool keep_state) {
   using Sh = Shape<C, NW_>;
   constexpr int NKB = Sh::NKB, NW = Sh::NW, NCT2 = Sh::NCT2;
   constexpr bool HAS_S1 = Sh::HAS_S1;
@@ -468,26 +515,19 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
   //      the tile, and k (g < 2) or q (g >= 2) dimensions 8(g%2)..+7: the
   //      natural row-major 16-byte pieces, which are exactly the A operand of
   //      the transposing MFMAs in `stage`.  Chunk c is loaded into register set
-  //      c % DEPTH, DEPTH chunks ahead of its use.  Every load is issued
-  //      unconditionally (token index clamped into the segment; the values of
-  //      padding tokens are zeroed when staged), so the number of loads in
-  //      flight is the same on every path and the waits for them are exact.
+  //      c % DEPTH, DEPTH chunks ahead of its use.  The loads are buffer loads
+  //      over the segment's rows: a token past the segment's end (the padding
+  //      of a partial chunk, or a chunk past the last) reads zeros, so padding
+  //      tokens need no clamping or masking, and every load is issued
+  //      unconditionally, so the waits for them are exact.
   constexpr int TPW = Sh::TPW;
   constexpr int NPF = 3 * TPW;
   constexpr int DEPTH = 2;  // register sets of prefetched loads
   uint4 pf[DEPTH][NPF];
+  const SegRows rows(q, k, v, bh, N, t_begin, t_end);
   auto issue_loads = [&](uint4 (&pfs)[NPF], int chunk) {
-    const int c0 = t_begin + min(chunk, nchunks - 1) * C;
-    const int last = min(C, t_end - c0) - 1;
-    const size_t base = (size_t)bh * N + c0;
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const size_t tok = base + min(16 * (w + NW * i) + li, last);
-      pfs[3 * i] = *reinterpret_cast<const uint4*>(v + tok * kDV + 8 * g);
-      pfs[3 * i + 1] = *reinterpret_cast<const uint4*>(v + tok * kDV + 32 + 8 * g);
-      const uint16_t* kq = g >= 2 ? q + tok * kD + 8 * (g - 2) : k + tok * kD + 8 * (g & 1);
-      pfs[3 * i + 2] = *reinterpret_cast<const uint4*>(kq);
-    }
+    for (int i = 0; i < TPW; ++i) rows.load<true>(pfs + 3 * i, chunk * C, C, 16 * (w + NW * i) + li, g);
   };
   // One-hot B operands: sel0 picks k-slots 0..15 and sel1 k-slots 16..31 of a
   // 16x16x32 product, so that A . sel = the A rows transposed into the
@@ -505,16 +545,16 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
     sel0 = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
     sel1 = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
   }
-  auto stage = [&](const uint4 (&pfs)[NPF], int b, int nv) {
+  // (padding tokens arrive as zeros; the q pieces of lanes g >= 2 sit in
+  // k-slots 16..31 of the k operand, which sel0 does not pick)
+  auto stage = [&](const uint4 (&pfs)[NPF], int b) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
       const int tt = w + NW * i;
-      const bool valid = 16 * tt + li < nv;  // row li of the A operands
-      const uint4 z4 = make_uint4(0, 0, 0, 0);
-      const bf16x8 v0 = __builtin_bit_cast(bf16x8, valid ? pfs[3 * i] : z4);
-      const bf16x8 v1 = __builtin_bit_cast(bf16x8, valid ? pfs[3 * i + 1] : z4);
-      const bf16x8 ka = __builtin_bit_cast(bf16x8, (valid && g < 2) ? pfs[3 * i + 2] : z4);
+      const bf16x8 v0 = __builtin_bit_cast(bf16x8, pfs[3 * i]);
+      const bf16x8 v1 = __builtin_bit_cast(bf16x8, pfs[3 * i + 1]);
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, pfs[3 * i + 2]);
       // V^T: four 16x16 tiles, lane (li, g) gets tokens 16tt + 4g + r of column 16ct + li
       const f32x4 d0 = mfma_bf16_k32(v0, sel0, zero);
       const f32x4 d1 = mfma_bf16_k32(v0, sel1, zero);
@@ -533,7 +573,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
       if (g >= 2) {
         // q / a, rounded to bfloat16 (exact for a = 1): then q.k comes out
         // already divided by a, and the query features need no scaling
-        const uint4 raw = valid ? pfs[3 * i + 2] : z4;
+        const uint4 raw = pfs[3 * i + 2];
         const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
         uint32_t sc[4];
 #pragma unroll
@@ -577,7 +617,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
   // when the loop starts, and body(j) refills the set it stages from with
   // chunk j + 1 + DEPTH
   issue_loads(pf[0], 0);
-  stage(pf[0], 0, min(C, t_end - t_begin));
+  stage(pf[0], 0);
 #pragma unroll
   for (int c = 1; c <= DEPTH; ++c) issue_loads(pf[c % DEPTH], c);
   publish(0);
@@ -596,7 +636,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
       for (int tw = 0; tw < TPW; ++tw) {
         // o = Y[:d_v] / Y[d_v]: the normaliser of token li sits in rows 0 and 1
         // of column tile 4 (lanes 0..15); every lane takes part in the shuffle
-        const float inv = 1.0f / __shfl(yo[tw][4][0] + yo[tw][4][1], li);
+        const float inv = __builtin_amdgcn_rcpf(__shfl(yo[tw][4][0] + yo[tw][4][1], li));  // within 1 ulp
         const int tok = 16 * (w + NW * tw) + li;
         if (tok < prev_nv) {
           TOUT* orow = o + ((size_t)bh * N + prev_t0 + tok) * kDV + 4 * g;
@@ -622,7 +662,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
     const int b = j & 1;
     const int t0 = t_begin + j * C;
     const int nv = min(C, t_end - t0);
-    if (j + 1 < nchunks) stage(pfs, b ^ 1, min(C, t_end - (t0 + C)));
+    if (j + 1 < nchunks) stage(pfs, b ^ 1);
     issue_loads(pfs, j + 1 + DEPTH);
     store_prev();
 
@@ -637,7 +677,8 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
     //      every product with x, and every product with v, vanishes for them;
     //      the constant feature is 1 for every token of the chunk, and its T'
     //      entry is corrected by the number of padding tokens.
-    {
+    //      The last chunk's update only matters for the final state (keep_state).
+    if (j + 1 < nchunks || keep_state) {  // uniform
       const uint32_t one2 = li == 0 ? 0x3F803F80u : 0u;
       const bf16x8 ones = __builtin_bit_cast(bf16x8, make_uint4(one2, one2, one2, one2));
       const bf16x8 zeros = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, 0u, 0u));
@@ -678,13 +719,15 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
             } else if (s == 1) {
               f[e] = xi[e] * from_lane_plus<4>(xa[e]);    // tile w + 4: x_li x_(li+w+4)
             } else {
-              // tile 8: x_li x_(li+8) (li < 8), the constant (li == 8), zero rows;
-              // tile 9: x_li.  (A select, not a branch: the DPP rotation reads
-              // its source from the other lanes, which must all be executing,
-              // and straight-line code schedules better.)
-              const float f8 = fmaf(xi[e] * from_lane_plus<8>(xi[e]), pair_m, const_m);
-              f[e] = tile8 ? f8 : xi[e];
+              f[e] = xi[e];  // tile 9: x_li (tile 8 below)
             }
+          }
+          // tile 8: x_li x_(li+8) (li < 8), the constant (li == 8), zero rows.
+          // The branch is wave-uniform, so every lane runs the DPP rotation,
+          // which reads its source from the other lanes of the row.
+          if (s == 2 && tile8) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = fmaf(xi[e] * from_lane_plus<8>(xi[e]), pair_m, const_m);
           }
           const bf16x8 aphi = __builtin_bit_cast(
               bf16x8, make_uint4(pack2(f[0], f[1]), pack2(f[2], f[3]), pack2(f[4], f[5]), pack2(f[6], f[7])));
@@ -718,24 +761,33 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
 
       // ---- diagonal block: P = tril(p_3(K Q^T / a)), lane holds P[token li][keys]
       const bf16x4 bq = __builtin_bit_cast(bf16x4, *reinterpret_cast<const uint2*>(&L.Q[b][tok][4 * g]));
-      // Every key tile of the chunk, without branches (the products are
-      // cheap, and straight-line code lets the key reads, the products and
-      // the polynomial of different key tiles overlap); tiles after the
-      // token tile are masked to zero, the diagonal tile causally (key
+      // Scores of every key tile first (straight-line: the key reads and the
+      // products of different tiles overlap), then the polynomial only for
+      // the key tiles up to the token tile (wave-uniform branches); later
+      // tiles are zero, and only the diagonal tile is masked causally (key
       // 16 kt + 4g + r against token 16 tt + li).
-      bf16x8 pb[NKB];
+      f32x4 sc[2 * NKB];
 #pragma unroll
       for (int kt = 0; kt < 2 * NKB; ++kt) {
         const int key0 = 16 * kt + li;
-        const bf16x4 ak = {f32_to_bf16(L.K[b][4 * g][key0]), f32_to_bf16(L.K[b][4 * g + 1][key0]),
-                           f32_to_bf16(L.K[b][4 * g + 2][key0]), f32_to_bf16(L.K[b][4 * g + 3][key0])};
-        const f32x4 s = mfma_bf16_k16(ak, bq, f32x4{0.f, 0.f, 0.f, 0.f});
+        const uint2 ak = make_uint2(pack2(L.K[b][4 * g][key0], L.K[b][4 * g + 1][key0]),
+                                    pack2(L.K[b][4 * g + 2][key0], L.K[b][4 * g + 3][key0]));
+        sc[kt] = mfma_bf16_k16(__builtin_bit_cast(bf16x4, ak), bq, f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+      bf16x8 pb[NKB];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fmaf(s[r], fmaf(0.5f, s[r], 1.0f), 1.0f);  // s = q.k / a
-          const bool keep = kt < tt || (kt == tt && 4 * g + r <= li);
-          pb[kt >> 1][4 * (kt & 1) + r] = f32_to_bf16(keep ? p : 0.0f);
+      for (int kt = 0; kt < 2 * NKB; ++kt) {
+        float p[4] = {0.f, 0.f, 0.f, 0.f};
+        if (kt <= tt) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[r] = fmaf(sc[kt][r], fmaf(0.5f, sc[kt][r], 1.0f), 1.0f);  // s = q.k / a
+          if (kt == tt) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = 4 * g + r <= li ? p[r] : 0.0f;
+          }
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pb[kt >> 1][4 * (kt & 1) + r] = f32_to_bf16(p[r]);
       }
 
       f32x4 y[5];
@@ -865,17 +917,12 @@ __device__ __forceinline__ void segment_sum_regs(unsigned char* lds_raw, const O
     for (int ct = 0; ct < 4; ++ct) F[f][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // loads of group G: per 16-token tile, v columns 8g..+7 and 32+8g..+7 and
-  // (lanes g < 2) k dimensions 8g..+7 of token li; clamped into the segment
+  // (lanes g < 2) k dimensions 8g..+7 of token li; tokens past the segment's
+  // end (and a group past the last) read as zeros
+  const SegRows rows(nullptr, k, v, bh, N, t_begin, t_end);
   auto issue = [&](uint4 (&r)[6], int G) {
-    const int base = t_begin + 32 * min(G, ngroups - 1);
-    const int last = t_end - 1;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const size_t tok = (size_t)bh * N + min(base + 16 * x + li, last);
-      r[3 * x] = *reinterpret_cast<const uint4*>(v + tok * kDV + 8 * g);
-      r[3 * x + 1] = *reinterpret_cast<const uint4*>(v + tok * kDV + 32 + 8 * g);
-      r[3 * x + 2] = *reinterpret_cast<const uint4*>(k + tok * kD + 8 * (g & 1));
-    }
+    for (int x = 0; x < 2; ++x) rows.load<false>(r + 3 * x, 32 * G, 32, 16 * x + li, g);
   };
   bf16x8 sel0, sel1;
   {
@@ -897,15 +944,15 @@ __device__ __forceinline__ void segment_sum_regs(unsigned char* lds_raw, const O
   auto group = [&](uint4 (&r)[6], int G, auto&& refill) {
     const int nvalid = min(32, t_end - (t_begin + 32 * G));
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-    const uint4 z4 = make_uint4(0, 0, 0, 0);
     uint32_t vw[4][4];  // B operands of the 4 column tiles, built in place
     float xi[8];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      const bool valid = 16 * x + li < nvalid;  // row li of the A operands
-      const bf16x8 v0 = __builtin_bit_cast(bf16x8, valid ? r[3 * x] : z4);
-      const bf16x8 v1 = __builtin_bit_cast(bf16x8, valid ? r[3 * x + 1] : z4);
-      const bf16x8 ka = __builtin_bit_cast(bf16x8, (valid && g < 2) ? r[3 * x + 2] : z4);
+      // (padding tokens arrive as zeros; the copies of k in lanes g >= 2 sit
+      // in k-slots 16..31, which sel0 does not pick)
+      const bf16x8 v0 = __builtin_bit_cast(bf16x8, r[3 * x]);
+      const bf16x8 v1 = __builtin_bit_cast(bf16x8, r[3 * x + 1]);
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, r[3 * x + 2]);
       const f32x4 d0 = mfma_bf16_k32(v0, sel0, zero), d1 = mfma_bf16_k32(v0, sel1, zero);
       const f32x4 d2 = mfma_bf16_k32(v1, sel0, zero), d3 = mfma_bf16_k32(v1, sel1, zero);
       const f32x4 dv[4] = {d0, d1, d2, d3};
@@ -1043,7 +1090,10 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
 
   int ticket = blockIdx.x;
   if (sync != nullptr) {  // uniform
-    if (tid == 0) s_ticket = __hip_atomic_fetch_add(&sync[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int b = blockIdx.x / nseg;  // the sequence; the counter gives the segment
+    if (tid == 0)
+      s_ticket = b * nseg + __hip_atomic_fetch_add(&sync[kHdr + (size_t)b * nseg * kFlagStride + kTicketWord], 1,
+                                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     ticket = __builtin_amdgcn_readfirstlane(s_ticket);
   }
@@ -1135,7 +1185,8 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
     }
   }
   // 3. replay from the prefix
-  segment_pass<C, NW, TOUT>(*reinterpret_cast<LB*>(lds_raw), own, pre, q, k, v, o, bh, N, t_begin, t_end, inv_a);
+  segment_pass<C, NW, TOUT>(*reinterpret_cast<LB*>(lds_raw), own, pre, q, k, v, o, bh, N, t_begin, t_end, inv_a,
+                            seg == nseg - 1);
   if (seg == nseg - 1) {  // uniform
     // the wait's operands come back from LDS (stored at the start), so that
     // none of them occupies a register during the replay
@@ -1149,11 +1200,14 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
   }
 }
 
-// Clears the ticket counter, the error code and the nslots flags, and marks
-// the header as this kernel's.
+// Clears the error code and the nslots flag slots (flag and ticket words), and
+// marks the header as this kernel's.
 static __global__ void clear_flags_kernel(int* sync, int nslots) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < nslots) sync[kHdr + (size_t)i * kFlagStride] = 0;
+  if (i < nslots) {
+    sync[kHdr + (size_t)i * kFlagStride] = 0;
+    sync[kHdr + (size_t)i * kFlagStride + kTicketWord] = 0;
+  }
   if (i < 3) sync[i] = i == 2 ? kN3Magic : 0;
 }
 

@@ -40,8 +40,10 @@
 // segment writes only after it has seen the flag of every earlier segment of
 // its group and of every earlier group's last member, each of which had seen
 // its own group's flags.
-// Workgroups take their segment from a ticket counter, so a workgroup only
-// waits for segments that started before it.  Waits are bounded; one that runs
+// Workgroup b serves sequence b / nseg and takes its segment from that
+// sequence's ticket counter (the flag word of its last segment, which never
+// carries a flag), so a workgroup only waits for segments that started before
+// it.  Waits are bounded; one that runs
 // out records an error code in the workspace header.  Images cross XCDs
 // through buffer accesses with the device-scope cache policy (sc1); a flag goes
 // up only after every wave has waited for its image stores and the waves have
@@ -59,7 +61,7 @@ constexpr int kThreads = 64 * kWaves;  // threads per workgroup
 constexpr int kL = 32 * kWaves;        // tokens per segment (2 chunks of 16 per wave)
 constexpr int kQS = 20;   // LDS row stride (floats) of q and k
 constexpr int kVS = 68;   // LDS row stride (floats) of v
-constexpr int kHdr = 64;  // header words: [0] ticket, [1] error code, [2] kN3Magic
+constexpr int kHdr = 64;  // header words: [0] unused, [1] error code, [2] kN3Magic
 constexpr int kSC1 = 16;  // buffer cache policy: device scope
 constexpr int kBufWord3 = 0x00020000;
 
@@ -158,7 +160,10 @@ __global__ __launch_bounds__(kThreads) void prefill_small_kernel(const TIN* __re
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int ticket = blockIdx.x;
   if (sync != nullptr) {  // uniform
-    if (tid == 0) s_ticket = __hip_atomic_fetch_add(&sync[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int b = blockIdx.x / nseg;  // the sequence; the counter gives the segment
+    if (tid == 0)
+      s_ticket = b * nseg + __hip_atomic_fetch_add(&sync[kHdr + (size_t)b * nseg + nseg - 1], 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     ticket = __builtin_amdgcn_readfirstlane(s_ticket);
   }
@@ -552,8 +557,9 @@ __global__ __launch_bounds__(kThreads) void prefill_small_kernel(const TIN* __re
   }
 }
 
-// Zeroes the ticket, the error code and every flag, and sets the header's
-// magic word (which tells taylor_prefill_check that the error word is live).
+// Zeroes the error code and every flag word (the ticket counters among them),
+// and sets the header's magic word (which tells taylor_prefill_check that the
+// error word is live).
 static __global__ void clear_kernel(int* sync, int nslots) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < nslots) sync[kHdr + i] = 0;

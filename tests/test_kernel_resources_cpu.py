@@ -144,13 +144,27 @@ def n3_asm(tmp_path_factory):
 
 @pytest.mark.parametrize("src", list(HANDOVER_UNITS))
 def test_n3_image_accesses_are_device_scope(n3_asm, src):
+    """Every state-image access carries the device-scope bit (sc1).  The n = 1, 2
+    kernel makes no other buffer accesses, so there every one must carry it.  The
+    n = 3 kernels also load their input rows (q, k, v) with buffer loads, which
+    need no such bit: those units have no plain buffer stores (inputs are never
+    written), their plain buffer loads are 16-byte row pieces, and the image loads
+    of the prefix step (tens per instance) all carry sc1."""
     fns = n3_asm[src]
     assert len(fns) == HANDOVER_UNITS[src][1], f"expected {HANDOVER_UNITS[src][1]} kernel instances in {src}, got {list(fns)}"
     for name, ins in fns.items():
         buf = [i for i in ins if i.startswith("buffer_load") or i.startswith("buffer_store")]
         assert any(i.startswith("buffer_store") for i in buf) and any(i.startswith("buffer_load") for i in buf), name
         missing = [i for i in buf if not re.search(r"\bsc1\b", i)]
-        assert not missing, f"{name}: image accesses without the device-scope bit: {missing[:4]}"
+        if src in N3_UNITS:
+            stores = [i for i in missing if i.startswith("buffer_store")]
+            assert not stores, f"{name}: image stores without the device-scope bit: {stores[:4]}"
+            odd = [i for i in missing if not i.startswith("buffer_load_dwordx4 ")]
+            assert not odd, f"{name}: plain buffer loads other than 16-byte input pieces: {odd[:4]}"
+            scoped = [i for i in buf if i.startswith("buffer_load") and re.search(r"\bsc1\b", i)]
+            assert len(scoped) >= 24, f"{name}: only {len(scoped)} device-scope image loads"
+        else:
+            assert not missing, f"{name}: image accesses without the device-scope bit: {missing[:4]}"
         # flag polls are device-scope loads of the header
         polls = [i for i in ins if i.startswith("global_load_dword ") and re.search(r"\bsc1\b", i)]
         assert polls, f"{name}: no device-scope flag poll found"
