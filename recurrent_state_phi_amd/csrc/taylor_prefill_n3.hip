@@ -261,8 +261,12 @@ struct SegRows {
                                      int t_begin, int t_end)
       : q(q_), k(k_), v(v_), row0((size_t)bh * N + t_begin), n(t_end - t_begin) {}
   // Lane (li, g) loads row r0 + lr (lr < span): v columns 8g..8g+7 into d[0]
-  // and 32+8g..+7 into d[1], and dimensions 8(g%2)..+7 of k into d[2], or of q
-  // for lanes g >= 2 when WITH_Q.
+  // and 32+8g..+7 into d[1], and into d[2] dimensions 8g..+7 of k for lanes
+  // g < 2, and for lanes g >= 2 dimensions 8(g-2)..+7 of q when WITH_Q, else
+  // zeros (an offset past the range: no memory traffic).  The k operand's
+  // upper k-slots must hold no k values: a transposing product multiplies
+  // them by zero, and 0 * Inf or 0 * NaN would spread a non-finite value
+  // across the token's row.
   template <bool WITH_Q>
   __device__ __forceinline__ void load(uint4* d, int r0, int span, int lr, int g) const {
     // (read back from lane 0: the clamps compile to vector instructions, and a
@@ -273,7 +277,7 @@ struct SegRows {
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(v + base * kDV), 0, rows * kDV * 2, kBufWord3);
     d[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lr * kDV * 2 + 16 * g, 0, 0));
     d[1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rv, lr * kDV * 2 + 64 + 16 * g, 0, 0));
-    const int ko = lr * kD * 2 + 16 * (g & 1);
+    const int ko = WITH_Q || g < 2 ? lr * kD * 2 + 16 * (g & 1) : 0x40000000;
     const __amdgpu_buffer_rsrc_t rk =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(k + base * kD), 0, rows * kD * 2, kBufWord3);
     if (WITH_Q && g >= 2) {
@@ -545,8 +549,9 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
     sel0 = __builtin_bit_cast(bf16x8, make_uint4(w0[0], w0[1], w0[2], w0[3]));
     sel1 = __builtin_bit_cast(bf16x8, make_uint4(w1[0], w1[1], w1[2], w1[3]));
   }
-  // (padding tokens arrive as zeros; the q pieces of lanes g >= 2 sit in
-  // k-slots 16..31 of the k operand, which sel0 does not pick)
+  // (padding tokens arrive as zeros; the q pieces of lanes g >= 2 are zeroed
+  // in the k operand: sel0 multiplies its k-slots 16..31 by zero, which would
+  // turn a non-finite q value into a NaN row of K^T)
   auto stage = [&](const uint4 (&pfs)[NPF], int b) {
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -554,7 +559,7 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
       const int tt = w + NW * i;
       const bf16x8 v0 = __builtin_bit_cast(bf16x8, pfs[3 * i]);
       const bf16x8 v1 = __builtin_bit_cast(bf16x8, pfs[3 * i + 1]);
-      const bf16x8 ka = __builtin_bit_cast(bf16x8, pfs[3 * i + 2]);
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, g < 2 ? pfs[3 * i + 2] : make_uint4(0, 0, 0, 0));
       // V^T: four 16x16 tiles, lane (li, g) gets tokens 16tt + 4g + r of column 16ct + li
       const f32x4 d0 = mfma_bf16_k32(v0, sel0, zero);
       const f32x4 d1 = mfma_bf16_k32(v0, sel1, zero);
@@ -948,8 +953,8 @@ __device__ __forceinline__ void segment_sum_regs(unsigned char* lds_raw, const O
     float xi[8];
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      // (padding tokens arrive as zeros; the copies of k in lanes g >= 2 sit
-      // in k-slots 16..31, which sel0 does not pick)
+      // (padding tokens arrive as zeros, and so do k-slots 16..31 of the k
+      // operand: lanes g >= 2 load nothing there)
       const bf16x8 v0 = __builtin_bit_cast(bf16x8, r[3 * x]);
       const bf16x8 v1 = __builtin_bit_cast(bf16x8, r[3 * x + 1]);
       const bf16x8 ka = __builtin_bit_cast(bf16x8, r[3 * x + 2]);
