@@ -19,10 +19,12 @@
 //  3. replay: it runs the segment again from its prefix, producing the outputs
 //     (Eq. (5)), and the last segment writes the final state.
 //
-// Workgroup b serves sequence b / nseg and takes its segment from that
-// sequence's atomic ticket counter; a workgroup only ever waits for earlier
-// segments of its own sequence, which hold smaller tickets of the same counter:
-// they started before it, are running (or done), and every wait ends.  (One
+// Every workgroup serves a fixed sequence (sequence_of_workgroup: all the
+// segments of a sequence on one XCD where the dispatch allows) and takes its
+// segment from that sequence's atomic ticket counter; a workgroup only ever
+// waits for earlier segments of its own sequence, which hold smaller tickets
+// of the same counter: they started before it, are running (or done), and
+// every wait ends.  (One
 // counter per sequence: a single counter for the whole grid serialises its
 // atomics, about 12 ns each, so the last of 512 workgroups would start 6 us
 // late.)
@@ -1095,7 +1097,8 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
 
   int ticket = blockIdx.x;
   if (sync != nullptr) {  // uniform
-    const int b = blockIdx.x / nseg;  // the sequence; the counter gives the segment
+    // the sequence (XCD-affine); its counter gives the segment
+    const int b = sequence_of_workgroup(blockIdx.x, nseg, gridDim.x / nseg);
     if (tid == 0)
       s_ticket = b * nseg + __hip_atomic_fetch_add(&sync[kHdr + (size_t)b * nseg * kFlagStride + kTicketWord], 1,
                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

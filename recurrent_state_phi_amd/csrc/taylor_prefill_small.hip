@@ -40,10 +40,11 @@
 // segment writes only after it has seen the flag of every earlier segment of
 // its group and of every earlier group's last member, each of which had seen
 // its own group's flags.
-// Workgroup b serves sequence b / nseg and takes its segment from that
-// sequence's ticket counter (the flag word of its last segment, which never
-// carries a flag), so a workgroup only waits for segments that started before
-// it.  Waits are bounded; one that runs
+// Every workgroup serves a fixed sequence (sequence_of_workgroup: all the
+// segments of a sequence on one XCD where the dispatch allows) and takes its
+// segment from that sequence's ticket counter (the flag word of its last
+// segment, which never carries a flag), so a workgroup only waits for segments
+// that started before it.  Waits are bounded; one that runs
 // out records an error code in the workspace header.  Images cross XCDs
 // through buffer accesses with the device-scope cache policy (sc1); a flag goes
 // up only after every wave has waited for its image stores and the waves have
@@ -160,7 +161,8 @@ __global__ __launch_bounds__(kThreads) void prefill_small_kernel(const TIN* __re
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int ticket = blockIdx.x;
   if (sync != nullptr) {  // uniform
-    const int b = blockIdx.x / nseg;  // the sequence; the counter gives the segment
+    // the sequence (XCD-affine); its counter gives the segment
+    const int b = sequence_of_workgroup(blockIdx.x, nseg, gridDim.x / nseg);
     if (tid == 0)
       s_ticket = b * nseg + __hip_atomic_fetch_add(&sync[kHdr + (size_t)b * nseg + nseg - 1], 1, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
