@@ -270,8 +270,8 @@ const char* taylor_last_error(void);
  * phases that do not run are recorded back to back).  For the single-kernel
  * paths (n = 1, 2 at d = 16; n = 3 with bfloat16 inputs) events[1] follows
  * the small kernel that clears the workspace flags and events[2], events[3]
- * bracket the prefill kernel (for n = 3 they are recorded by its dispatch
- * itself, at its start and its end).
+ * are recorded by the prefill kernel's dispatch itself, at its start and its
+ * end.
  * count == 0 turns it off.  The events stay owned by the caller. */
 int taylor_set_phase_events(hipEvent_t* events, int count);
 

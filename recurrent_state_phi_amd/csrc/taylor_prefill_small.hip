@@ -49,6 +49,7 @@
 // through buffer accesses with the device-scope cache policy (sc1); a flag goes
 // up only after every wave has waited for its image stores and the waves have
 // met at a barrier.
+#include <hip/hip_ext.h>
 #include <type_traits>
 
 #include "taylor_device.h"
@@ -596,14 +597,19 @@ hipError_t launch_t(const PrefillArgs& a) {
     hipLaunchKernelGGL(clear_kernel, dim3((nslots + 255) / 256), dim3(256), 0, a.stream, sync, nslots);
   }
   if (ev) {
+    // events 2 and 3 are recorded by the dispatch itself, at the kernel's
+    // start and end (no launch gap inside the interval)
     (void)hipEventRecord(ev[1], a.stream);
-    (void)hipEventRecord(ev[2], a.stream);
+    hipExtLaunchKernelGGL((prefill_small_kernel<NT, TIN, TOUT>), dim3(a.BH * nseg), dim3(kThreads), 0, a.stream,
+                          ev[2], ev[3], 0, static_cast<const TIN*>(a.q), static_cast<const TIN*>(a.k),
+                          static_cast<const TIN*>(a.v), static_cast<TOUT*>(a.o), a.state, t_base, sync, imgs, a.N, nseg,
+                          group_size(nseg), 1.0f / a.a, a.wait_limit);
+  } else {
+    hipLaunchKernelGGL((prefill_small_kernel<NT, TIN, TOUT>), dim3(a.BH * nseg), dim3(kThreads), 0, a.stream,
+                       static_cast<const TIN*>(a.q), static_cast<const TIN*>(a.k), static_cast<const TIN*>(a.v),
+                       static_cast<TOUT*>(a.o), a.state, t_base, sync, imgs, a.N, nseg, group_size(nseg), 1.0f / a.a,
+                       a.wait_limit);
   }
-  hipLaunchKernelGGL((prefill_small_kernel<NT, TIN, TOUT>), dim3(a.BH * nseg), dim3(kThreads), 0, a.stream,
-                     static_cast<const TIN*>(a.q), static_cast<const TIN*>(a.k), static_cast<const TIN*>(a.v),
-                     static_cast<TOUT*>(a.o), a.state, t_base, sync, imgs, a.N, nseg, group_size(nseg), 1.0f / a.a,
-                     a.wait_limit);
-  if (ev) (void)hipEventRecord(ev[3], a.stream);
   return hipGetLastError();
 }
 
