@@ -89,8 +89,9 @@ int taylor_state_init(float* state, int B, int H, int d, int d_v, int n, hipStre
  * Host only; -1 cast to size_t on
  * error.  For states of several 176-row feature blocks (d = 16 with n >= 4,
  * and n = 3 at d = 32, 64) it includes a row of d_v + 4 floats per
- * head-token per feature block.  For n = 1, 2 at d = 16 (segments of 256
- * tokens, so 0 for N <= 256) it is a 64-word header, one flag word per
+ * head-token per feature block.  For n = 1, 2 at d = 16 (segments of 128
+ * tokens for n = 1 and 256 for n = 2, so 0 for N up to one segment) it is a
+ * 64-word header, one flag word per
  * segment rounded up to 64 words, and two state images per segment of 1,108
  * (n = 2) or 68 (n = 1) floats; `chunk` does not change it. */
 size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n, int chunk);
@@ -108,7 +109,8 @@ size_t taylor_prefill_workspace_bytes(int B, int H, int N, int d, int d_v, int n
  *           for TAYLOR_BF16.  d = 16 with n = 4..6, and d = 32, 64: 32 or 64
  *           for either input type.  At d = 16 with n = 1, 2 the value is
  *           checked but the kernel always evaluates chunks of 16 tokens inside
- *           segments of 256 (the outputs agree to float32 rounding).
+ *           segments of 128 (n = 1) or 256 (n = 2) tokens (the outputs agree
+ *           to float32 rounding).
  *   Arithmetic: float32 inputs use float32 MFMA throughout.  bfloat16 inputs
  *   use bfloat16 MFMA with float32 accumulation and a float32 state at d = 16
  *   for n = 3 with chunk 64 or 128; everywhere else (d = 16 with n = 1, 2, n =
@@ -140,8 +142,8 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, fl
  * held until the process ends; this call allocates nothing and calls no
  * allocating routine.  A plan that needs more (taylor_prefill_workspace_bytes
  * > 32 MiB: d = 16 with n >= 4, whose per-block partial outputs are large,
- * the wide heads, and n = 1, 2 at d = 16 beyond about 3,780 (n = 2) or
- * 61,000 (n = 1) segments of 256 tokens over all heads) returns
+ * the wide heads, and n = 1, 2 at d = 16 beyond about 3,780 segments of 256
+ * tokens (n = 2) or 61,000 segments of 128 tokens (n = 1) over all heads) returns
  * TAYLOR_EINVAL with the size in the message and launches nothing; every
  * plan with n = 3 at d = 16 fits.  All calls on one
  * GPU share its array: calls that overlap in time on one GPU (other streams,

@@ -11,10 +11,11 @@
 // the diagonal block)
 //     Y = C + P V + (Q / a) M,   den = count + rowsum(P) + (Q / a) . K,   o = Y / den,
 // and every term is linear in A.  States are additive (section 5.2), so each
-// (b, h) sequence is cut into segments of kL = 256 tokens, one workgroup of 8
-// waves each (one workgroup per CU: its q, k, v and state sums fill most of
-// the 160 KB of LDS), and A before a chunk = caller's state + earlier
-// segments' sums + the segment's own tokens before the chunk:
+// (b, h) sequence is cut into segments of 32 tokens per wave, one workgroup
+// each: 8 waves and 256 tokens at n = 2 (one workgroup per CU: its q, k, v
+// and state sums fill most of the 160 KB of LDS), 4 waves and 128 tokens at
+// n = 1 (two per CU); A before a chunk = caller's state + earlier segments'
+// sums + the segment's own tokens before the chunk:
 //   1. the workgroup loads its segment's q, k, v into LDS once (zeros past the
 //      end of the sequence), and the caller's state into registers;
 //   2. wave w sums tokens 32w .. 32w+31 (M on the float32 matrix cores, C, K
@@ -58,9 +59,14 @@
 namespace taylor {
 namespace small {
 
-constexpr int kWaves = 8;              // waves per workgroup
-constexpr int kThreads = 64 * kWaves;  // threads per workgroup
-constexpr int kL = 32 * kWaves;        // tokens per segment (2 chunks of 16 per wave)
+// Waves per workgroup: 4 at n = 1 (128-token segments, two workgroups per CU,
+// whose phases then overlap), 8 at n = 2, whose 26 times larger images make
+// the look-back over twice as many segments cost more than the overlap gains
+// (n = 1 / n = 2 on the order sweep: 11.9 / 17.2 us per call with 4 waves,
+// 12.3 / 16.2 us with 8).
+template <int NT> constexpr int waves_of() { return NT == 1 ? 4 : 8; }
+template <int NT> constexpr int threads_of() { return 64 * waves_of<NT>(); }
+template <int NT> constexpr int seg_tokens() { return 32 * waves_of<NT>(); }  // 2 chunks of 16 per wave
 constexpr int kQS = 20;   // LDS row stride (floats) of q and k
 constexpr int kVS = 68;   // LDS row stride (floats) of v
 constexpr int kHdr = 64;  // header words: [0] unused, [1] error code, [2] kN3Magic
@@ -75,7 +81,7 @@ template <int NT> struct Img {
   static constexpr int kS = state_width(NT) * kDV;  // floats of S
   static constexpr int kFloats = NT == 2 ? 1108 : 68;
   static constexpr int kVec = kFloats / 4;         // 16-byte units
-  static constexpr int kPer = (kVec + kThreads - 1) / kThreads;  // units per thread
+  static constexpr int kPer = (kVec + threads_of<NT>() - 1) / threads_of<NT>();  // units per thread
   static constexpr int kCnt = kS;                  // T row 0
   static constexpr int kK = kS + 1;                // T rows 1-16 (n = 2)
   static constexpr int kPad = kS + state_width(NT);
@@ -144,11 +150,12 @@ template <> struct Raw<uint16_t> {  // 8 elements
 };
 
 template <int NT, typename TIN, typename TOUT>
-__global__ __launch_bounds__(kThreads) void prefill_small_kernel(const TIN* __restrict__ q, const TIN* __restrict__ k,
+__global__ __launch_bounds__(threads_of<NT>(), NT == 1 ? 2 : 1) void prefill_small_kernel(const TIN* __restrict__ q, const TIN* __restrict__ k,
                                                             const TIN* __restrict__ v, TOUT* __restrict__ o,
                                                             float* __restrict__ state, size_t t_base,
                                                             int* __restrict__ sync, float* __restrict__ imgs, int N,
                                                             int nseg, int G, float inv_a, int wait_limit) {
+  constexpr int kWaves = waves_of<NT>(), kThreads = threads_of<NT>(), kL = seg_tokens<NT>();
   using I = Img<NT>;
   constexpr int IMG = I::kFloats, NV = I::kPer;
   __shared__ __align__(16) float Xq[kL][kQS];
@@ -584,6 +591,7 @@ inline int group_size(int nseg) {
 
 template <int NT, typename TIN, typename TOUT>
 hipError_t launch_t(const PrefillArgs& a) {
+  constexpr int kL = seg_tokens<NT>(), kThreads = threads_of<NT>();
   const int nseg = (a.N + kL - 1) / kL;
   const size_t t_base = (size_t)a.BH * state_width(NT) * kDV;
   int* sync = nullptr;
@@ -622,7 +630,8 @@ hipError_t launch_n(const PrefillArgs& a) {
 }  // namespace small
 
 size_t prefill_small_workspace_floats(int BH, int N, int n) {
-  const int nseg = (N + small::kL - 1) / small::kL;
+  const int L = n == 2 ? small::seg_tokens<2>() : small::seg_tokens<1>();
+  const int nseg = (N + L - 1) / L;
   if (BH <= 0 || nseg <= 1) return 0;
   const size_t img = n == 2 ? small::Img<2>::kFloats : small::Img<1>::kFloats;
   const size_t slots = (size_t)BH * nseg;

@@ -105,17 +105,19 @@ def test_workspace_sizing(rsp):
     # one segment per head when the heads alone fill the GPU: no workspace
     assert rsp.prefill_workspace_bytes(64, 8, 4096, 3, 64) == 0
     assert rsp.prefill_workspace_bytes(1, 1, 0, 3, 64) == 0
-    # n = 1, 2 (single-launch kernel, 256-token segments whatever the chunk): a
-    # header of 64 words, one flag word per segment (rounded up to 64 words),
-    # then two images per segment (its sum and its inclusive prefix) of 1,108
-    # (n = 2) or 68 floats
-    slots = 4 * 8 * (8192 // 256)
-    for n, img in ((2, 1108), (1, 68)):
+    # n = 1, 2 (single-launch kernel, segments of 128 (n = 1) or 256 (n = 2)
+    # tokens whatever the chunk): a header of 64 words, one flag word per segment
+    # (rounded up to 64 words), then two images per segment (its sum and its
+    # inclusive prefix) of 1,108 (n = 2) or 68 floats
+    for n, img, seg in ((2, 1108, 256), (1, 68, 128)):
+        slots = 4 * 8 * (8192 // seg)
         for chunk in (32, 64):
-            assert rsp.prefill_workspace_bytes(4, 8, 8192, n, chunk) == 4 * (64 + 1024 + slots * 2 * img)
+            assert rsp.prefill_workspace_bytes(4, 8, 8192, n, chunk) == 4 * (64 + -(-slots // 64) * 64 + slots * 2 * img)
     assert rsp.prefill_workspace_bytes(4, 8, 256, 2, 64) == 0  # one segment per head
+    assert rsp.prefill_workspace_bytes(4, 8, 128, 1, 64) == 0
     assert rsp.prefill_workspace_bytes(1, 1, 257, 2, 64) == 4 * (64 + 64 + 2 * 2 * 1108)
-    assert rsp.prefill_workspace_bytes(1, 1, 257, 1, 32) == 4 * (64 + 64 + 2 * 2 * 68)
+    assert rsp.prefill_workspace_bytes(1, 1, 129, 1, 32) == 4 * (64 + 64 + 2 * 2 * 68)
+    assert rsp.prefill_workspace_bytes(1, 1, 257, 1, 32) == 4 * (64 + 64 + 3 * 2 * 68)
     # n = 3 (single-launch kernel): a header of 64 words plus one 64-word flag
     # slot per segment, then one state image of 10624 floats per segment
     nseg = 512 // 32

@@ -1,6 +1,6 @@
 """GPU parity of the single-launch n = 1, 2 prefill at d = 16 (section 3.5 of "A
 Taylor-Series Route to Linear-Time Transformers with a Fixed Number of Recurrent
-States", arXiv 2610.20637): 256-token segments, 16-token chunks inside, a
+States", arXiv 2610.20637): segments of 128 (n = 1) or 256 (n = 2) tokens, 16-token chunks inside, a
 look-back over the earlier segments of a sequence for the prefix.  Against the
 float64 oracle through the C ABI; tolerances (max over rows of
 ||o_t - o_t^oracle||_inf / ||o_t^oracle||_inf): 1e-4 float32, 2e-2 bfloat16 inputs.
@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
 DEV = "cuda:0"
-SEG = 256  # tokens per segment
+SEG = {1: 128, 2: 256}  # tokens per segment, by n
 
 
 @pytest.fixture(scope="module")
@@ -43,14 +43,14 @@ def state_of(k, v, n):
     return feats.T @ np.concatenate([v.astype(np.float64), np.ones((v.shape[0], 1))], axis=1)
 
 
-def edge_rows(N, per_head, heads, seed):
-    """Rows of every head: first and last token of every segment, of every 16-token
-    chunk in the first two and the last two segments, the last token, and seeded
-    random positions."""
+def edge_rows(N, per_head, heads, seed, seg):
+    """Rows of every head: first and last token of every segment of `seg` tokens, of
+    every 16-token chunk in the first two and the last two segments, the last token,
+    and seeded random positions."""
     rng = np.random.default_rng(seed)
-    edges = set(range(0, N, SEG)) | set(range(SEG - 1, N, SEG)) | {N - 1}
-    last = (N - 1) // SEG * SEG
-    for lo, hi in ((0, 2 * SEG), (max(0, last - SEG), N)):
+    edges = set(range(0, N, seg)) | set(range(seg - 1, N, seg)) | {N - 1}
+    last = (N - 1) // seg * seg
+    for lo, hi in ((0, 2 * seg), (max(0, last - seg), N)):
         edges |= set(range(lo, min(hi, N), 16)) | set(range(lo + 15, min(hi, N), 16))
     rows = []
     for bh in range(heads):
@@ -63,16 +63,17 @@ def edge_rows(N, per_head, heads, seed):
 @pytest.mark.parametrize("n", [1, 2])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_many_segments_per_head(rsp, n, dtype):
-    """B=1, H=2, N=70,001: 274 segments per head (the look-back polls 64 flags per
-    read, so it has to move its window back several times), a one-token last
-    segment; sampled rows and the final state against the oracle."""
+    """B=1, H=2, N=70,001: 547 (n = 1) or 274 (n = 2) segments per head (the
+    look-back polls 64 flags per read, so it has to move its window back several
+    times), a short last segment; sampled rows and the final state against the
+    oracle."""
     say("n<=2 many segments", n, dtype)
     B, H, N, a = 1, 2, 70001, 1.3
     q, k, v = TI.make_qkv(700 + n, B, H, N, 16, 64, dtype=dtype)
     st = rsp.new_state(B, H, n, device=DEV)
     o = rsp.prefill(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), st, n, a, chunk=64, check=True)
     got = o.float().cpu().numpy().astype(np.float64).reshape(-1, 64)
-    rows = edge_rows(N, 128, B * H, 5)
+    rows = edge_rows(N, 128, B * H, 5, SEG[n])
     ref = oracle.taylor_direct(q, k, v, n, a, rows=rows)
     assert oracle.rel_err_rowwise(got[rows], ref) <= TOL[dtype]
     S, T = (x.cpu().numpy().astype(np.float64) for x in rsp.state_views(st, B, H, n))
@@ -84,10 +85,10 @@ def test_many_segments_per_head(rsp, n, dtype):
 
 
 @pytest.mark.parametrize("n", [1, 2])
-@pytest.mark.parametrize("N", [1, 15, 16, 17, 255, 256, 257, 511, 513, 1000])
+@pytest.mark.parametrize("N", [1, 15, 16, 17, 127, 128, 129, 255, 256, 257, 511, 513, 1000])
 def test_lengths_around_segment_edges(rsp, n, N):
     """Every output row against the oracle for lengths around the 16-token chunk and
-    the 256-token segment (one segment, one full, one plus a token, ...)."""
+    the 128- and 256-token segments (one segment, one full, one plus a token, ...)."""
     say("n<=2 length", n, N)
     q, k, v = TI.make_qkv(710 + N, 2, 3, N, 16, 64)
     st = rsp.new_state(2, 3, n, device=DEV)
@@ -207,7 +208,7 @@ def test_many_heads_several_rounds(rsp, dtype):
     st = rsp.new_state(B, H, n, device=DEV)
     o = rsp.prefill(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), st, n, 1.0, chunk=64, check=True)
     got = o.float().cpu().numpy().astype(np.float64).reshape(-1, 64)
-    rows = edge_rows(N, 8, B * H, 6)
+    rows = edge_rows(N, 8, B * H, 6, SEG[n])
     ref = oracle.taylor_direct(q, k, v, n, 1.0, rows=rows)
     assert oracle.rel_err_rowwise(got[rows], ref) <= TOL[dtype]
     S, T = (x.cpu().numpy().astype(np.float64) for x in rsp.state_views(st, B, H, n))
@@ -218,27 +219,28 @@ def test_many_heads_several_rounds(rsp, dtype):
 
 
 def test_more_than_4096_segments(rsp):
-    """One head of 1,152,001 tokens, n = 1: 4,501 segments in groups of 68, so both
+    """One head of 576,001 tokens, n = 1: 4,501 segments in groups of 68, so both
     parts of the look-back (67 earlier members, 66 earlier groups) wait on more than
     64 flags and poll in two reads; sampled rows (segment starts and ends, the chunks
     around the first group edges, the last segments) and the final state against the
     oracle."""
     say("n<=2 4,501 segments")
-    B, H, N, n = 1, 1, 256 * 4500 + 1, 1
+    B, H, N, n = 1, 1, SEG[1] * 4500 + 1, 1
     q, k, v = TI.make_qkv(770, B, H, N, 16, 64)
     st = rsp.new_state(B, H, n, device=DEV)
     o = rsp.prefill(to_dev(q, "f32"), to_dev(k, "f32"), to_dev(v, "f32"), st, n, 1.0, chunk=64, check=True)
     got = o.cpu().numpy().astype(np.float64).reshape(-1, 64)
-    G, nseg = 68, (N + SEG - 1) // SEG
+    G, L = 68, SEG[1]
+    nseg = (N + L - 1) // L
     # first and last token of every segment of the first three groups, of every 40th
     # segment, and of the last two; the chunks on both sides of the first group edges
     segs = set(range(3 * G)) | set(range(0, nseg, 40)) | {nseg - 2, nseg - 1}
     pos = {N - 1}
     for s in segs:
-        pos |= {s * SEG, min(N - 1, s * SEG + SEG - 1)}
+        pos |= {s * L, min(N - 1, s * L + L - 1)}
     for grp in range(3):
-        edge = (grp + 1) * G * SEG
-        pos |= set(range(edge - SEG, min(N, edge + SEG), 16))
+        edge = (grp + 1) * G * L
+        pos |= set(range(edge - L, min(N, edge + L), 16))
     rows = np.asarray(sorted(pos), np.int64)
     ref = oracle.taylor_direct(q, k, v, n, 1.0, rows=rows)
     assert oracle.rel_err_rowwise(got[rows], ref) <= TOL["f32"]
