@@ -156,10 +156,13 @@ int taylor_attn_prefill(const void* q, const void* k, const void* v, void* o, fl
     return fail(TAYLOR_EINVAL, "taylor_attn_prefill: q, k, v, o and state must be 16-byte aligned");
   if ((int64_t)B * H > (1 << 24) || (int64_t)N * chunk > ((int64_t)1 << 40))
     return fail(TAYLOR_EINVAL, "taylor_attn_prefill: sizes out of range");
-  // n <= 2 at d = 16: one 512-thread workgroup per 256-token segment
+  // n <= 2 at d = 16: one workgroup per segment (256 threads per 128 tokens at
+  // n = 1, 512 per 256 at n = 2)
   if (d == 16 && n <= 2 &&
-      (int64_t)B * H * ((N + taylor::kSmallSegment - 1) / taylor::kSmallSegment) >= (1 << 23))
-    return fail(TAYLOR_EINVAL, "taylor_attn_prefill: sizes out of range (B*H*ceil(N/256) must be < 2^23 for n <= 2)");
+      (int64_t)B * H * ((N + taylor::small_segment_tokens(n) - 1) / taylor::small_segment_tokens(n)) >= (1 << 23))
+    return fail(TAYLOR_EINVAL, "taylor_attn_prefill: sizes out of range (B*H*ceil(N/" +
+                                   std::to_string(taylor::small_segment_tokens(n)) + ") must be < 2^23 for n = " +
+                                   std::to_string(n) + ")");
   const taylor::PrefillPlan plan = taylor::plan_prefill(B * H, N, d, n, chunk);
   const size_t need = plan.workspace_floats * sizeof(float);
   if (need > 0) {

@@ -56,11 +56,12 @@ constexpr int kN3Magic = 0x54617933;
 constexpr int kN3ErrTimeout = 1;
 
 // n = 1, 2 at d = 16 (taylor_prefill_small.hip): one launch over segments of
-// 256 tokens (16-token chunks inside, whatever the requested chunk), with a
-// look-back across segments, and the workspace it needs.
+// 128 (n = 1) or 256 (n = 2) tokens (16-token chunks inside, whatever the
+// requested chunk), with a look-back across segments, and the workspace it
+// needs.
 hipError_t launch_prefill_small(const PrefillArgs& a);
 size_t prefill_small_workspace_floats(int BH, int N, int n);
-constexpr int kSmallSegment = 256;
+constexpr int small_segment_tokens(int n) { return n == 1 ? 128 : 256; }
 
 // Feature-blocked prefill, chunk 32 or 64 (taylor_prefill_fb.hip): d = 16
 // with n = 3 (one block; bfloat16 inputs with chunk 64 or 128 take the

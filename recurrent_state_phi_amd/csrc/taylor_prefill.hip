@@ -71,10 +71,11 @@ hipError_t launch_segment_scan(const float* st_S, const float* st_T, float* W_S,
 PrefillPlan plan_prefill(int BH, int N, int d, int n, int chunk) {
   PrefillPlan p;
   if (BH <= 0 || N <= 0 || chunk <= 0) return p;
-  if (d == 16 && n <= 2) {  // fixed segments of 256 tokens, 16-token chunks inside
+  if (d == 16 && n <= 2) {  // fixed segments of 128 or 256 tokens, 16-token chunks inside
+    const int L = small_segment_tokens(n);
     p.nchunks = (N + 15) / 16;
-    p.chunks_per_seg = kSmallSegment / 16;
-    p.nseg = (N + kSmallSegment - 1) / kSmallSegment;
+    p.chunks_per_seg = L / 16;
+    p.nseg = (N + L - 1) / L;
     p.workspace_floats = prefill_small_workspace_floats(BH, N, n);
     return p;
   }

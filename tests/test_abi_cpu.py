@@ -163,6 +163,13 @@ def test_invalid_arguments_are_rejected_before_launch(rsp):
     # workspace too small for a multi-segment plan
     assert _prefill_rc(lib, B=1, H=1, N=4096, q=16, k=16, v=16, o=16, state=16) == -1
     assert b"workspace" in lib.taylor_last_error()
+    # n <= 2: at most 2^23 - 1 segment workgroups, segments of 128 (n = 1) or
+    # 256 (n = 2) tokens
+    big = dict(B=1 << 12, H=1 << 4, N=128 * 128, q=16, k=16, v=16, o=16, state=16)
+    assert _prefill_rc(lib, n=1, **big) == -1
+    assert b"out of range" in lib.taylor_last_error() and b"N/128" in lib.taylor_last_error()
+    assert _prefill_rc(lib, n=2, **big) == -1  # half as many segments: stops at the workspace
+    assert b"workspace" in lib.taylor_last_error()
     dec = lib.taylor_attn_decode
     assert dec(None, None, None, None, None, 1, 1, 16, 64, 3, 1.0, 0, 0, None) == -1
     assert dec(None, None, None, None, None, 1, 1, 16, 64, 9, 1.0, 0, 0, None) == -2
