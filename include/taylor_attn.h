@@ -294,6 +294,14 @@ int taylor_prefill_check(const void* workspace, size_t workspace_bytes, hipStrea
  * for a negative argument (nothing changed). */
 int taylor_set_wait_limit(int polls);
 
+/* Test hook for reads of LDS before it is written (races between the waves of
+ * a workgroup, a missing initialisation): fills the LDS of every CU with the
+ * 32-bit `pattern` (0xFFFFFFFF reads as a float NaN, 0 re-zeros it) by a
+ * kernel on `stream`, so that the next kernel on that stream starts from LDS
+ * holding it.  Results of every entry point must not depend on it.  Returns
+ * TAYLOR_EHIP if the launch fails. */
+int taylor_debug_fill_lds(unsigned int pattern, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,12 +21,17 @@ import torch
 __all__ = [
     "LIB_PATH", "TaylorError", "state_width", "state_numel", "new_state", "state_init",
     "state_views", "prefill_workspace_bytes", "prefill", "decode", "set_phase_events",
-    "prefill_check", "set_wait_limit", "softmax_prefill", "softmax_decode", "softmax_decode_workspace_bytes",
+    "prefill_check", "set_wait_limit", "debug_fill_lds", "softmax_prefill", "softmax_decode",
+    "softmax_decode_workspace_bytes",
     "prefill_noalloc", "state_bf16_bytes", "new_state_bf16", "state_to_bf16", "state_bf16_views",
     "decode_bf16state", "hybrid_fill_window", "hybrid_decode", "EXPORTED_SYMBOLS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtaylor_attn.so")
+# TAYLOR_ATTN_LIB names another build of the same library to load instead (the
+# CPU test that runs the ABI tests against an AddressSanitizer build of the
+# host code uses it)
+LIB_PATH = os.environ.get("TAYLOR_ATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                              "libtaylor_attn.so")
 
 TAYLOR_F32, TAYLOR_BF16 = 0, 1
 _CODES = {0: "TAYLOR_OK", -1: "TAYLOR_EINVAL", -2: "TAYLOR_EUNSUPPORTED", -3: "TAYLOR_EHIP", -4: "TAYLOR_ETIMEOUT"}
@@ -37,7 +42,7 @@ EXPORTED_SYMBOLS = (
     "taylor_prefill_check", "taylor_set_wait_limit", "taylor_softmax_prefill",
     "taylor_softmax_decode_workspace_bytes", "taylor_softmax_decode", "taylor_attn_prefill_noalloc",
     "taylor_state_bf16_bytes", "taylor_state_to_bf16", "taylor_attn_decode_bf16state",
-    "taylor_hybrid_fill_window", "taylor_hybrid_decode",
+    "taylor_hybrid_fill_window", "taylor_hybrid_decode", "taylor_debug_fill_lds",
 )
 
 
@@ -89,6 +94,8 @@ _lib.taylor_prefill_check.argtypes = [_vp, _sz, _vp]
 _lib.taylor_prefill_check.restype = _i
 _lib.taylor_set_wait_limit.argtypes = [_i]
 _lib.taylor_set_wait_limit.restype = _i
+_lib.taylor_debug_fill_lds.argtypes = [ctypes.c_uint, _vp]
+_lib.taylor_debug_fill_lds.restype = _i
 _lib.taylor_softmax_prefill.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _i, _vp]
 _lib.taylor_softmax_prefill.restype = _i
 _lib.taylor_softmax_decode_workspace_bytes.argtypes = [_i, _i, _i, _i, _i]
@@ -269,6 +276,12 @@ def set_wait_limit(polls: int) -> int:
     if prev < 0:
         raise TaylorError(-1, _lib.taylor_last_error().decode())
     return prev
+
+
+def debug_fill_lds(pattern: int, device="cuda") -> None:
+    """Test hook: fill every CU's LDS with a 32-bit pattern on the device's current
+    stream, so that the next kernel there starts from it (see taylor_debug_fill_lds)."""
+    _check(_lib.taylor_debug_fill_lds(int(pattern) & 0xFFFFFFFF, _stream_ptr(torch.device(device))))
 
 
 # ---- exact causal softmax attention (the comparison method, Eq. (1)) ----------

@@ -19,7 +19,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 SOURCES = ["taylor_abi.cpp", "taylor_decode.hip", "taylor_prefill.hip", "taylor_prefill_n3.hip",
            "taylor_prefill_n3_c128.hip", "taylor_prefill_fb.hip", "taylor_prefill_small.hip",
            "softmax_attn.hip", "taylor_decode_bf16.hip",
-           "taylor_hybrid.hip"]
+           "taylor_hybrid.hip", "taylor_debug.hip"]
 # per-source extra flags: the 64-token n = 3 prefill is scheduled for
 # instruction-level parallelism (measured faster for it, slower for 128 tokens);
 # the n <= 2 prefill and the softmax kernels keep matrix-core results in

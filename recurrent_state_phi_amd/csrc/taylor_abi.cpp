@@ -243,6 +243,12 @@ int taylor_set_wait_limit(int polls) {
   return g_wait_limit.exchange(polls);
 }
 
+int taylor_debug_fill_lds(unsigned int pattern, hipStream_t stream) {
+  if (hipError_t e = taylor::launch_fill_lds(pattern, stream))
+    return fail(TAYLOR_EHIP, std::string("taylor_debug_fill_lds: ") + hipGetErrorString(e));
+  return TAYLOR_OK;
+}
+
 int taylor_softmax_prefill(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d, int d_v,
                            float a, taylor_dtype in_dtype, taylor_dtype out_dtype, hipStream_t stream) {
   if (int e = check_dtypes(in_dtype, out_dtype)) return e;

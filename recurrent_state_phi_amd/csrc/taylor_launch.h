@@ -63,6 +63,9 @@ hipError_t launch_prefill_small(const PrefillArgs& a);
 size_t prefill_small_workspace_floats(int BH, int N, int n);
 constexpr int small_segment_tokens(int n) { return n == 1 ? 128 : 256; }
 
+// Test hook (taylor_debug.hip): fills every CU's LDS with `pattern`.
+hipError_t launch_fill_lds(uint32_t pattern, hipStream_t stream);
+
 // Feature-blocked prefill, chunk 32 or 64 (taylor_prefill_fb.hip): d = 16
 // with n = 3 (one block; bfloat16 inputs with chunk 64 or 128 take the
 // single-launch n = 3 kernel instead), 4, 5, 6, and d = 32, 64 with n = 1, 2,
