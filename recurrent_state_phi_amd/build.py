@@ -26,7 +26,8 @@ SOURCES = ["taylor_abi.cpp", "taylor_decode.hip", "taylor_prefill.hip", "taylor_
 # ordinary vector registers (by default the compiler places them in the
 # accumulation registers and copies every one back with a vector instruction)
 VGPR_MFMA = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
-EXTRA = {"taylor_prefill_n3.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+MAX_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+EXTRA = {"taylor_prefill_n3.hip": MAX_ILP, "taylor_prefill_n3_c128.hip": MAX_ILP,
          "softmax_attn.hip": VGPR_MFMA, "taylor_prefill_small.hip": VGPR_MFMA}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-Wall", "-Wno-unused-function",

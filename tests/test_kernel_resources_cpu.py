@@ -21,12 +21,10 @@ SOURCES = ["taylor_decode.hip", "taylor_prefill.hip", "taylor_prefill_n3.hip", "
            "taylor_prefill_fb.hip", "taylor_prefill_small.hip", "softmax_attn.hip", "taylor_decode_bf16.hip",
            "taylor_hybrid.hip"]
 
-# Scalar spills allowed per kernel (mangled-name prefix -> count).  The
-# 128-token n = 3 prefill keeps 8 scalar registers in vector-register lanes
-# (3 before its matrix loops ran at raised wave priority, 7 before the last
-# segment waited for the other segments' reads of the caller's state; a form
-# of the causal mask that needed 25 cost the long prefill 7%).
-SGPR_SPILL_ALLOWANCE = {"_ZN6taylor2n317prefill_n3_kernelILi128E": 8}
+# Scalar spills allowed per kernel (mangled-name prefix -> count): none.  (The
+# 128-token n = 3 prefill once kept up to 8 scalar registers in vector-register
+# lanes; a form of its causal mask that needed 25 cost the long prefill 7%.)
+SGPR_SPILL_ALLOWANCE = {}
 
 
 def _build_module():
