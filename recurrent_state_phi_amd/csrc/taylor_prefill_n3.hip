@@ -841,6 +841,9 @@ __device__ __forceinline__ void segment_pass(Lds<C>& L, const Own<NW_>& own, Acc
       const float cB = g >= 2 ? 1.0f : 0.0f, cC = g == 1 ? 1.0f : 0.0f;
       constexpr int kD0[4] = {0, 1, 4, 5};
       __builtin_amdgcn_s_setprio(1);
+      // (a scheduling hint that interleaves the state copy's LDS reads with the
+      // products: about 0.5 us per call)
+      __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
       for (int kb = 0; kb < 5; ++kb) {
         float f[8];
