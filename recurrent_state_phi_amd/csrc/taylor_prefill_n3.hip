@@ -17,7 +17,9 @@
 //     the earlier members of its own group: at most about 2 sqrt(nseg) state
 //     images per workgroup, all published right after step 1.
 //  3. replay: it runs the segment again from its prefix, producing the outputs
-//     (Eq. (5)), and the last segment writes the final state.
+//     (Eq. (5)).  The last segment writes the final state (its prefix plus
+//     its own sum) before its replay, so that the store is not left for the
+//     end of the kernel; a single segment writes it after the replay.
 //
 // Every workgroup serves a fixed sequence (sequence_of_workgroup: all the
 // segments of a sequence on one XCD where the dispatch allows) and takes its
@@ -388,12 +390,10 @@ __device__ __forceinline__ int wait_flag(const int* flag, int* err, int limit) {
 // reports before its final store.  The order is the same as for the images:
 // every wave waits for its loads to return, the waves meet at a barrier, one
 // thread bumps the counter; the writer's stores are issued only after it has
-// seen the full count.  The wait is bounded like the others, and practically
-// free: it comes after the last segment's whole replay.
-struct WaitArgs {
-  uintptr_t sync;
-  int slot, want, limit;
-};
+// seen the full count.  The wait is bounded like the others, and nearly free:
+// it comes after the last segment's prefix step, which has already waited for
+// the group sums that the last readers (the group leaders) publish just before
+// they read the caller's state.
 
 __device__ __forceinline__ void report_state_read(int* ctr) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -495,6 +495,37 @@ __device__ __forceinline__ void store_caller_state(float* img, float* st_S, floa
   for (int i = tid; i < kD3 * kDV / 4; i += Sh::NTHREADS)
     __builtin_nontemporal_store(reinterpret_cast<const f32x4*>(img)[i], reinterpret_cast<f32x4*>(ds4) + i);
   for (int i = tid; i < kD3; i += Sh::NTHREADS) __builtin_nontemporal_store(img[kD3 * kDV + i], dt + i);
+}
+
+// The final state a + b (the prefix and the segment's own sum) stored straight
+// from the accumulators: each wave writes the rows it owns (16 consecutive
+// floats of a row per lane group, the T entry from lane li = 0), with no
+// barrier and no pass through LDS; every element of S and T is written by
+// exactly one lane (zero rows of the internal layout map nowhere).
+template <int NW>
+__device__ __forceinline__ void store_caller_state_sum(float* st_S, float* st_T, int bh, const Own<NW>& own,
+                                                       const Acc& a, const Acc& b) {
+  using Sh = Waves<NW>;
+  const int lane = threadIdx.x & 63, li = lane & 15, g = lane >> 4;
+  float* S = st_S + (size_t)bh * kD3 * kDV;
+  float* T = st_T + (size_t)bh * kD3;
+#pragma unroll
+  for (int s = 0; s < 3; ++s) {
+    if (s == 1 && !Sh::HAS_S1) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float wt;
+      const int row = abi_row(own.ft[s], 4 * g + r, &wt);
+      if (row >= 0) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          if (Sh::has(s, ct))
+            __builtin_nontemporal_store((a.s[s][ct][r] + b.s[s][ct][r]) * wt,
+                                        &S[row * kDV + 16 * (s == 2 ? own.ctb + ct : ct) + li]);
+        if (li == 0 && (s < 2 || own.own_t2)) __builtin_nontemporal_store((a.t[s][r] + b.t[s][r]) * wt, &T[row]);
+      }
+    }
+  }
 }
 
 // ---- the replay: one pass over the chunks [t_begin, t_end) of sequence bh ---
@@ -1085,13 +1116,12 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
   constexpr int NW = waves_for<C>();
   using LB = Lds<C>;
   // The replay's chunk buffers, the sum pass's reduction area, and while the
-  // final state is stored, a float [153 * 65] image of it in the caller's
-  // layout.
+  // final state of a single segment is stored, a float [153 * 65] image of it
+  // in the caller's layout.
   constexpr size_t kA = sizeof(LB) > (size_t)sum_lds_bytes<NW>() ? sizeof(LB) : (size_t)sum_lds_bytes<NW>();
   constexpr size_t kLdsBytes = kA > kAbiImg * 4 ? kA : kAbiImg * 4;
   __shared__ __align__(16) unsigned char lds_raw[kLdsBytes];
   __shared__ int s_ticket;
-  __shared__ WaitArgs s_wait;
   float* img = reinterpret_cast<float*>(lds_raw);
 
   const int tid = threadIdx.x, lane = tid & 63, li = lane & 15;
@@ -1109,13 +1139,6 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
     ticket = __builtin_amdgcn_readfirstlane(s_ticket);
   }
   const int bh = ticket / nseg, seg = ticket % nseg;
-  if (tid == 0 && seg == nseg - 1) {  // the final wait's operands, for after the replay
-    volatile WaitArgs* sw = &s_wait;
-    sw->sync = reinterpret_cast<uintptr_t>(sync);
-    sw->slot = ticket;                        // = head0 + nseg - 1, the counter's slot
-    sw->want = sync != nullptr ? nseg - 1 : 0;  // no other segment: nothing to wait for
-    sw->limit = wait_limit;
-  }
   const int t_begin = seg * cps * C;
   const int t_end = min(N, t_begin + cps * C);
   const Own<NW> own(w, li);
@@ -1126,9 +1149,10 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
   // the last member of a group publishes the group's sum, unless no group follows
   const bool leader = seg == g0 + gs - 1 && seg < nseg - 1;
 
-  // 1. the segment's own sum (not needed for the last segment)
+  // 1. the segment's own sum (that of the last of several segments is part of
+  //    the final state; a single segment carries its state through the replay)
   Acc acc;
-  if (seg < nseg - 1) segment_sum_regs<NW>(lds_raw, own, acc, k, v, bh, N, t_begin, t_end);
+  if (nseg > 1) segment_sum_regs<NW>(lds_raw, own, acc, k, v, bh, N, t_begin, t_end);
   else zero_acc(acc);
   // a segment that is not the last of its group publishes its sum at once
   if (nseg > 1 && !leader && seg < nseg - 1) {  // uniform
@@ -1195,20 +1219,17 @@ __global__ __launch_bounds__(64 * waves_for<C>(), (C == 64 ? 2 : 1)) void prefil
       }
     }
   }
-  // 3. replay from the prefix
-  segment_pass<C, NW, TOUT>(*reinterpret_cast<LB*>(lds_raw), own, pre, q, k, v, o, bh, N, t_begin, t_end, inv_a,
-                            seg == nseg - 1);
-  if (seg == nseg - 1) {  // uniform
-    // the wait's operands come back from LDS (stored at the start), so that
-    // none of them occupies a register during the replay
-    volatile WaitArgs* sw = &s_wait;
-    const int want = __builtin_amdgcn_readfirstlane(sw->want);
-    if (want > 0) {  // uniform
-      int* const sy = reinterpret_cast<int*>(sw->sync);
-      wait_count(&sy[kHdr + (size_t)sw->slot * kFlagStride], want, &sy[1], sw->limit);
-    }
-    store_caller_state<NW>(img, st_S, st_T, bh, own, pre);
+  // the last of several segments has the final state = its prefix + its own
+  // sum now, and stores it before its replay (once every other segment has
+  // read the caller's state), so that the store is off the kernel's tail
+  if (nseg > 1 && seg == nseg - 1) {  // uniform
+    wait_count(flag_of(nseg - 1), nseg - 1, &sync[1], wait_limit);
+    store_caller_state_sum<NW>(st_S, st_T, bh, own, pre, acc);
   }
+  // 3. replay from the prefix (a single segment also carries the state to the end)
+  segment_pass<C, NW, TOUT>(*reinterpret_cast<LB*>(lds_raw), own, pre, q, k, v, o, bh, N, t_begin, t_end, inv_a,
+                            nseg == 1);
+  if (nseg == 1) store_caller_state<NW>(img, st_S, st_T, bh, own, pre);  // uniform
 }
 
 // Clears the error code and the nslots flag slots (flag and ticket words), and
